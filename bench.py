@@ -1,0 +1,213 @@
+#!/usr/bin/env python
+"""Benchmark of exact relative-position attention, forward + backward, on one GPU.
+
+One step = every stage of the path on one batch of seeded synthetic input
+already resident in HBM: map tables and relation projection, fused forward,
+backward row terms, query-parallel pass, key-parallel pass, contraction and
+bucket fold.  The default workload is the 8K layer-benchmark shape of the
+setup section of "Fast and Exact Relative-Position Attention via
+Structure-Aware Kernels" (nanless.github.io digest) for the Shaw mechanism:
+B=1, H=12, N=8192, d=64, fp16, truncation +-128.
+
+Timing: W untimed warmup steps, then exactly K steps between two
+synchronisations.  HIP events are recorded between the stage calls, on the
+stream the library launches on, so each kernel's average duration is measured
+live; the dominant attention kernel gives the roofline figure.
+FLOP convention (FlashAttention): forward 4 d per live (query, key) pair,
+backward 10 d; each backward kernel's own count is its GEMM work (query pass
+6 d, key pass 8 d per pair).  The CPU baseline is the fp64 oracle on a
+bounded sample (one head of the same workload), timed on the host cores.
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd ms and TFLOP/s (% fp16 MFMA peak), N=8192 H=12 d=64 fp16; peak memory"
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+
+def live_pairs(w, key_len):
+    """Number of unmasked (query, key) pairs over the whole batch, per head."""
+    N = w.N
+    total = 0
+    for b in range(w.B):
+        kl = N if key_len is None else int(key_len[b])
+        kl = max(0, min(N, kl))
+        if w.causal:
+            # query i sees keys j <= min(i, kl - 1)
+            m = min(N, kl)
+            total += m * (m + 1) // 2 + (N - m) * m
+        else:
+            total += N * kl
+    return total
+
+
+def describe(w):
+    phi = w.phi
+    if phi["kind"] == "truncated":
+        ps = f"truncated[{phi['lo']},{phi['hi']}]"
+    elif phi["kind"] == "t5":
+        ps = f"t5[{phi['num_buckets']} buckets, max {phi['max_distance']}]"
+    else:
+        ps = "identity"
+    terms = "+".join(t for t, f in (("aQ", w.has_aq), ("aK", w.has_ak), ("b", w.has_b)) if f)
+    mask = "+".join(m for m, f in (("causal", w.causal), ("key_padding", w.key_padding)) if f)
+    return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "phi": ps,
+            "terms": terms or "none", "mask": mask or "none", "tau": round(w.tau, 6)}
+
+
+def cpu_baseline(w, x, pairs_per_head):
+    """fp64 oracle, forward + backward of (batch 0, head 0) at the full length."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+    from relpos_synth import as_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    f = {k: as_f64(v) for k, v in x.items() if k != "key_len"}
+    kl = None if x["key_len"] is None else x["key_len"].numpy()
+    t0 = time.perf_counter()
+    oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi, tau=w.tau,
+                   causal=w.causal, key_len=kl, bh=[(0, 0)])
+    oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"], phi=w.phi,
+                    tau=w.tau, causal=w.causal, key_len=kl, bh=[(0, 0)])
+    dt = time.perf_counter() - t0
+    pairs0 = live_pairs(w.with_(B=1), None if kl is None else kl[:1])
+    flops = 14.0 * w.d * pairs0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"forward+backward of 1 of {w.B * w.H} (batch, head) slices "
+                      f"(b=0, h=0) at full N={w.N}, fp64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="shaw_n8192_f16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is a "
+              "single-device operator and no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_relative_position_amd._binding as B_
+    from relpos_synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = make_inputs(w)
+    t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    torch.cuda.synchronize(dev)
+    mem_inputs = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
+                      tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True)
+    stages = [("project", lambda: run.fwd(B_.FWD_PROJECT)),
+              ("attend", lambda: run.fwd(B_.FWD_ATTEND)),
+              ("prepare", lambda: run.bwd(B_.BWD_PREPARE)),
+              ("query_pass", lambda: run.bwd(B_.BWD_QUERY_PASS)),
+              ("key_pass", lambda: run.bwd(B_.BWD_KEY_PASS)),
+              ("contract", lambda: run.bwd(B_.BWD_CONTRACT))]
+
+    for _ in range(args.warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize(dev)
+    peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for k, (_, fn) in enumerate(stages):
+            fn()
+            ev[s][k + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    K = args.steps
+    stage_ms = {name: sum(ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(K)) / K
+                for k, (name, _) in enumerate(stages)}
+    gpu_ms = ev[0][0].elapsed_time(ev[K - 1][len(stages)]) / K
+    fwd_ms = stage_ms["project"] + stage_ms["attend"]
+    bwd_ms = sum(stage_ms[n] for n in ("prepare", "query_pass", "key_pass", "contract"))
+
+    kl = None if x["key_len"] is None else x["key_len"].numpy()
+    pairs = live_pairs(w, kl) * w.H
+    d = w.d
+    useful = 14.0 * d * pairs
+    value = useful / (gpu_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    kern_flops = {"attend": 4.0 * d * pairs, "query_pass": 6.0 * d * pairs,
+                  "key_pass": 8.0 * d * pairs}
+    kern_name = {"attend": "fwd_kernel", "query_pass": "bwd_q_kernel", "key_pass": "bwd_k_kernel"}
+    dom = max(kern_flops, key=lambda n: stage_ms[n])
+    achieved = kern_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+
+    # projection pass: algorithmic bytes = fp32 window written + Q and table read
+    zbytes = run.zs.numel() if run.zs is not None else 0
+    proj = None
+    if zbytes:
+        rd = t["q"].numel() * t["q"].element_size() * (1 + int(w.has_ak))
+        proj = {"GB/s": round((zbytes + rd) / (stage_ms["project"] * 1e-3) / 1e9, 1),
+                "bytes": int(zbytes + rd), "ms": round(stage_ms["project"], 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal inputs of the workload's shape and scales)",
+        "config": describe(w),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        "pct_peak": round(100.0 * value / peak, 2),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "projection": proj,
+        "peak_extra_bytes": int(peak_extra),
+        "peak_extra_bytes_fwd": int(run.O.numel() * run.O.element_size() + run.lse.numel() * 4
+                                    + zbytes + run.ws_f.numel()),
+        "roofline": {"bound": "mfma", "kernel": kern_name[dom], "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None, "flops_per_launch": kern_flops[dom],
+                     "ms_per_launch": round(stage_ms[dom], 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, pairs / w.H / w.B)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

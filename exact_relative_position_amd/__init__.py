@@ -1,0 +1,57 @@
+"""Exact relative-position attention on MI355X (gfx950).
+
+``relpos_attention`` is a drop-in attention with additive relative-position
+terms (Eq. 1 of "Fast and Exact Relative-Position Attention via
+Structure-Aware Kernels", nanless.github.io digest):
+
+    S_ij = tau * (q_i.k_j + q_i.aQ[phi(i,j)] + k_j.aK[phi(i,j)] + b[phi(i,j)]) + M_ij
+    O    = softmax(S) V
+
+with phi a truncated (Shaw, DeBERTa), bucketed (T5) or identity
+(Transformer-XL) offset map.  Forward and backward run in the HIP library
+``librelpos_attn.so`` (C ABI in include/relpos_attn.h); this package only
+marshals arguments and lets PyTorch own device memory and streams.
+
+phi is a dict: {"kind": "truncated", "lo": lo, "hi": hi},
+{"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": True},
+or {"kind": "identity"}.
+"""
+
+import torch
+
+from . import _binding
+from ._binding import RelposError, phi_info, phi_rows  # noqa: F401
+
+__all__ = ["relpos_attention", "RelPosAttention", "forward", "backward", "phi_rows",
+           "phi_info", "RelposError"]
+
+forward = _binding.forward
+backward = _binding.backward
+
+
+class RelPosAttention(torch.autograd.Function):
+    """Autograd wrapper: the forward keeps O, LSE and the relation projections."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, aq, ak, b, phi, tau, causal, key_len):
+        O, lse, zs = _binding.forward(q, k, v, aq, ak, b, phi=phi, tau=tau, causal=causal,
+                                      key_len=key_len, keep_z=True)
+        ctx.save_for_backward(q, k, v, aq, ak, b, O, lse, zs, key_len)
+        ctx.cfg = (phi, tau, causal)
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v, aq, ak, b, O, lse, zs, key_len = ctx.saved_tensors
+        phi, tau, causal = ctx.cfg
+        dq, dk, dv, daq, dak, db = _binding.backward(
+            q, k, v, aq, ak, b, O, lse, dO.contiguous(), zs, phi=phi, tau=tau, causal=causal,
+            key_len=key_len)
+        cast = lambda g, t: None if g is None else g.to(t.dtype)  # noqa: E731
+        return dq, dk, dv, cast(daq, aq), cast(dak, ak), cast(db, b), None, None, None, None
+
+
+def relpos_attention(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False,
+                     key_len=None):
+    """Differentiable relative-position attention; q, k, v are [B, H, N, 64] on the GPU."""
+    return RelPosAttention.apply(q, k, v, aq, ak, b, phi, tau, causal, key_len)

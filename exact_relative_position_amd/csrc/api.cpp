@@ -1,0 +1,743 @@
+// api.cpp -- the C ABI: argument validation, workspace planning and the
+// launch sequence of the forward and backward passes.
+//
+// Forward (pipeline section of "Fast and Exact Relative-Position Attention via
+// Structure-Aware Kernels", nanless.github.io digest):
+//   map tables (T5 unfold) -> relation projection of the reachable window ->
+//   fused tiled forward.
+// Backward (backward section of the same page):
+//   D preprocess -> query-parallel pass -> key-parallel pass ->
+//   dZ . table into dQ / dK -> dZ^T . Q / K into the table gradients ->
+//   fold of copied bucket columns.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "geometry.hpp"
+#include "relpos_attn.h"
+#include "t5.hpp"
+
+namespace relpos {
+hipError_t launch_fwd(int dtype, const AttnArgs& a, hipStream_t st);
+hipError_t launch_pre(int dtype, const PreArgs& p, hipStream_t st);
+hipError_t launch_bwd_q(int dtype, const AttnArgs& a, hipStream_t st);
+hipError_t launch_bwd_k(int dtype, const AttnArgs& a, hipStream_t st);
+hipError_t launch_phi_rows(const PhiArgs& p, int32_t* rows, hipStream_t st);
+hipError_t launch_phi_fold(const PhiArgs& p, int32_t* fold, int32_t* ub, int32_t* ue, int R,
+                           hipStream_t st);
+hipError_t launch_bias_unfold(int dtype, const BiasArgs& a, hipStream_t st);
+hipError_t launch_proj(int dtype, const ProjArgs& a, hipStream_t st);
+hipError_t launch_rows(int dtype, const RowsArgs& a, hipStream_t st);
+hipError_t launch_cols(int dtype, const ColsArgs& a, int Ho, hipStream_t st);
+hipError_t launch_fold(const FoldArgs& a, hipStream_t st);
+}  // namespace relpos
+
+using namespace relpos;
+
+namespace {
+
+thread_local std::string g_err;
+
+relpos_status fail(relpos_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr int64_t kMaxN = 1 << 20;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int elem_size(int dtype) { return dtype == RELPOS_F32 ? 4 : 2; }
+
+// Resolved description of one call.
+struct Plan {
+  int dtype = 0, esz = 0;
+  int B = 0, H = 0, N = 0;
+  Geo geo{};
+  PhiArgs phi{};
+  int R = 0;       // rows of the caller's tables
+  int Runf = 0;    // rows of the unfolded truncated map
+  bool t5 = false;
+  bool has_aq = false, has_ak = false, has_b = false;
+  bool keypad = false;
+  int64_t aq_hs = 0, ak_hs = 0, b_hs = 0;
+  int nblk = 0;        // 128-row blocks per (b, h)
+  int ncol_q = 0, ncol_k = 0;
+  size_t z_elems = 0;  // one projection buffer, elements
+  int rtiles = 0, Rpad = 0;
+  int split_q = 1, split_k = 1, split_b = 1;
+  int ho_aq = 1, ho_ak = 1, ho_b = 1;
+};
+
+// Unfolded thresholds of a map: the first offsets on each side beyond which
+// the row no longer changes.
+relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& lo, int64_t& hi) {
+  switch (p.kind) {
+    case RELPOS_PHI_TRUNCATED:
+      if (p.lo > p.hi) return fail(RELPOS_ERR_INVALID_ARG, "truncated map needs lo <= hi");
+      if (p.lo < -(1 << 29) || p.hi > (1 << 29))
+        return fail(RELPOS_ERR_INVALID_ARG, "truncation thresholds out of range");
+      R = (int64_t)p.hi - p.lo + 1;
+      lo = p.lo;
+      hi = p.hi;
+      return RELPOS_OK;
+    case RELPOS_PHI_IDENTITY:
+      R = 2 * N - 1;
+      lo = -(N - 1);
+      hi = N - 1;
+      return RELPOS_OK;
+    case RELPOS_PHI_BUCKET_T5: {
+      if (p.num_buckets < 2 || p.num_buckets > 4096)
+        return fail(RELPOS_ERR_INVALID_ARG, "T5 num_buckets must be in [2, 4096]");
+      if (p.bidirectional && (p.num_buckets & 1))
+        return fail(RELPOS_ERR_INVALID_ARG, "bidirectional T5 needs an even num_buckets");
+      const int nb = p.bidirectional ? p.num_buckets / 2 : p.num_buckets;
+      const int me = p.max_exact > 0 ? p.max_exact : nb / 2;
+      if (me < 1 || me >= nb)
+        return fail(RELPOS_ERR_INVALID_ARG, "T5 max_exact must be in [1, buckets per side)");
+      if (p.max_distance <= me || p.max_distance > (1 << 24))
+        return fail(RELPOS_ERR_INVALID_ARG, "T5 max_distance must exceed max_exact");
+      int nsat = p.max_distance;
+      for (int n = 0; n <= p.max_distance; ++n) {
+        if (t5_bucket_dev(-n, p.num_buckets, p.max_exact, p.max_distance, p.bidirectional) ==
+            nb - 1) {
+          nsat = n;
+          break;
+        }
+      }
+      R = p.num_buckets;
+      lo = -nsat;
+      hi = p.bidirectional ? nsat : 0;
+      return RELPOS_OK;
+    }
+    default:
+      return fail(RELPOS_ERR_INVALID_ARG, "unknown phi kind");
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
+                        const relpos_mask* mask, int terms, Plan& pl) {
+  if (!prob || !phi || !mask) return fail(RELPOS_ERR_INVALID_ARG, "null descriptor");
+  if (prob->dtype < RELPOS_F32 || prob->dtype > RELPOS_BF16)
+    return fail(RELPOS_ERR_INVALID_ARG, "unknown dtype");
+  if (prob->B < 0 || prob->H < 0 || prob->N < 0)
+    return fail(RELPOS_ERR_INVALID_ARG, "negative size");
+  if (prob->d != kHeadDim) return fail(RELPOS_ERR_UNSUPPORTED, "only head dim 64 is implemented");
+  if (prob->N > kMaxN) return fail(RELPOS_ERR_UNSUPPORTED, "N above 1048576");
+  if (prob->B > 65535 || prob->H > 65535) return fail(RELPOS_ERR_UNSUPPORTED, "B or H too large");
+  if (!(prob->tau > 0.f) || !std::isfinite(prob->tau))
+    return fail(RELPOS_ERR_INVALID_ARG, "tau must be finite and > 0");
+  if (mask->flags & ~(RELPOS_MASK_CAUSAL | RELPOS_MASK_KEY_PADDING))
+    return fail(RELPOS_ERR_INVALID_ARG, "unknown mask bits");
+  if ((mask->flags & RELPOS_MASK_KEY_PADDING) && !mask->key_len)
+    return fail(RELPOS_ERR_INVALID_ARG, "key padding needs key_len");
+  if (terms & ~(RELPOS_TERM_AQ | RELPOS_TERM_AK | RELPOS_TERM_B))
+    return fail(RELPOS_ERR_INVALID_ARG, "unknown term bits");
+  pl.dtype = prob->dtype;
+  pl.esz = elem_size(prob->dtype);
+  pl.B = (int)prob->B;
+  pl.H = (int)prob->H;
+  pl.N = (int)prob->N;
+  pl.has_aq = terms & RELPOS_TERM_AQ;
+  pl.has_ak = terms & RELPOS_TERM_AK;
+  pl.has_b = terms & RELPOS_TERM_B;
+  pl.keypad = mask->flags & RELPOS_MASK_KEY_PADDING;
+  pl.t5 = phi->kind == RELPOS_PHI_BUCKET_T5;
+  const int64_t Nn = pl.N > 0 ? pl.N : 1;
+  int64_t R, lo, hi;
+  relpos_status s = unfold_range(*phi, Nn, R, lo, hi);
+  if (s != RELPOS_OK) return s;
+  pl.R = (int)R;
+  pl.Runf = (int)(hi - lo + 1);
+  pl.geo.N = pl.N;
+  pl.geo.lo = (int)lo;
+  pl.geo.hi = (int)hi;
+  pl.geo.R = pl.Runf;
+  pl.geo.W = (int)std::min<int64_t>(pl.Runf, (int64_t)pl.N + kGroup - 1);
+  pl.geo.causal = (mask->flags & RELPOS_MASK_CAUSAL) ? 1 : 0;
+  if (pl.geo.W < 1) pl.geo.W = 1;
+  pl.phi.kind = phi->kind;
+  pl.phi.N = pl.N;
+  pl.phi.lo_unf = (int)lo;
+  pl.phi.hi_unf = (int)hi;
+  pl.phi.num_buckets = phi->num_buckets;
+  pl.phi.max_exact = phi->max_exact;
+  pl.phi.max_distance = phi->max_distance;
+  pl.phi.bidirectional = phi->bidirectional ? 1 : 0;
+  pl.phi.lo = phi->lo;
+  pl.phi.hi = phi->hi;
+  pl.aq_hs = prob->aq_head_stride;
+  pl.ak_hs = prob->ak_head_stride;
+  pl.b_hs = prob->b_head_stride;
+  if (pl.aq_hs < 0 || pl.ak_hs < 0 || pl.b_hs < 0)
+    return fail(RELPOS_ERR_INVALID_ARG, "negative table head stride");
+  if ((pl.has_aq && (pl.aq_hs * pl.esz) % 16) || (pl.has_ak && (pl.ak_hs * pl.esz) % 16))
+    return fail(RELPOS_ERR_INVALID_ARG, "table head stride must be a multiple of 16 bytes");
+  if ((size_t)pl.B * pl.H * pl.N * (size_t)pl.geo.W > (size_t)1 << 40)
+    return fail(RELPOS_ERR_UNSUPPORTED, "projection window too large");
+  pl.ho_aq = pl.aq_hs == 0 ? 1 : pl.H;
+  pl.ho_ak = pl.ak_hs == 0 ? 1 : pl.H;
+  pl.ho_b = pl.b_hs == 0 ? 1 : pl.H;
+  pl.nblk = (pl.N + kBlockRows - 1) / kBlockRows;
+  pl.z_elems = (size_t)pl.B * pl.H * pl.N * pl.geo.W;
+  // column tiles of the projection (max over groups)
+  for (int grp = 0; grp < pl.nblk; ++grp) {
+    int cb, ce;
+    cols_q(pl.geo, grp, cb, ce);
+    pl.ncol_q = std::max(pl.ncol_q, (ce - cb + 63) / 64);
+    cols_k(pl.geo, grp, cb, ce);
+    pl.ncol_k = std::max(pl.ncol_k, (ce - cb + 63) / 64);
+    if (!grouped(pl.geo)) break;
+  }
+  pl.rtiles = (pl.Runf + 31) / 32;
+  pl.Rpad = pl.rtiles * 32;
+  auto splits = [&](int ho, bool shared) {
+    const int64_t rows = (int64_t)(shared ? pl.B * pl.H : pl.B) * pl.N;
+    int64_t want = (1024 + (int64_t)pl.rtiles * ho - 1) / std::max<int64_t>(1, (int64_t)pl.rtiles * ho);
+    int64_t cap = std::max<int64_t>(1, rows / 512);
+    return (int)std::max<int64_t>(1, std::min(want, cap));
+  };
+  pl.split_q = splits(pl.ho_aq, pl.aq_hs == 0);
+  pl.split_k = splits(pl.ho_ak, pl.ak_hs == 0);
+  pl.split_b = splits(pl.ho_b, pl.b_hs == 0);
+  return RELPOS_OK;
+}
+
+relpos_status check_tensor(const Plan& pl, const relpos_problem* prob, int role, const void* ptr,
+                           const char* name) {
+  if (!ptr) return fail(RELPOS_ERR_INVALID_ARG, std::string("null pointer: ") + name);
+  if (!aligned16(ptr)) return fail(RELPOS_ERR_INVALID_ARG, std::string("misaligned: ") + name);
+  for (int t = 0; t < 3; ++t) {
+    const int64_t s = prob->strides[role][t];
+    if (s < 0 || (s * pl.esz) % 16)
+      return fail(RELPOS_ERR_INVALID_ARG,
+                  std::string("stride must be a non-negative multiple of 16 bytes: ") + name);
+  }
+  if (prob->strides[role][2] < kHeadDim && pl.N > 1)
+    return fail(RELPOS_ERR_INVALID_ARG, std::string("row stride smaller than d: ") + name);
+  return RELPOS_OK;
+}
+
+Str str_of(const relpos_problem* prob, int role) {
+  return Str{prob->strides[role][0], prob->strides[role][1], prob->strides[role][2]};
+}
+
+// Workspace carving ---------------------------------------------------------
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+struct WsFwd {
+  int32_t* fold = nullptr;
+  float* bunf = nullptr;
+  float* zq = nullptr;
+  float* zk = nullptr;
+};
+
+struct WsBwd {
+  int32_t* fold = nullptr;
+  int32_t* ub = nullptr;
+  int32_t* ue = nullptr;
+  float* bunf = nullptr;
+  float* zq = nullptr;
+  float* zk = nullptr;
+  float* D = nullptr;
+  float* dq_part = nullptr;
+  float* dk_part = nullptr;
+  float* dzq = nullptr;
+  float* dzk = nullptr;
+  float* part_q = nullptr;
+  float* part_qb = nullptr;
+  float* part_k = nullptr;
+};
+
+bool need_bunf(const Plan& pl) { return pl.has_b && !pl.has_aq; }
+
+size_t carve_fwd(const Plan& pl, bool zsave_given, void* base, WsFwd& w) {
+  Carve c(base);
+  if (pl.t5) w.fold = c.take<int32_t>(sizeof(int32_t) * pl.Runf);
+  if (need_bunf(pl)) w.bunf = c.take<float>(sizeof(float) * pl.Runf * pl.ho_b);
+  if (!zsave_given) {
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+  }
+  return c.off;
+}
+
+size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
+  Carve c(base);
+  const size_t bhn = (size_t)pl.B * pl.H * pl.N;
+  if (pl.t5) {
+    w.fold = c.take<int32_t>(sizeof(int32_t) * pl.Runf);
+    w.ub = c.take<int32_t>(sizeof(int32_t) * pl.R);
+    w.ue = c.take<int32_t>(sizeof(int32_t) * pl.R);
+  }
+  if (need_bunf(pl)) w.bunf = c.take<float>(sizeof(float) * pl.Runf * pl.ho_b);
+  if (!zsave_given) {
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+  }
+  w.D = c.take<float>(sizeof(float) * bhn);
+  if (pl.has_aq) w.dq_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
+  if (pl.has_ak) w.dk_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
+  if (pl.has_aq || pl.has_b) w.dzq = c.take<float>(sizeof(float) * pl.z_elems);
+  if (pl.has_ak) w.dzk = c.take<float>(sizeof(float) * pl.z_elems);
+  if (pl.has_aq)
+    w.part_q = c.take<float>(sizeof(float) * pl.split_q * pl.ho_aq * pl.Rpad * kHeadDim);
+  if (pl.has_b) w.part_qb = c.take<float>(sizeof(float) * pl.split_b * pl.ho_b * pl.Rpad);
+  if (pl.has_ak)
+    w.part_k = c.take<float>(sizeof(float) * pl.split_k * pl.ho_ak * pl.Rpad * kHeadDim);
+  return c.off;
+}
+
+size_t zsave_bytes(const Plan& pl) {
+  size_t n = 0;
+  if (pl.has_aq) n += align256(sizeof(float) * pl.z_elems);
+  if (pl.has_ak) n += align256(sizeof(float) * pl.z_elems);
+  return n;
+}
+
+relpos_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RELPOS_OK;
+  return fail(RELPOS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int terms_of(const void* aQ, const void* aK, const void* b) {
+  return (aQ ? RELPOS_TERM_AQ : 0) | (aK ? RELPOS_TERM_AK : 0) | (b ? RELPOS_TERM_B : 0);
+}
+
+// Map tables needed by both passes: T5 fold table (+ ranges), unfolded bias.
+relpos_status prepare_tables(const Plan& pl, const void* b, int32_t* fold, int32_t* ub,
+                             int32_t* ue, float* bunf, hipStream_t st) {
+  if (pl.t5) {
+    relpos_status s = hip_check(launch_phi_fold(pl.phi, fold, ub, ue, pl.R, st), "phi fold");
+    if (s != RELPOS_OK) return s;
+  }
+  if (bunf) {
+    BiasArgs ba{b, pl.b_hs, pl.t5 ? fold : nullptr, bunf, pl.ho_b, pl.Runf};
+    relpos_status s = hip_check(launch_bias_unfold(pl.dtype, ba, st), "bias unfold");
+    if (s != RELPOS_OK) return s;
+  }
+  return RELPOS_OK;
+}
+
+relpos_status project(const Plan& pl, const relpos_problem* prob, const void* Q, const void* K,
+                      const void* aQ, const void* aK, const void* b, const int32_t* fold,
+                      float* zq, float* zk, hipStream_t st) {
+  if (pl.has_aq) {
+    ProjArgs pa{};
+    pa.x = Q;
+    pa.sx = str_of(prob, RELPOS_T_Q);
+    pa.tab = aQ;
+    pa.tab_hs = pl.aq_hs;
+    pa.bias = pl.has_b ? b : nullptr;
+    pa.bias_hs = pl.b_hs;
+    pa.fold = pl.t5 ? fold : nullptr;
+    pa.z = zq;
+    pa.B = pl.B;
+    pa.H = pl.H;
+    pa.geo = pl.geo;
+    pa.key_side = 0;
+    pa.ncol_tiles = pl.ncol_q;
+    pa.ngroups = pl.nblk;
+    relpos_status s = hip_check(launch_proj(pl.dtype, pa, st), "projection Q");
+    if (s != RELPOS_OK) return s;
+  }
+  if (pl.has_ak) {
+    ProjArgs pa{};
+    pa.x = K;
+    pa.sx = str_of(prob, RELPOS_T_K);
+    pa.tab = aK;
+    pa.tab_hs = pl.ak_hs;
+    pa.bias = nullptr;
+    pa.fold = pl.t5 ? fold : nullptr;
+    pa.z = zk;
+    pa.B = pl.B;
+    pa.H = pl.H;
+    pa.geo = pl.geo;
+    pa.key_side = 1;
+    pa.ncol_tiles = pl.ncol_k;
+    pa.ngroups = pl.nblk;
+    relpos_status s = hip_check(launch_proj(pl.dtype, pa, st), "projection K");
+    if (s != RELPOS_OK) return s;
+  }
+  return RELPOS_OK;
+}
+
+AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask* mask,
+                   const void* Q, const void* K, const void* V) {
+  AttnArgs a{};
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.key_len = mask->key_len;
+  a.sq = str_of(prob, RELPOS_T_Q);
+  a.sk = str_of(prob, RELPOS_T_K);
+  a.sv = str_of(prob, RELPOS_T_V);
+  a.so = str_of(prob, RELPOS_T_O);
+  a.sdo = str_of(prob, RELPOS_T_DO);
+  a.sdq = str_of(prob, RELPOS_T_DQ);
+  a.sdk = str_of(prob, RELPOS_T_DK);
+  a.sdv = str_of(prob, RELPOS_T_DV);
+  a.B = pl.B;
+  a.H = pl.H;
+  a.geo = pl.geo;
+  a.tau = prob->tau;
+  a.scale2 = prob->tau * 1.4426950408889634f;
+  a.flags = (pl.has_aq ? F_ZQ : 0) | (pl.has_ak ? F_ZK : 0) | (need_bunf(pl) ? F_B : 0) |
+            (pl.keypad ? F_KEYPAD : 0) | ((pl.has_aq || pl.has_b) ? F_ZQ_NEEDED : 0);
+  a.bunf_hs = pl.b_hs == 0 ? 0 : pl.Runf;
+  a.nblk = pl.nblk;
+  return a;
+}
+
+relpos_status check_tables(const Plan& pl, const void* aQ, const void* aK, const void* b) {
+  if (aQ && !aligned16(aQ)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: aQ");
+  if (aK && !aligned16(aK)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: aK");
+  (void)pl;
+  (void)b;
+  return RELPOS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* relpos_status_string(int32_t status) {
+  switch (status) {
+    case RELPOS_OK: return "RELPOS_OK";
+    case RELPOS_ERR_INVALID_ARG: return "RELPOS_ERR_INVALID_ARG";
+    case RELPOS_ERR_UNSUPPORTED: return "RELPOS_ERR_UNSUPPORTED";
+    case RELPOS_ERR_WORKSPACE: return "RELPOS_ERR_WORKSPACE";
+    case RELPOS_ERR_HIP: return "RELPOS_ERR_HIP";
+    default: return "RELPOS_UNKNOWN_STATUS";
+  }
+}
+
+const char* relpos_last_error(void) { return g_err.c_str(); }
+
+relpos_status relpos_phi_info(const relpos_phi* phi, int64_t N, int64_t* R, int64_t* lo_unf,
+                              int64_t* hi_unf) {
+  g_err.clear();
+  if (!phi || !R || !lo_unf || !hi_unf) return fail(RELPOS_ERR_INVALID_ARG, "null argument");
+  if (N < 1 || N > kMaxN) return fail(RELPOS_ERR_INVALID_ARG, "N must be in [1, 1048576]");
+  return unfold_range(*phi, N, *R, *lo_unf, *hi_unf);
+}
+
+relpos_status relpos_phi_rows(const relpos_phi* phi, int64_t N, int32_t* rows, int32_t* fold,
+                              void* stream) {
+  g_err.clear();
+  if (!phi) return fail(RELPOS_ERR_INVALID_ARG, "null phi");
+  if (N < 1 || N > kMaxN) return fail(RELPOS_ERR_INVALID_ARG, "N must be in [1, 1048576]");
+  int64_t R, lo, hi;
+  relpos_status s = unfold_range(*phi, N, R, lo, hi);
+  if (s != RELPOS_OK) return s;
+  PhiArgs p{};
+  p.kind = phi->kind;
+  p.N = (int)N;
+  p.lo_unf = (int)lo;
+  p.hi_unf = (int)hi;
+  p.num_buckets = phi->num_buckets;
+  p.max_exact = phi->max_exact;
+  p.max_distance = phi->max_distance;
+  p.bidirectional = phi->bidirectional ? 1 : 0;
+  p.lo = phi->lo;
+  p.hi = phi->hi;
+  hipStream_t st = (hipStream_t)stream;
+  if (rows) {
+    s = hip_check(launch_phi_rows(p, rows, st), "phi rows");
+    if (s != RELPOS_OK) return s;
+  }
+  if (fold) {
+    s = hip_check(launch_phi_fold(p, fold, nullptr, nullptr, (int)R, st), "phi fold");
+    if (s != RELPOS_OK) return s;
+  }
+  return RELPOS_OK;
+}
+
+relpos_status relpos_attn_zsave_size(const relpos_problem* prob, const relpos_phi* phi,
+                                     int32_t terms, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(RELPOS_ERR_INVALID_ARG, "null bytes");
+  relpos_mask m{0, nullptr};
+  Plan pl;
+  relpos_status s = make_plan(prob, phi, &m, terms, pl);
+  if (s != RELPOS_OK) return s;
+  *bytes = zsave_bytes(pl);
+  return RELPOS_OK;
+}
+
+relpos_status relpos_attn_workspace_size(const relpos_problem* prob, const relpos_phi* phi,
+                                         const relpos_mask* mask, int32_t terms, int32_t pass,
+                                         int32_t zsave_given, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(RELPOS_ERR_INVALID_ARG, "null bytes");
+  if (pass != RELPOS_PASS_FWD && pass != RELPOS_PASS_BWD)
+    return fail(RELPOS_ERR_INVALID_ARG, "unknown pass");
+  Plan pl;
+  relpos_status s = make_plan(prob, phi, mask, terms, pl);
+  if (s != RELPOS_OK) return s;
+  if (pass == RELPOS_PASS_FWD) {
+    WsFwd w;
+    *bytes = carve_fwd(pl, zsave_given != 0, nullptr, w);
+  } else {
+    WsBwd w;
+    *bytes = carve_bwd(pl, zsave_given != 0, nullptr, w);
+  }
+  return RELPOS_OK;
+}
+
+relpos_status relpos_attn_fwd_stages(const relpos_problem* prob, const relpos_phi* phi,
+                                     const relpos_mask* mask, const void* Q, const void* K,
+                                     const void* V, const void* aQ, const void* aK, const void* b,
+                                     void* O, float* lse, void* zsave, void* workspace,
+                                     size_t workspace_bytes, void* stream, int32_t stages) {
+  g_err.clear();
+  if (stages & ~RELPOS_FWD_ALL) return fail(RELPOS_ERR_INVALID_ARG, "unknown forward stage bits");
+  Plan pl;
+  relpos_status s = make_plan(prob, phi, mask, terms_of(aQ, aK, b), pl);
+  if (s != RELPOS_OK) return s;
+  if (pl.B * pl.H * pl.N == 0) return RELPOS_OK;
+  if ((s = check_tensor(pl, prob, RELPOS_T_Q, Q, "Q")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_K, K, "K")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_V, V, "V")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_O, O, "O")) != RELPOS_OK) return s;
+  if ((s = check_tables(pl, aQ, aK, b)) != RELPOS_OK) return s;
+  if (!lse || !aligned16(lse)) return fail(RELPOS_ERR_INVALID_ARG, "lse null or misaligned");
+  if (zsave && !aligned16(zsave)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: zsave");
+  WsFwd w;
+  const size_t need = carve_fwd(pl, zsave != nullptr, nullptr, w);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(RELPOS_ERR_WORKSPACE, "workspace smaller than relpos_attn_workspace_size()");
+  if (workspace && !aligned16(workspace))
+    return fail(RELPOS_ERR_INVALID_ARG, "misaligned: workspace");
+  carve_fwd(pl, zsave != nullptr, workspace, w);
+  if (zsave) {
+    Carve c(zsave);
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (stages & RELPOS_FWD_PROJECT) {
+    if ((s = prepare_tables(pl, b, w.fold, nullptr, nullptr, w.bunf, st)) != RELPOS_OK) return s;
+    if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st)) != RELPOS_OK) return s;
+  }
+  if (!(stages & RELPOS_FWD_ATTEND)) return RELPOS_OK;
+  AttnArgs a = attn_args(pl, prob, mask, Q, K, V);
+  a.o_out = O;
+  a.lse = lse;
+  a.zq = w.zq;
+  a.zk = w.zk;
+  a.bunf = w.bunf;
+  return hip_check(launch_fwd(pl.dtype, a, st), "forward");
+}
+
+relpos_status relpos_attn_fwd(const relpos_problem* prob, const relpos_phi* phi,
+                              const relpos_mask* mask, const void* Q, const void* K, const void* V,
+                              const void* aQ, const void* aK, const void* b, void* O, float* lse,
+                              void* zsave, void* workspace, size_t workspace_bytes, void* stream) {
+  return relpos_attn_fwd_stages(prob, phi, mask, Q, K, V, aQ, aK, b, O, lse, zsave, workspace,
+                                workspace_bytes, stream, RELPOS_FWD_ALL);
+}
+
+relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_phi* phi,
+                                     const relpos_mask* mask, const void* Q, const void* K,
+                                     const void* V, const void* aQ, const void* aK, const void* b,
+                                     const void* O, const float* lse, const void* dO,
+                                     const void* zsave, void* dQ, void* dK, void* dV, float* daQ,
+                                     float* daK, float* db, void* workspace,
+                                     size_t workspace_bytes, void* stream, int32_t stages) {
+  g_err.clear();
+  if (stages & ~RELPOS_BWD_ALL) return fail(RELPOS_ERR_INVALID_ARG, "unknown backward stage bits");
+  Plan pl;
+  relpos_status s = make_plan(prob, phi, mask, terms_of(aQ, aK, b), pl);
+  if (s != RELPOS_OK) return s;
+  if ((aQ == nullptr) != (daQ == nullptr))
+    return fail(RELPOS_ERR_INVALID_ARG, "daQ must be given exactly when aQ is");
+  if ((aK == nullptr) != (daK == nullptr))
+    return fail(RELPOS_ERR_INVALID_ARG, "daK must be given exactly when aK is");
+  if ((b == nullptr) != (db == nullptr))
+    return fail(RELPOS_ERR_INVALID_ARG, "db must be given exactly when b is");
+  hipStream_t st = (hipStream_t)stream;
+  if (pl.B * pl.H * pl.N == 0) {
+    if (!(stages & RELPOS_BWD_CONTRACT)) return RELPOS_OK;
+    // no token pairs: the table gradients are zero (an identity map at N = 0 has no rows)
+    const int Rout = (phi->kind == RELPOS_PHI_IDENTITY && pl.N == 0) ? 0 : pl.R;
+    if (daQ) {
+      FoldArgs f{nullptr, nullptr, nullptr, nullptr, daQ, nullptr, pl.ho_aq, Rout, pl.Rpad, 0};
+      if ((s = hip_check(launch_fold(f, st), "zero daQ")) != RELPOS_OK) return s;
+    }
+    if (daK) {
+      FoldArgs f{nullptr, nullptr, nullptr, nullptr, daK, nullptr, pl.ho_ak, Rout, pl.Rpad, 0};
+      if ((s = hip_check(launch_fold(f, st), "zero daK")) != RELPOS_OK) return s;
+    }
+    if (db) {
+      FoldArgs f{nullptr, nullptr, nullptr, nullptr, nullptr, db, pl.ho_b, Rout, pl.Rpad, 0};
+      if ((s = hip_check(launch_fold(f, st), "zero db")) != RELPOS_OK) return s;
+    }
+    return RELPOS_OK;
+  }
+  if ((s = check_tensor(pl, prob, RELPOS_T_Q, Q, "Q")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_K, K, "K")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_V, V, "V")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_O, O, "O")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_DO, dO, "dO")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_DQ, dQ, "dQ")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_DK, dK, "dK")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_DV, dV, "dV")) != RELPOS_OK) return s;
+  if ((s = check_tables(pl, aQ, aK, b)) != RELPOS_OK) return s;
+  if (!lse) return fail(RELPOS_ERR_INVALID_ARG, "null lse");
+  WsBwd w;
+  const size_t need = carve_bwd(pl, zsave != nullptr, nullptr, w);
+  if (!workspace || workspace_bytes < need)
+    return fail(RELPOS_ERR_WORKSPACE, "workspace smaller than relpos_attn_workspace_size()");
+  if (!aligned16(workspace)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: workspace");
+  if (zsave && !aligned16(zsave)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: zsave");
+  carve_bwd(pl, zsave != nullptr, workspace, w);
+  if (zsave) {
+    Carve c(const_cast<void*>(zsave));
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+  }
+
+  if (stages & RELPOS_BWD_PREPARE) {
+    if ((s = prepare_tables(pl, b, w.fold, w.ub, w.ue, w.bunf, st)) != RELPOS_OK) return s;
+    if (!zsave) {
+      if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st)) != RELPOS_OK) return s;
+    }
+  }
+
+  AttnArgs a = attn_args(pl, prob, mask, Q, K, V);
+  a.o = O;
+  a.lse = const_cast<float*>(lse);
+  a.dO = dO;
+  a.D = w.D;
+  a.zq = w.zq;
+  a.zk = w.zk;
+  a.bunf = w.bunf;
+  a.dq = pl.has_aq ? (void*)w.dq_part : dQ;
+  a.dk = pl.has_ak ? (void*)w.dk_part : dK;
+  a.dv = dV;
+  a.dzq = w.dzq;
+  a.dzk = w.dzk;
+  if (stages & RELPOS_BWD_PREPARE) {
+    PreArgs p{O, dO, str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), w.D, pl.B, pl.H, pl.N};
+    if ((s = hip_check(launch_pre(pl.dtype, p, st), "backward (row terms)")) != RELPOS_OK)
+      return s;
+  }
+  if (stages & RELPOS_BWD_QUERY_PASS) {
+    if ((s = hip_check(launch_bwd_q(pl.dtype, a, st), "backward (query pass)")) != RELPOS_OK)
+      return s;
+  }
+  if (stages & RELPOS_BWD_KEY_PASS) {
+    if ((s = hip_check(launch_bwd_k(pl.dtype, a, st), "backward (key pass)")) != RELPOS_OK)
+      return s;
+  }
+  if (!(stages & RELPOS_BWD_CONTRACT)) return RELPOS_OK;
+
+  // dQ += dZ^Q aQ, dK += dZ^K aK
+  if (pl.has_aq) {
+    RowsArgs r{w.dq_part, w.dzq, aQ, pl.aq_hs, pl.t5 ? w.fold : nullptr, dQ,
+               str_of(prob, RELPOS_T_DQ), pl.B, pl.H, pl.geo, 0, pl.nblk};
+    if ((s = hip_check(launch_rows(pl.dtype, r, st), "contraction dQ")) != RELPOS_OK) return s;
+  }
+  if (pl.has_ak) {
+    RowsArgs r{w.dk_part, w.dzk, aK, pl.ak_hs, pl.t5 ? w.fold : nullptr, dK,
+               str_of(prob, RELPOS_T_DK), pl.B, pl.H, pl.geo, 1, pl.nblk};
+    if ((s = hip_check(launch_rows(pl.dtype, r, st), "contraction dK")) != RELPOS_OK) return s;
+  }
+  // table gradients: dZ^T Q, dZ^T K, column sums of dZ^Q; then the fold
+  const int32_t* ub = pl.t5 ? w.ub : nullptr;
+  const int32_t* ue = pl.t5 ? w.ue : nullptr;
+  const bool joint_b = pl.has_aq && pl.has_b && pl.ho_aq == pl.ho_b && pl.split_q == pl.split_b;
+  if (pl.has_aq) {
+    ColsArgs c{};
+    c.dz = w.dzq;
+    c.x = Q;
+    c.sx = str_of(prob, RELPOS_T_Q);
+    c.part = w.part_q;
+    c.partb = joint_b ? w.part_qb : nullptr;
+    c.B = pl.B;
+    c.H = pl.H;
+    c.geo = pl.geo;
+    c.key_side = 0;
+    c.shared = pl.aq_hs == 0;
+    c.splits = pl.split_q;
+    c.rtiles = pl.rtiles;
+    c.Rpad = pl.Rpad;
+    c.want_x = 1;
+    if ((s = hip_check(launch_cols(pl.dtype, c, pl.ho_aq, st), "contraction daQ")) != RELPOS_OK)
+      return s;
+    FoldArgs f{w.part_q, joint_b ? w.part_qb : nullptr, ub, ue, daQ, joint_b ? db : nullptr,
+               pl.ho_aq, pl.R, pl.Rpad, pl.split_q};
+    if ((s = hip_check(launch_fold(f, st), "fold daQ")) != RELPOS_OK) return s;
+  }
+  if (pl.has_b && !joint_b) {
+    ColsArgs c{};
+    c.dz = w.dzq;
+    c.x = Q;
+    c.sx = str_of(prob, RELPOS_T_Q);
+    c.part = nullptr;
+    c.partb = w.part_qb;
+    c.B = pl.B;
+    c.H = pl.H;
+    c.geo = pl.geo;
+    c.key_side = 0;
+    c.shared = pl.b_hs == 0;
+    c.splits = pl.split_b;
+    c.rtiles = pl.rtiles;
+    c.Rpad = pl.Rpad;
+    c.want_x = 0;
+    if ((s = hip_check(launch_cols(pl.dtype, c, pl.ho_b, st), "contraction db")) != RELPOS_OK)
+      return s;
+    FoldArgs f{nullptr, w.part_qb, ub, ue, nullptr, db, pl.ho_b, pl.R, pl.Rpad, pl.split_b};
+    if ((s = hip_check(launch_fold(f, st), "fold db")) != RELPOS_OK) return s;
+  }
+  if (pl.has_ak) {
+    ColsArgs c{};
+    c.dz = w.dzk;
+    c.x = K;
+    c.sx = str_of(prob, RELPOS_T_K);
+    c.part = w.part_k;
+    c.partb = nullptr;
+    c.B = pl.B;
+    c.H = pl.H;
+    c.geo = pl.geo;
+    c.key_side = 1;
+    c.shared = pl.ak_hs == 0;
+    c.splits = pl.split_k;
+    c.rtiles = pl.rtiles;
+    c.Rpad = pl.Rpad;
+    c.want_x = 1;
+    if ((s = hip_check(launch_cols(pl.dtype, c, pl.ho_ak, st), "contraction daK")) != RELPOS_OK)
+      return s;
+    FoldArgs f{w.part_k, nullptr, ub, ue, daK, nullptr, pl.ho_ak, pl.R, pl.Rpad, pl.split_k};
+    if ((s = hip_check(launch_fold(f, st), "fold daK")) != RELPOS_OK) return s;
+  }
+  return RELPOS_OK;
+}
+
+relpos_status relpos_attn_bwd(const relpos_problem* prob, const relpos_phi* phi,
+                              const relpos_mask* mask, const void* Q, const void* K, const void* V,
+                              const void* aQ, const void* aK, const void* b, const void* O,
+                              const float* lse, const void* dO, const void* zsave, void* dQ,
+                              void* dK, void* dV, float* daQ, float* daK, float* db,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return relpos_attn_bwd_stages(prob, phi, mask, Q, K, V, aQ, aK, b, O, lse, dO, zsave, dQ, dK,
+                                dV, daQ, daK, db, workspace, workspace_bytes, stream,
+                                RELPOS_BWD_ALL);
+}
+
+}  // extern "C"

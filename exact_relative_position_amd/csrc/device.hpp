@@ -1,0 +1,125 @@
+// device.hpp -- gfx950 building blocks: 32x32 MFMA traits per element type,
+// the lane layout of the MFMA operands and results, XCD-aware block order.
+//
+// MFMA lane layout (CDNA, 32x32 output tiles, 64-wide wavefront):
+//  * operand A (M x K) and operand B (K x N) have the same per-lane shape:
+//    lane l holds index l % 32 of its free dimension and E consecutive
+//    k-indices starting at E * (l / 32) of each k-step of KS = 2E values;
+//  * result element e (0..15) of lane l sits at row 8*(e/4) + 4*(l/32) + e%4,
+//    column l % 32.
+// fp16 / bf16 use v_mfma_f32_32x32x16_{f16,bf16} (KS = 16, E = 8); fp32 uses
+// v_mfma_f32_32x32x2_f32 (KS = 2, E = 1).
+//
+// Row permutation: the rows of a score tile come out of the MFMA as result
+// elements, and the next MFMA consumes the same registers as its k-operand.
+// Loading A-row m from tile row sigma(m) makes result element e of lane-half h
+// hold tile row kappa(h, e) = KS*(e/E) + E*h + e%E, which is exactly the
+// k-index the next MFMA expects there, so no data moves between the two.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "geometry.hpp"
+
+namespace relpos {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T>
+struct MT;
+
+template <>
+struct MT<_Float16> {
+  using frag = f16x8;
+  static constexpr int KS = 16, E = 8;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag zero() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (_Float16)0.f;
+    return z;
+  }
+  __device__ static inline frag pack(const float* p) {
+    frag r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)p[i];
+    return r;
+  }
+  __device__ static inline float to_f(_Float16 x) { return (float)x; }
+  __device__ static inline _Float16 from_f(float x) { return (_Float16)x; }
+};
+
+template <>
+struct MT<__bf16> {
+  using frag = bf16x8;
+  static constexpr int KS = 16, E = 8;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag zero() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.f;
+    return z;
+  }
+  __device__ static inline frag pack(const float* p) {
+    frag r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)p[i];
+    return r;
+  }
+  __device__ static inline float to_f(__bf16 x) { return (float)x; }
+  __device__ static inline __bf16 from_f(float x) { return (__bf16)x; }
+};
+
+template <>
+struct MT<float> {
+  using frag = float;
+  static constexpr int KS = 2, E = 1;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag zero() { return 0.f; }
+  __device__ static inline frag pack(const float* p) { return p[0]; }
+  __device__ static inline float to_f(float x) { return x; }
+  __device__ static inline float from_f(float x) { return x; }
+};
+
+// Tile row held by result element e of lane-half h (see header comment).
+template <typename T>
+__device__ inline int kappa(int h, int e) {
+  constexpr int KS = MT<T>::KS, E = MT<T>::E;
+  return KS * (e / E) + E * h + (e % E);
+}
+// Tile row that lane-row m of an A operand loads.
+template <typename T>
+__device__ inline int sigma(int m) {
+  int h = (m >> 2) & 1;
+  int e = 4 * (m >> 3) + (m & 3);
+  return kappa<T>(h, e);
+}
+// Row of result element e of lane-half h (plain MFMA result layout).
+__device__ inline int res_row(int h, int e) { return 8 * (e >> 2) + 4 * h + (e & 3); }
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Blocks are dealt to the 8 XCDs round-robin; renumber them so that blocks
+// consecutive in the logical order run on the same XCD (and share its L2).
+__device__ inline int xcd_remap(int bid, int total) {
+  int q = total >> 3;
+  if (bid >= (q << 3)) return bid;
+  return (bid & 7) * q + (bid >> 3);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace relpos

@@ -1,0 +1,199 @@
+// geometry.hpp -- offset-map geometry shared by the host dispatcher and the
+// kernels: the unfolded truncated map, the reachable offset windows of the
+// relation projections, and the kernel argument blocks.
+//
+// Source: "Fast and Exact Relative-Position Attention via Structure-Aware
+// Kernels" (nanless.github.io digest):
+//  * every map is handled as a truncated map r(o) = clip(o, lo, hi) - lo
+//    (section on constant tiles: bucketed maps are unfolded to this form;
+//    the identity map is the truncation at +-(N-1));
+//  * section on the grouped reachable range: G consecutive queries reach a
+//    contiguous range of at most N + G - 1 offsets, so only that window of the
+//    projection is computed; G = 128 equals the largest block, so a query
+//    block lies in one group; when the table is shorter than the window a
+//    single group covers everything.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define RP_HD __host__ __device__ inline
+#else
+#define RP_HD inline
+#endif
+
+namespace relpos {
+
+constexpr int kGroup = 128;   // G: query/key group = largest block
+constexpr int kHeadDim = 64;  // d
+constexpr int kBlockRows = kGroup;  // rows owned by a workgroup (4 waves x 32)
+
+struct Geo {
+  int N;       // sequence length
+  int lo, hi;  // unfolded truncated map
+  int R;       // rows of the unfolded map = hi - lo + 1
+  int W;       // projection window width (= R for a single group, else N + G - 1)
+  int causal;  // 1 if j > i is masked
+};
+
+RP_HD int imin(int a, int b) { return a < b ? a : b; }
+RP_HD int imax(int a, int b) { return a > b ? a : b; }
+
+// Unfolded row of offset o = j - i.
+RP_HD int rrow(const Geo& g, int o) { return imin(imax(o, g.lo), g.hi) - g.lo; }
+
+RP_HD bool grouped(const Geo& g) { return g.W < g.R; }
+
+// First unfolded row stored for query group `grp` (window [ws, ws + W)).
+RP_HD int win_q(const Geo& g, int grp) {
+  if (!grouped(g)) return 0;
+  int s = rrow(g, -(grp * kGroup + kGroup - 1));
+  return imin(s, g.R - g.W);
+}
+// First unfolded row stored for key group `grp`.
+RP_HD int win_k(const Geo& g, int grp) {
+  if (!grouped(g)) return 0;
+  int s = rrow(g, grp * kGroup - (g.N - 1));
+  return imin(s, g.R - g.W);
+}
+
+// Window columns [cb, ce) that can hold a live entry for some query of group
+// `grp` (all queries when ungrouped): offsets from -(last query) to
+// N-1-(first query), and not beyond 0 when causal.
+RP_HD void cols_q(const Geo& g, int grp, int& cb, int& ce) {
+  int first = grouped(g) ? grp * kGroup : 0;
+  int last = grouped(g) ? imin(g.N - 1, grp * kGroup + kGroup - 1) : g.N - 1;
+  int omin = -last, omax = g.N - 1 - first;
+  if (g.causal) omax = imin(omax, 0);
+  int ws = win_q(g, grp);
+  cb = imax(0, rrow(g, omin) - ws);
+  ce = imin(g.W, rrow(g, omax) - ws + 1);
+}
+// Same for key group `grp`: offsets from (first key)-(N-1) to (last key).
+RP_HD void cols_k(const Geo& g, int grp, int& cb, int& ce) {
+  int first = grouped(g) ? grp * kGroup : 0;
+  int last = grouped(g) ? imin(g.N - 1, grp * kGroup + kGroup - 1) : g.N - 1;
+  int omin = first - (g.N - 1), omax = last;
+  if (g.causal) omax = imin(omax, 0);
+  int ws = win_k(g, grp);
+  cb = imax(0, rrow(g, omin) - ws);
+  ce = imin(g.W, rrow(g, omax) - ws + 1);
+}
+
+enum : int { F_ZQ = 1, F_ZK = 2, F_B = 4, F_KEYPAD = 8, F_ZQ_NEEDED = 16 };
+
+// Strides of a [B, H, N, d] tensor in elements.
+struct Str {
+  int64_t b, h, n;
+};
+
+// Map kernel (tables + projection) ------------------------------------------
+struct PhiArgs {
+  int kind;  // relpos_phi_kind
+  int N;
+  int lo_unf, hi_unf;
+  int num_buckets, max_exact, max_distance, bidirectional;
+  int lo, hi;  // truncated map parameters (kind 0)
+};
+
+struct ProjArgs {
+  const void* x;       // Q or K
+  Str sx;
+  const void* tab;     // aQ or aK
+  int64_t tab_hs;      // table head stride (elements)
+  const void* bias;    // b folded into the projection (query side only), or null
+  int64_t bias_hs;
+  const int32_t* fold; // unfolded row -> table row, or null (identity)
+  float* z;            // [B*H][N][W]
+  int B, H;
+  Geo geo;
+  int key_side;        // 0: query windows, 1: key windows
+  int ncol_tiles;      // 64-column tiles per group launched
+  int ngroups;         // groups per (b, h)
+};
+
+// Attention kernels -----------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;   // forward output (backward reads it only through D)
+  void* o_out;     // forward output pointer
+  float* lse;      // [B*H][N]
+  const void* dO;
+  const float* D;  // [B*H][N]
+  const float* zq; // [B*H][N][W] or null
+  const float* zk;
+  const float* bunf;  // [Hb][R] fp32 unfolded scalar bias, or null
+  int64_t bunf_hs;
+  const int32_t* key_len;
+  void* dq;        // output (dtype) or fp32 partial when F_ZQ
+  void* dk;
+  void* dv;
+  float* dzq;      // [B*H][N][W]
+  float* dzk;
+  Str sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  int B, H;
+  Geo geo;
+  float tau;
+  float scale2;    // tau * log2(e)
+  int flags;
+  int nblk;        // blocks per (b, h) along the parallel dimension
+};
+
+struct PreArgs {
+  const void* o;
+  const void* dO;
+  Str so, sdo;
+  float* D;
+  int B, H, N;
+};
+
+struct RowsArgs {       // dX = part + dZ . table   (per row)
+  const float* part;    // [B*H][N][64] fp32
+  const float* dz;      // [B*H][N][W]
+  const void* tab;
+  int64_t tab_hs;
+  const int32_t* fold;
+  void* out;            // dtype
+  Str sout;
+  int B, H;
+  Geo geo;
+  int key_side;
+  int nblk;             // 128-row blocks per (b, h)
+};
+
+struct ColsArgs {       // partial[s][ho][u][:] = sum_i dZ[i][u - ws] x_i[:]
+  const float* dz;
+  const void* x;
+  Str sx;
+  float* part;          // [S][Ho][Rpad][64]
+  float* partb;         // [S][Ho][Rpad] or null
+  int B, H;
+  Geo geo;
+  int key_side;
+  int shared;           // 1: sum over heads too (Ho = 1)
+  int splits;
+  int rtiles;
+  int Rpad;
+  int want_x;           // 0: only the column sums (db)
+};
+
+struct FoldArgs {       // out[ho][k][:] = sum_s sum_{u in fold range of k} part[s][ho][u][:]
+  const float* part;
+  const float* partb;
+  const int32_t* ub;    // [R] first unfolded row of table row k (or null: identity)
+  const int32_t* ue;
+  float* out;           // [Ho][R][64] or null
+  float* outb;          // [Ho][R] or null
+  int Ho, R, Rpad, splits;
+};
+
+struct BiasArgs {       // bunf[h][u] = b[h][fold[u]]
+  const void* b;
+  int64_t b_hs;
+  const int32_t* fold;
+  float* bunf;
+  int Hb, Runf;
+};
+
+}  // namespace relpos

@@ -1,0 +1,174 @@
+// proj.hip -- offset-map tables and the relation projection.
+//
+// Source: "Fast and Exact Relative-Position Attention via Structure-Aware
+// Kernels" (nanless.github.io digest):
+//  * Eq. (3): Z^Q[i, r] = q_i . aQ[r] and Z^K[j, r] = k_j . aK[r];
+//  * grouped reachable range: each group of G = 128 queries (keys) projects
+//    only the contiguous window of rows it can reach (N + G - 1 rows), or all
+//    rows when the table is shorter; with a causal mask only offsets <= 0 are
+//    live, so only those columns are computed;
+//  * constant tiles: a bucketed map is unfolded into a truncated map by
+//    copying each bucket row once per offset it covers (here the copy is an
+//    index table `fold`: unfolded row u reads table row fold[u]).
+//
+// The projection is an HBM-write-bound GEMM: 128 rows x 64 columns per
+// workgroup, fp16/bf16 (or fp32) MFMA with fp32 accumulation, coalesced fp32
+// stores of the window.  When the scalar bias b sits next to a query-side
+// table it is added here, so the score needs one lookup instead of two.
+#include <math.h>
+
+#include "device.hpp"
+#include "tiles.hpp"
+#include "t5.hpp"
+
+namespace relpos {
+
+__device__ inline int phi_row(const PhiArgs& p, int o) {
+  switch (p.kind) {
+    case 0: return imin(imax(o, p.lo), p.hi) - p.lo;
+    case 1: return t5_bucket_dev(o, p.num_buckets, p.max_exact, p.max_distance, p.bidirectional);
+    default: return o + p.N - 1;
+  }
+}
+
+// rows[t] = phi(t - (N - 1)), t in [0, 2N - 1)
+__global__ void phi_rows_kernel(PhiArgs p, int32_t* rows) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < 2LL * p.N - 1) rows[t] = phi_row(p, (int)(t - (p.N - 1)));
+}
+
+// fold[u] = phi(u + lo_unf), u in [0, R_unf)
+__global__ void phi_fold_kernel(PhiArgs p, int32_t* fold) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  const int R = p.hi_unf - p.lo_unf + 1;
+  if (u < R) fold[u] = phi_row(p, u + p.lo_unf);
+}
+
+// For each table row k: the unfolded rows [ub[k], ue[k]) that copy it (each
+// bucket covers one contiguous offset range; empty buckets get ub = ue = 0).
+__global__ void fold_range_kernel(const int32_t* fold, int Runf, int R, int32_t* ub, int32_t* ue) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= R) return;
+  int b = -1, e = -1;
+  for (int u = 0; u < Runf; ++u) {
+    if (fold[u] == k) {
+      if (b < 0) b = u;
+      e = u + 1;
+    }
+  }
+  ub[k] = b < 0 ? 0 : b;
+  ue[k] = b < 0 ? 0 : e;
+}
+
+// bunf[h][u] = b[h][fold[u]] as fp32 (fold null: identity)
+template <typename T>
+__global__ void bias_unfold_kernel(BiasArgs a) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  if (u >= a.Runf) return;
+  const int r = a.fold ? a.fold[u] : u;
+  a.bunf[(int64_t)h * a.Runf + u] = MT<T>::to_f(((const T*)a.b)[h * a.b_hs + r]);
+}
+
+// Z[bh][i][c] = x_i . tab[fold(ws + c)] (+ bias[fold(ws + c)]) for c in the
+// group's live columns [cb, ce).  Block: 128 rows x 64 columns; wave w owns
+// rows 32w..32w+31 and two 32-column MFMA tiles.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
+  using M = MT<T>;
+  using frag = typename M::frag;
+  constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
+  const Geo g = a.geo;
+  const int N = g.N;
+  const int per_bh = a.ngroups * a.ncol_tiles;
+  const int total = a.B * a.H * per_bh;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / per_bh;
+  const int rem = lid - bh * per_bh;
+  const int grp = rem / a.ncol_tiles, ct = rem - grp * a.ncol_tiles;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  int cb, ce, ws;
+  if (a.key_side) {
+    cols_k(g, grp, cb, ce);
+    ws = win_k(g, grp);
+  } else {
+    cols_q(g, grp, cb, ce);
+    ws = win_q(g, grp);
+  }
+  const int c0 = cb + ct * 64;
+  if (c0 >= ce) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int i = grp * kBlockRows + 32 * w + l32;  // row loaded by this lane (operand A)
+
+  const T* xrow = (const T*)a.x + bb * a.sx.b + hh * a.sx.h + (int64_t)i * a.sx.n;
+  frag xf[NSD];
+#pragma unroll
+  for (int ks = 0; ks < NSD; ++ks) xf[ks] = i < N ? frag_g<T>(xrow, KS * ks + E * hl) : M::zero();
+
+  const T* tab = (const T*)a.tab + hh * a.tab_hs;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int col = c0 + 32 * sub + l32;  // column of operand B held by this lane
+    const bool cv = col < ce;
+    const int u = ws + col;
+    const int r = cv ? (a.fold ? a.fold[u] : u) : 0;
+    const T* trow = tab + (int64_t)r * kHeadDim;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < NSD; ++ks) {
+      frag tf = cv ? frag_g<T>(trow, KS * ks + E * hl) : M::zero();
+      acc = M::mma(xf[ks], tf, acc);
+    }
+    float badd = 0.f;
+    if (a.bias && cv) badd = MT<T>::to_f(((const T*)a.bias)[hh * a.bias_hs + r]);
+    if (cv) {
+      float* zc = a.z + (int64_t)bh * N * g.W + col;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = grp * kBlockRows + 32 * w + res_row(hl, e);
+        if (row < N) zc[(int64_t)row * g.W] = acc[e] + badd;
+      }
+    }
+  }
+}
+
+hipError_t launch_phi_rows(const PhiArgs& p, int32_t* rows, hipStream_t st) {
+  const int64_t n = 2LL * p.N - 1;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(phi_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_phi_fold(const PhiArgs& p, int32_t* fold, int32_t* ub, int32_t* ue, int R,
+                           hipStream_t st) {
+  const int Runf = p.hi_unf - p.lo_unf + 1;
+  hipLaunchKernelGGL(phi_fold_kernel, dim3((Runf + 255) / 256), dim3(256), 0, st, p, fold);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !ub) return e;
+  hipLaunchKernelGGL(fold_range_kernel, dim3((R + 255) / 256), dim3(256), 0, st, (const int32_t*)fold,
+                     Runf, R, ub, ue);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_unfold(int dtype, const BiasArgs& a, hipStream_t st) {
+  dim3 grid((a.Runf + 255) / 256, a.Hb);
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(bias_unfold_kernel<float>, grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(bias_unfold_kernel<_Float16>, grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(bias_unfold_kernel<__bf16>, grid, dim3(256), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_proj(int dtype, const ProjArgs& a, hipStream_t st) {
+  const int total = a.B * a.H * a.ngroups * a.ncol_tiles;
+  if (total <= 0) return hipSuccess;
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(proj_kernel<float>, dim3(total), dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(proj_kernel<_Float16>, dim3(total), dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL(proj_kernel<__bf16>, dim3(total), dim3(kThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace relpos

@@ -1,0 +1,147 @@
+// qside.hpp -- the score tile in "lane = query" orientation, shared by the
+// forward kernel and the query-parallel backward kernel.
+//
+// Source: "Fast and Exact Relative-Position Attention via Structure-Aware
+// Kernels" (nanless.github.io digest), sections on the score formula (Eq. 2:
+// S_ij = tau (q_i.k_j + Z^Q[i, r] + Z^K[j, r] + b[r]) + M_ij) and on constant
+// tiles:
+//  * two comparisons of a tile's extreme offsets against the thresholds tell
+//    whether the whole tile maps to the first row (LO), the last row (HI) or
+//    crosses the band (BAND);
+//  * on a constant tile the query term and b are one scalar per query, added
+//    outside the tile, and the key term one scalar per key;
+//  * only band tiles look up a row per score.
+//
+// Orientation: S^T = K Q^T is computed with K rows as MFMA operand A (loaded
+// with the sigma row permutation) and the wave's 32 queries as operand B, so
+// lane l owns query l % 32 and 16 keys per 32-key subtile.  Row statistics of
+// the softmax are then lane-local up to one exchange with lane l ^ 32.
+// The key-side scalars seed the MFMA accumulator, so adding them costs no
+// vector instruction.
+#pragma once
+#include "tiles.hpp"
+
+namespace relpos {
+
+enum : int { KIND_LO = 0, KIND_BAND = 1, KIND_HI = 2 };
+
+// Kind of the tile of keys [j0, j0 + 64) for the 32 queries [iw0, iw0 + 32).
+__device__ inline int tile_kind_q(const Geo& g, int j0, int iw0) {
+  int omax = j0 + kTile - 1 - iw0;
+  int omin = j0 - (iw0 + 31);
+  return omax <= g.lo ? KIND_LO : (omin >= g.hi ? KIND_HI : KIND_BAND);
+}
+
+struct QCtx {
+  int iq;                // this lane's query
+  int hl;                // lane half (l / 32)
+  int sig;               // sigma(l % 32)
+  int kv_end;            // keys >= kv_end are masked
+  int wsq;               // first unfolded row of this group's Z^Q window
+  const float* zq_row;   // Z^Q row of iq (valid when has_zq and iq < N)
+  const float* zkb;      // Z^K of this (b, h)
+  const float* bun;      // unfolded b of this head
+  bool has_zq, has_zk, has_b;
+};
+
+// Relation response rel(i, j) for a band entry (0 for masked entries).
+__device__ inline float band_rel(const Geo& g, const QCtx& c, int j, int i) {
+  float v = 0.f;
+  int r = rrow(g, j - i);
+  if (c.has_zq) v += c.zq_row[r - c.wsq];
+  if (c.has_zk) v += c.zkb[(int64_t)j * g.W + r - win_k(g, j / kGroup)];
+  if (c.has_b) v += c.bun[r];
+  return v;
+}
+
+// Raw scores of keys [j0, j0 + 64) for this lane's query, masked entries = -inf.
+// s[st][e] <-> key j0 + 32*st + kappa(hl, e).  The per-query constant of a
+// saturated tile (Z^Q of the saturated row plus b) is NOT included.
+template <typename T>
+__device__ inline void qside_scores(f32x16 (&s)[2], const Geo& g, const QCtx& c, const T* sK,
+                                    const float* sZK, const typename MT<T>::frag* qf, int kind,
+                                    int j0, bool needmask) {
+  using M = MT<T>;
+  constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
+  if (kind != KIND_BAND) {
+    if (c.has_zk) {
+      const float* z = sZK + (kind == KIND_LO ? 0 : kTile);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float v[16];
+        lds_rows16<T>(z + 32 * st, c.hl, v);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[st][e] = v[e];
+      }
+    } else {
+      s[0] = zero16();
+      s[1] = zero16();
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int j = j0 + 32 * st + kappa<T>(c.hl, e);
+        bool live = c.iq < g.N && j < c.kv_end && !(g.causal && j > c.iq);
+        s[st][e] = live ? band_rel(g, c, j, c.iq) : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < NSD; ++ks) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      s[st] = M::mma(frag_rm<T>(sK, 32 * st + c.sig, KS * ks + E * c.hl), qf[ks], s[st]);
+    }
+  }
+  if (needmask) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int j = j0 + 32 * st + kappa<T>(c.hl, e);
+        if (j >= c.kv_end || (g.causal && j > c.iq)) s[st][e] = -INFINITY;
+      }
+    }
+  }
+}
+
+// Saturated-row constants of this lane's query: Z^Q[i, first/last row] + b.
+// Columns outside the group's live window are never used for a live entry;
+// they read as 0 so that no uninitialised value enters the arithmetic.
+__device__ inline void qside_consts(const Geo& g, const QCtx& c, int grp, float& lo_c,
+                                    float& hi_c) {
+  lo_c = 0.f;
+  hi_c = 0.f;
+  if (c.has_zq && c.iq < g.N) {
+    int cb, ce;
+    cols_q(g, grp, cb, ce);
+    int c0 = 0 - c.wsq, c1 = g.R - 1 - c.wsq;
+    if (c0 >= cb && c0 < ce) lo_c += c.zq_row[c0];
+    if (c1 >= cb && c1 < ce) hi_c += c.zq_row[c1];
+  }
+  if (c.has_b) {
+    lo_c += c.bun[0];
+    hi_c += c.bun[g.R - 1];
+  }
+}
+
+// Key-side saturated scalars of key j (Z^K[j, first/last row]); 0 outside the
+// key group's live window or beyond N.
+__device__ inline void kside_sat(const Geo& g, const float* zkb, int j, float& z0, float& z1) {
+  z0 = 0.f;
+  z1 = 0.f;
+  if (j < g.N) {
+    int grp = j / kGroup;
+    int wk = win_k(g, grp);
+    int cb, ce;
+    cols_k(g, grp, cb, ce);
+    const float* zr = zkb + (int64_t)j * g.W;
+    int c0 = 0 - wk, c1 = g.R - 1 - wk;
+    if (c0 >= cb && c0 < ce) z0 = zr[c0];
+    if (c1 >= cb && c1 < ce) z1 = zr[c1];
+  }
+}
+
+}  // namespace relpos

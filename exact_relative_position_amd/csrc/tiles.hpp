@@ -1,0 +1,164 @@
+// tiles.hpp -- staging of 64 x 64 operand tiles from HBM into LDS.
+//
+// A tile is 64 rows (tokens) x 64 columns (head dim) of the input dtype.
+// It is kept in LDS row-major ("RM", rows padded to PITCH elements) and, for
+// 16-bit types, also transposed ("TR", [column][row]) when an MFMA needs the
+// token index as its contraction index: the contraction index must be
+// contiguous inside a lane's fragment.  fp32 fragments hold one element, so
+// fp32 tiles are only stored row-major and the transposed view reads them
+// with swapped indices.
+//
+// Two thread->chunk maps are used for the HBM loads (a chunk is 16 bytes):
+//  * row map: 8 lanes cover one row (coalesced), used for RM-only tiles;
+//  * col map: 64 consecutive lanes cover 64 rows at one column chunk, which
+//    makes the 2-byte transposed LDS writes hit 32 distinct banks.
+#pragma once
+#include "device.hpp"
+
+namespace relpos {
+
+constexpr int kTile = 64;        // inner-loop tile
+constexpr int kThreads = 256;
+
+template <typename T>
+struct TileCfg {
+  static constexpr bool kHalf = sizeof(T) == 2;
+  static constexpr int PITCH = kHalf ? 72 : 65;      // elements per LDS row
+  static constexpr int ELEMS = 64 * PITCH;
+  static constexpr int CH = 16 / sizeof(T);          // elements per 16-byte chunk
+  static constexpr int NCH = 64 * 64 / CH / kThreads;  // chunks per thread
+};
+
+struct alignas(16) Chunk {
+  uint32_t w[4];
+};
+
+template <typename T, bool COLMAP>
+__device__ inline void chunk_pos(int c, int& row, int& col) {
+  constexpr int CH = TileCfg<T>::CH;
+  if (COLMAP) {
+    row = c & 63;
+    col = (c >> 6) * CH;
+  } else {
+    row = c / (64 / CH);
+    col = (c % (64 / CH)) * CH;
+  }
+}
+
+// Load rows [row0, row0 + 64) of a [*, 64] matrix (row stride sn elements);
+// rows >= nrows read as zero.
+template <typename T, bool COLMAP>
+__device__ inline void tile_load(Chunk (&r)[TileCfg<T>::NCH], const T* base, int64_t sn, int row0,
+                                 int nrows, int tid) {
+#pragma unroll
+  for (int u = 0; u < TileCfg<T>::NCH; ++u) {
+    int row, col;
+    chunk_pos<T, COLMAP>(tid + kThreads * u, row, col);
+    if (row0 + row < nrows) {
+      r[u] = *reinterpret_cast<const Chunk*>(base + (int64_t)(row0 + row) * sn + col);
+    } else {
+      r[u] = Chunk{{0u, 0u, 0u, 0u}};
+    }
+  }
+}
+
+template <typename T, bool COLMAP>
+__device__ inline void tile_store_rm(T* lds, const Chunk (&r)[TileCfg<T>::NCH], int tid) {
+  constexpr int P = TileCfg<T>::PITCH;
+#pragma unroll
+  for (int u = 0; u < TileCfg<T>::NCH; ++u) {
+    int row, col;
+    chunk_pos<T, COLMAP>(tid + kThreads * u, row, col);
+    if constexpr (TileCfg<T>::kHalf) {
+      *reinterpret_cast<Chunk*>(lds + row * P + col) = r[u];
+    } else {
+      const float* f = reinterpret_cast<const float*>(&r[u]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) lds[row * P + col + t] = f[t];
+    }
+  }
+}
+
+// 16-bit only: write the transposed tile lds[col][row] from col-map chunks.
+template <typename T>
+__device__ inline void tile_store_tr(T* lds, const Chunk (&r)[TileCfg<T>::NCH], int tid) {
+  constexpr int P = TileCfg<T>::PITCH;
+  static_assert(TileCfg<T>::kHalf, "transposed tiles are for 16-bit types");
+#pragma unroll
+  for (int u = 0; u < TileCfg<T>::NCH; ++u) {
+    int row, col;
+    chunk_pos<T, true>(tid + kThreads * u, row, col);
+    const T* e = reinterpret_cast<const T*>(&r[u]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) lds[(col + t) * P + row] = e[t];
+  }
+}
+
+// Fragment of row `row`, columns [col, col + E) of an RM tile.
+template <typename T>
+__device__ inline typename MT<T>::frag frag_rm(const T* lds, int row, int col) {
+  if constexpr (TileCfg<T>::kHalf) {
+    return *reinterpret_cast<const typename MT<T>::frag*>(lds + row * TileCfg<T>::PITCH + col);
+  } else {
+    return lds[row * TileCfg<T>::PITCH + col];
+  }
+}
+// Fragment of the transposed view: element (row, col..col+E) of X^T where X
+// is the staged tile (TR layout for 16-bit, RM read with swapped indices for fp32).
+template <typename T>
+__device__ inline typename MT<T>::frag frag_t(const T* lds, int row, int col) {
+  if constexpr (TileCfg<T>::kHalf) {
+    return *reinterpret_cast<const typename MT<T>::frag*>(lds + row * TileCfg<T>::PITCH + col);
+  } else {
+    return lds[col * TileCfg<T>::PITCH + row];
+  }
+}
+
+// Fragment straight from HBM: row pointer p, columns [col, col + E).
+template <typename T>
+__device__ inline typename MT<T>::frag frag_g(const T* p, int col) {
+  if constexpr (TileCfg<T>::kHalf) {
+    return *reinterpret_cast<const typename MT<T>::frag*>(p + col);
+  } else {
+    return p[col];
+  }
+}
+
+// The 16 per-row values of a 32-row subtile in result-element order
+// (element e <- v[kappa(h, e)]), read from an fp32 LDS vector.
+template <typename T>
+__device__ inline void lds_rows16(const float* v, int h, float (&out)[16]) {
+  if constexpr (TileCfg<T>::kHalf) {
+    const f32x4* a = reinterpret_cast<const f32x4*>(v + 8 * h);
+    const f32x4* b = reinterpret_cast<const f32x4*>(v + 16 + 8 * h);
+    f32x4 x0 = a[0], x1 = a[1], y0 = b[0], y1 = b[1];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      out[t] = x0[t];
+      out[4 + t] = x1[t];
+      out[8 + t] = y0[t];
+      out[12 + t] = y1[t];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[e] = v[kappa<T>(h, e)];
+  }
+}
+
+// Store 4 consecutive outputs (fp32 values) as dtype T.
+template <typename T>
+__device__ inline void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (TileCfg<T>::kHalf) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    v4 x;
+    x[0] = MT<T>::from_f(a);
+    x[1] = MT<T>::from_f(b);
+    x[2] = MT<T>::from_f(c);
+    x[3] = MT<T>::from_f(d);
+    *reinterpret_cast<v4*>(p) = x;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+  }
+}
+
+}  // namespace relpos

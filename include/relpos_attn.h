@@ -1,0 +1,240 @@
+/*
+ * relpos_attn.h -- C ABI of the exact relative-position attention library
+ * (gfx950 / MI355X, hand-written HIP kernels).
+ *
+ * The operation is the one described in "Fast and Exact Relative-Position
+ * Attention via Structure-Aware Kernels" (Boychev, Petrov, Dimitrov; digest on
+ * nanless.github.io), section on the score formula, Eq. (1):
+ *
+ *   S_ij = tau * ( q_i.k_j + q_i.aQ[phi(i,j)] + k_j.aK[phi(i,j)] + b[phi(i,j)] ) + M_ij
+ *   P    = softmax_j(S),   O = P V,   LSE_i = log sum_j exp(S_ij)
+ *
+ * computed FlashAttention-style (no N x N matrix is ever stored), forward and
+ * backward.  Eq. (2)/(3) of the same section rewrite the two vector terms as
+ * scalar lookups Z^Q[i, r] = q_i.aQ[r] and Z^K[j, r] = k_j.aK[r]; the library
+ * stores those projections (fp32) for the reachable offset window only
+ * (section on the grouped reachable range), adds them on chip, and in the
+ * backward accumulates dS per offset with a single writer per entry (section
+ * on the backward pass, Eq. (4)), then contracts to the table gradients.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates or frees device memory; scratch comes from `workspace`.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it and return without synchronising the host.
+ *  - Every argument is validated before anything is launched; on an error
+ *    nothing is written and the status says why (see relpos_last_error()).
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Results are bitwise reproducible run to run: no atomics, fixed
+ *    summation orders.
+ *  - Thread-safe; no global state except the thread-local error message.
+ */
+#ifndef RELPOS_ATTN_H
+#define RELPOS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum relpos_status {
+  RELPOS_OK = 0,
+  RELPOS_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size, bad descriptor */
+  RELPOS_ERR_UNSUPPORTED = -2,  /* valid request the kernels do not implement (e.g. d != 64) */
+  RELPOS_ERR_WORKSPACE = -3,    /* workspace smaller than relpos_attn_workspace_size() */
+  RELPOS_ERR_HIP = -4           /* a HIP launch failed */
+} relpos_status;
+
+/* Element type of Q, K, V, O, dO, dQ, dK, dV and of the tables aQ, aK, b. */
+typedef enum relpos_dtype { RELPOS_F32 = 0, RELPOS_F16 = 1, RELPOS_BF16 = 2 } relpos_dtype;
+
+/* Offset maps phi(i, j) = phi(o), o = j - i (key index minus query index).
+ * The setup section of the page lists the maps per mechanism:
+ *  TRUNCATED (Shaw, DeBERTa as configured):  r = clip(o, lo, hi) - lo,  R = hi - lo + 1
+ *  BUCKET_T5 (T5): standard T5 relative bucket (num_buckets, max_exact,
+ *            max_distance, bidirectional), R = num_buckets.  Inside the
+ *            library the bucketed map is unfolded into a truncated map whose
+ *            rows are copies of bucket rows (section on constant tiles), and
+ *            the copied gradient columns are folded back in ascending offset.
+ *  IDENTITY (Transformer-XL): r = o + N - 1, R = 2N - 1. */
+typedef enum relpos_phi_kind {
+  RELPOS_PHI_TRUNCATED = 0,
+  RELPOS_PHI_BUCKET_T5 = 1,
+  RELPOS_PHI_IDENTITY = 2
+} relpos_phi_kind;
+
+typedef struct relpos_phi {
+  int32_t kind;           /* relpos_phi_kind */
+  int32_t lo, hi;         /* TRUNCATED: lo <= hi */
+  int32_t num_buckets;    /* BUCKET_T5: >= 2 (even when bidirectional) */
+  int32_t max_exact;      /* BUCKET_T5: 0 = default (half of the buckets per side, halved) */
+  int32_t max_distance;   /* BUCKET_T5: > max_exact */
+  int32_t bidirectional;  /* BUCKET_T5: 1 = keys after the query use the upper half */
+} relpos_phi;
+
+/* Additive mask M_ij of Eq. (1): 0 or -inf. */
+enum {
+  RELPOS_MASK_NONE = 0,
+  RELPOS_MASK_CAUSAL = 1,       /* M_ij = -inf for j > i */
+  RELPOS_MASK_KEY_PADDING = 2   /* M_ij = -inf for j >= key_len[batch] */
+};
+typedef struct relpos_mask {
+  int32_t flags;            /* OR of the RELPOS_MASK_* bits */
+  const int32_t* key_len;   /* device int32[B]; required iff KEY_PADDING; values clamped to [0, N] */
+} relpos_mask;
+
+/* Roles of the [B, H, N, d] tensors, used to index relpos_problem.strides. */
+enum {
+  RELPOS_T_Q = 0, RELPOS_T_K, RELPOS_T_V, RELPOS_T_O,
+  RELPOS_T_DO, RELPOS_T_DQ, RELPOS_T_DK, RELPOS_T_DV,
+  RELPOS_T_COUNT
+};
+
+/* Problem descriptor.
+ *  - Tensors are [B, H, N, d] with d contiguous; strides[role] = {batch, head,
+ *    row} strides in ELEMENTS.  Each stride must be a multiple of 8 elements
+ *    (16 bytes) and every tensor pointer 16-byte aligned.
+ *  - Tables: aQ, aK are [H, R, d] (rows contiguous, row stride d), b is [H, R];
+ *    their head strides are given in elements and may be 0 (one table shared
+ *    by all heads; its gradient is then summed over heads).
+ *  - tau > 0 (the softmax scale of Eq. (1)).
+ *  - d must be 64 (ERR_UNSUPPORTED otherwise); any N >= 0 (N = 0 is a no-op). */
+typedef struct relpos_problem {
+  int64_t B, H, N, d;
+  int32_t dtype;            /* relpos_dtype */
+  float tau;
+  int64_t strides[RELPOS_T_COUNT][3];
+  int64_t aq_head_stride;   /* elements; 0 = shared */
+  int64_t ak_head_stride;
+  int64_t b_head_stride;
+} relpos_problem;
+
+/* Which relation terms are present (a "= 0" table is simply absent). */
+enum { RELPOS_TERM_AQ = 1, RELPOS_TERM_AK = 2, RELPOS_TERM_B = 4 };
+/* Pass selector for relpos_attn_workspace_size. */
+enum { RELPOS_PASS_FWD = 0, RELPOS_PASS_BWD = 1 };
+
+/* Bytes of device workspace relpos_attn_fwd (pass = FWD) or relpos_attn_bwd
+ * (pass = BWD) needs for this problem.  `zsave_given` says whether the caller
+ * will pass a zsave buffer (then the projections do not live in the
+ * workspace).  Host-only; launches nothing. */
+relpos_status relpos_attn_workspace_size(const relpos_problem* prob, const relpos_phi* phi,
+                                         const relpos_mask* mask, int32_t terms, int32_t pass,
+                                         int32_t zsave_given, size_t* bytes);
+
+/* Bytes of the optional buffer in which the forward keeps the relation
+ * projections Z^Q, Z^K (fp32, reachable window only) for the backward
+ * (keeping them trades memory for recomputation, section on ablations).
+ * 0 when no vector table is present.  Host-only. */
+relpos_status relpos_attn_zsave_size(const relpos_problem* prob, const relpos_phi* phi,
+                                     int32_t terms, size_t* bytes);
+
+/* Forward of Eq. (1).
+ *  Q, K, V   : device [B,H,N,d], dtype prob->dtype (strides Q, K, V).
+ *  aQ, aK, b : device tables or NULL when the term is absent.
+ *  O         : device [B,H,N,d] output, dtype prob->dtype (strides O).
+ *  lse       : device float32 [B,H,N] contiguous output, natural-log LSE
+ *              (-inf for a row whose keys are all masked; its O row is 0).
+ *  zsave     : device buffer of relpos_attn_zsave_size() bytes or NULL.  When
+ *              given, the projections are written there for the backward.
+ *  workspace : device scratch of at least relpos_attn_workspace_size(FWD).  */
+relpos_status relpos_attn_fwd(const relpos_problem* prob, const relpos_phi* phi,
+                              const relpos_mask* mask,
+                              const void* Q, const void* K, const void* V,
+                              const void* aQ, const void* aK, const void* b,
+                              void* O, float* lse, void* zsave,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward: gradients of sum(O * dO) (section on the backward pass).
+ *  O, lse    : the forward's outputs for the same inputs.
+ *  dO        : device [B,H,N,d] (strides DO).
+ *  zsave     : the buffer filled by relpos_attn_fwd, or NULL to recompute
+ *              the projections into the workspace.
+ *  dQ, dK, dV: device [B,H,N,d] outputs, dtype prob->dtype (strides DQ, DK, DV).
+ *  daQ, daK  : device float32 [Ho, R, d] contiguous outputs, Ho = H (or 1 for a
+ *              shared table); must be NULL exactly when the table is absent.
+ *  db        : device float32 [Ho, R] contiguous output; NULL iff b is absent.
+ *  workspace : device scratch of at least relpos_attn_workspace_size(BWD).  */
+relpos_status relpos_attn_bwd(const relpos_problem* prob, const relpos_phi* phi,
+                              const relpos_mask* mask,
+                              const void* Q, const void* K, const void* V,
+                              const void* aQ, const void* aK, const void* b,
+                              const void* O, const float* lse, const void* dO,
+                              const void* zsave,
+                              void* dQ, void* dK, void* dV,
+                              float* daQ, float* daK, float* db,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages of the two passes, for callers that schedule them separately (for
+ * example to overlap the key-parallel pass with other work, or to time each
+ * kernel).  The pipeline section of the page orders the forward as relation
+ * projection, then the fused tiled attention; the backward section as the
+ * query-parallel pass, the key-parallel pass, then the final contraction.
+ *  FWD_PROJECT   map tables (T5 unfold) and Z^Q, Z^K of the reachable window
+ *                (Eq. 3; section on the grouped reachable range)
+ *  FWD_ATTEND    fused forward: O and LSE
+ *  BWD_PREPARE   map tables, projections (only when zsave is NULL) and the
+ *                row terms D_i = sum_d dO_id O_id
+ *  BWD_QUERY_PASS  dQ (partial when aQ is present) and dZ^Q per offset
+ *  BWD_KEY_PASS    dK (partial when aK is present), dV and dZ^K per offset
+ *  BWD_CONTRACT    dQ += dZ^Q aQ, dK += dZ^K aK, daQ, daK, db, bucket fold
+ * relpos_attn_fwd_stages / relpos_attn_bwd_stages take the same arguments as
+ * relpos_attn_fwd / relpos_attn_bwd plus a stage mask; the stages given run
+ * in the order above.  Intermediate results live in `workspace` (and
+ * `zsave`), so a pass split over several calls must pass identical
+ * arguments and the same buffers to every call, on the same stream.
+ * relpos_attn_fwd and relpos_attn_bwd are these calls with every stage. */
+enum { RELPOS_FWD_PROJECT = 1, RELPOS_FWD_ATTEND = 2, RELPOS_FWD_ALL = 3 };
+enum {
+  RELPOS_BWD_PREPARE = 1,
+  RELPOS_BWD_QUERY_PASS = 2,
+  RELPOS_BWD_KEY_PASS = 4,
+  RELPOS_BWD_CONTRACT = 8,
+  RELPOS_BWD_ALL = 15
+};
+
+relpos_status relpos_attn_fwd_stages(const relpos_problem* prob, const relpos_phi* phi,
+                                     const relpos_mask* mask,
+                                     const void* Q, const void* K, const void* V,
+                                     const void* aQ, const void* aK, const void* b,
+                                     void* O, float* lse, void* zsave,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     int32_t stages);
+
+relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_phi* phi,
+                                     const relpos_mask* mask,
+                                     const void* Q, const void* K, const void* V,
+                                     const void* aQ, const void* aK, const void* b,
+                                     const void* O, const float* lse, const void* dO,
+                                     const void* zsave,
+                                     void* dQ, void* dK, void* dV,
+                                     float* daQ, float* daK, float* db,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     int32_t stages);
+
+/* Host-side facts about a map at length N: R (rows of the caller's tables),
+ * and the truncated map the library unfolds it into, [lo_unf, hi_unf]
+ * (R_unf = hi_unf - lo_unf + 1 rows).  For T5 the unfolded thresholds are
+ * the first offsets beyond which the bucket no longer changes. */
+relpos_status relpos_phi_info(const relpos_phi* phi, int64_t N, int64_t* R, int64_t* lo_unf,
+                              int64_t* hi_unf);
+
+/* Device-computed row tables (exported so they can be checked bit for bit):
+ *  rows[o + N - 1]     = phi(o) for every o in [-(N-1), N-1]       (int32[2N-1])
+ *  fold[u]             = original row of unfolded row u, u in [0, R_unf)  (int32[R_unf])
+ * Either pointer may be NULL.  Enqueued on `stream`. */
+relpos_status relpos_phi_rows(const relpos_phi* phi, int64_t N, int32_t* rows, int32_t* fold,
+                              void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* relpos_status_string(int32_t status);
+/* Message describing the last error on the calling thread ("" if none). */
+const char* relpos_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RELPOS_ATTN_H */

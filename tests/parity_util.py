@@ -1,0 +1,105 @@
+"""Shared helpers of the parity tests: run the HIP path and the oracle on the
+same seeded inputs and compare them (test infrastructure only)."""
+
+import numpy as np
+import torch
+
+import oracle
+from relpos_synth import as_f64, make_inputs  # noqa: F401
+
+# Tolerances, max |x - ref| / max |ref| per tensor.
+#  fp16: 2e-3 on O and 1e-2 on every gradient (fp16 inputs, fp32 accumulation).
+#  bf16: O to 2 * 2^-8 (two bf16 unit roundoffs: O is stored in bf16, up to
+#        2^-9 |O|, and P is rounded to bf16 before P V, up to 2^-9 per term);
+#        gradients keep 1e-2.
+#  fp32: 1e-4 on everything (no 16-bit rounding anywhere on the path).
+# LSE is fp32 in every case: absolute 2e-3.
+# A reference that is identically zero in exact arithmetic (max |ref| below
+# 1e-12, e.g. table gradients when every offset maps to one row) is checked
+# absolutely: max |x| <= ZERO_ABS.
+TOL = {"f16": (2e-3, 1e-2), "bf16": (2.0 ** -7, 1e-2), "f32": (1e-4, 1e-4)}
+TOL_O, TOL_G = TOL["f16"]
+TOL_LSE_ABS = 2e-3
+ZERO_ABS = 1e-4
+ALL_OUTPUTS = ("O", "lse", "dq", "dk", "dv", "daq", "dak", "db")
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU test run without a visible GPU"
+    import exact_relative_position_amd._binding as b
+    b.lib()  # raises if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def gpu_run(w, x, dev, keep_z=True, backward=True):
+    import exact_relative_position_amd as rp
+    t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    O, lse, zs = rp.forward(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], phi=w.phi,
+                            tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=keep_z)
+    out = {"O": O, "lse": lse}
+    if backward:
+        dq, dk, dv, daq, dak, db = rp.backward(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"],
+                                               O, lse, t["do"], zs, phi=w.phi, tau=w.tau,
+                                               causal=w.causal, key_len=t["key_len"])
+        out.update(dq=dq, dk=dk, dv=dv, daq=daq, dak=dak, db=db)
+    torch.cuda.synchronize(dev)
+    return {k: (None if v is None else v.detach().cpu().double().numpy()) for k, v in out.items()}
+
+
+def oracle_run(w, x, bh=None, query_rows=None, backward=True):
+    f = {k: as_f64(v) for k, v in x.items() if k != "key_len"}
+    kl = None if x["key_len"] is None else x["key_len"].numpy()
+    O, L = oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi, tau=w.tau,
+                          causal=w.causal, key_len=kl, bh=bh, query_rows=query_rows)
+    out = {"O": O, "lse": L}
+    if backward:
+        g = oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"],
+                            phi=w.phi, tau=w.tau, causal=w.causal, key_len=kl, bh=bh,
+                            query_rows=query_rows)
+        out.update(g)
+    return out
+
+
+def rel_err(x, ref):
+    """max |x - ref| / max |ref|; absolute max |x| when ref is identically zero."""
+    x, ref = np.asarray(x), np.asarray(ref)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(x)), "non-finite entries differ"
+    if not fin.any():
+        return 0.0
+    assert np.array_equal(x[~fin], ref[~fin])
+    scale = np.abs(ref[fin]).max()
+    diff = np.abs(x[fin] - ref[fin]).max()
+    if scale < 1e-12:
+        return float(np.abs(x[fin]).max())
+    return float(diff / scale)
+
+
+def tolerances(dtype):
+    return TOL[dtype]
+
+
+def compare(got, ref, names, sel=None, tol_o=TOL_O, tol_g=TOL_G, label=""):
+    """Assert the tolerances on the named outputs; ``sel`` indexes a subset."""
+    report = {}
+    for n in names:
+        if ref.get(n) is None:
+            assert got.get(n) is None, n
+            continue
+        a, r = got[n], ref[n]
+        if sel is not None:
+            a, r = a[sel], r[sel]
+        if n == "lse":
+            fin = np.isfinite(r)
+            assert np.array_equal(fin, np.isfinite(a)), f"{label} lse: -inf rows differ"
+            err = float(np.abs(a[fin] - r[fin]).max()) if fin.any() else 0.0
+            report[n] = err
+            assert err <= TOL_LSE_ABS, f"{label} lse abs err {err:.3e}"
+            continue
+        err = rel_err(a, r)
+        report[n] = err
+        tol = tol_o if n == "O" else tol_g
+        if np.abs(r[np.isfinite(r)]).max(initial=0.0) < 1e-12:
+            tol = ZERO_ABS
+        assert err <= tol, f"{label} {n}: err {err:.3e} > {tol:.1e}"
+    return report
