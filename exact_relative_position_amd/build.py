@@ -2,7 +2,9 @@
 
 Every source is compiled with hipcc for gfx950 only.  Packed-fp32 VALU
 instructions are disabled (``-packed-fp32-ops``); the host pass prints a
-harmless warning that it does not know that feature.
+harmless warning that it does not know that feature.  MFMA results are kept
+in ordinary VGPRs (``-amdgpu-mfma-vgpr-form``), which removes the copies
+between accumulation and architectural registers around every MFMA.
 """
 
 import os
@@ -30,6 +32,8 @@ ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (gfx950 allows it): no AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"), "-I" + SRC,
     "-Wall", "-Wno-unused-function",
 ]

@@ -144,16 +144,19 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[st][e] = exp2_fast(fmaf(s[st][e], sc2, off));
-          lsum += p[st][e];
-        }
+        for (int e = 0; e < 16; ++e) p[st][e] = exp2_fast(fmaf(s[st][e], sc2, off));
+      // P is rounded to the input type for P V; the normaliser sums the same
+      // rounded values, in independent chains per fragment
       frag pf[NSK];
+      float part[NSK];
 #pragma unroll
       for (int ks = 0; ks < NSK; ++ks) {
         const int st = (ks * KS) / 32, e0 = ((ks * KS) % 32) / KS * E;
         pf[ks] = M::pack(&p[st][e0]);
+        part[ks] = M::sum_acc(pf[ks], 0.f);
       }
+#pragma unroll
+      for (int ks = 0; ks < NSK; ++ks) lsum += part[ks];
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll

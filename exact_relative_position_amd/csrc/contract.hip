@@ -58,22 +58,41 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
     }
 
   for (int c0 = cb; c0 < ce; c0 += 64) {
-    // stage dZ[i0 .. i0+127][c0 .. c0+63] and the 64 table rows (as fp32)
-    for (int idx = tid; idx < kBlockRows * 64; idx += kThreads) {
-      const int r = idx >> 6, cc = idx & 63;
-      const int i = i0 + r, col = c0 + cc;
-      sZ[r * P + cc] = (i < N && col < ce) ? dzb[(int64_t)i * g.W + col] : 0.f;
-    }
-    for (int idx = tid; idx < 64 * 64; idx += kThreads) {
-      const int cc = idx >> 6, d = idx & 63;
-      const int col = c0 + cc;
-      float v = 0.f;
-      if (col < ce) {
-        const int u = ws + col;
-        const int r = a.fold ? a.fold[u] : u;
-        v = MT<T>::to_f(tab[(int64_t)r * kHeadDim + d]);
+    // stage dZ[i0 .. i0+127][c0 .. c0+63] and the 64 table rows (as fp32);
+    // all loads of a thread are issued before its LDS stores
+    {
+      float zv[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int idx = tid + kThreads * u;
+        const int r = idx >> 6, cc = idx & 63;
+        const int i = i0 + r, col = c0 + cc;
+        zv[u] = (i < N && col < ce) ? dzb[(int64_t)i * g.W + col] : 0.f;
       }
-      sT[cc * P + d] = v;
+      float tv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int idx = tid + kThreads * u;
+        const int cc = idx >> 6, d = idx & 63;
+        const int col = c0 + cc;
+        float v = 0.f;
+        if (col < ce) {
+          const int uu = ws + col;
+          const int r = a.fold ? a.fold[uu] : uu;
+          v = MT<T>::to_f(tab[(int64_t)r * kHeadDim + d]);
+        }
+        tv[u] = v;
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int idx = tid + kThreads * u;
+        sZ[(idx >> 6) * P + (idx & 63)] = zv[u];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int idx = tid + kThreads * u;
+        sT[(idx >> 6) * P + (idx & 63)] = tv[u];
+      }
     }
     __syncthreads();
 #pragma unroll 4
@@ -144,17 +163,25 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
       const int col = u - ws;
       const bool colv = col >= cb && col < ce;
       const int i_end = (int)(fend - (int64_t)seg * N);
-      for (int ip = i_start + 2 * w; ip < i_end; ip += 8) {
-        const int i = ip + hl;
-        const bool rv = i < i_end;
-        const float av = (rv && colv) ? dzb[(int64_t)i * g.W + col] : 0.f;
-        csum += av;
-        if (a.want_x) {
+      // each wave takes 16 consecutive rows (8 MFMA k-steps) per round, loads first
+      for (int ib = i_start + 16 * w; ib < i_end; ib += 64) {
+        float av[8], bv[8][2];
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const int i = ib + 2 * s2 + hl;
+          const bool rv = i < i_end;
+          av[s2] = (rv && colv) ? dzb[(int64_t)i * g.W + col] : 0.f;
           const T* xr = xb + (int64_t)i * a.sx.n;
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const float bv = rv ? MT<T>::to_f(xr[32 * nt + l32]) : 0.f;
-            acc[nt] = mma32(av, bv, acc[nt]);
+          for (int nt = 0; nt < 2; ++nt)
+            bv[s2][nt] = (rv && a.want_x) ? MT<T>::to_f(xr[32 * nt + l32]) : 0.f;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          csum += av[s2];
+          if (a.want_x) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[nt] = mma32(av[s2], bv[s2][nt], acc[nt]);
           }
         }
       }

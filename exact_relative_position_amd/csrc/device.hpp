@@ -51,6 +51,14 @@ struct MT<_Float16> {
   }
   __device__ static inline float to_f(_Float16 x) { return (float)x; }
   __device__ static inline _Float16 from_f(float x) { return (_Float16)x; }
+  // acc + sum of the 8 elements of a fragment (v_dot2 against ones)
+  __device__ static inline float sum_acc(frag f, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(h2{f[2 * i], f[2 * i + 1]}, one, acc, false);
+    return acc;
+  }
 };
 
 template <>
@@ -74,6 +82,14 @@ struct MT<__bf16> {
   }
   __device__ static inline float to_f(__bf16 x) { return (float)x; }
   __device__ static inline __bf16 from_f(float x) { return (__bf16)x; }
+  __device__ static inline float sum_acc(frag f, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(b2{f[2 * i], f[2 * i + 1]}, one, acc, false);
+    return acc;
+  }
 };
 
 template <>
@@ -87,6 +103,7 @@ struct MT<float> {
   __device__ static inline frag pack(const float* p) { return p[0]; }
   __device__ static inline float to_f(float x) { return x; }
   __device__ static inline float from_f(float x) { return x; }
+  __device__ static inline float sum_acc(frag f, float acc) { return acc + f; }
 };
 
 // Tile row held by result element e of lane-half h (see header comment).

@@ -63,19 +63,22 @@ __device__ inline void qside_scores(f32x16 (&s)[2], const Geo& g, const QCtx& c,
                                     int j0, bool needmask) {
   using M = MT<T>;
   constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
-  if (kind != KIND_BAND) {
-    if (c.has_zk) {
-      const float* z = sZK + (kind == KIND_LO ? 0 : kTile);
+  int ks0 = 0;
+  if (kind != KIND_BAND && !c.has_zk) {
+    // constant tile without a key term: the accumulator starts at literal zero
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float v[16];
-        lds_rows16<T>(z + 32 * st, c.hl, v);
+    for (int st = 0; st < 2; ++st)
+      s[st] = M::mma(frag_rm<T>(sK, 32 * st + c.sig, E * c.hl), qf[0], zero16());
+    ks0 = 1;
+  } else if (kind != KIND_BAND) {
+    // constant tile: one Z^K scalar per key seeds the accumulator
+    const float* z = sZK + (kind == KIND_LO ? 0 : kTile);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[st][e] = v[e];
-      }
-    } else {
-      s[0] = zero16();
-      s[1] = zero16();
+    for (int st = 0; st < 2; ++st) {
+      float v[16];
+      lds_rows16<T>(z + 32 * st, c.hl, v);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[st][e] = v[e];
     }
   } else {
 #pragma unroll
@@ -90,6 +93,7 @@ __device__ inline void qside_scores(f32x16 (&s)[2], const Geo& g, const QCtx& c,
   }
 #pragma unroll
   for (int ks = 0; ks < NSD; ++ks) {
+    if (ks < ks0) continue;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       s[st] = M::mma(frag_rm<T>(sK, 32 * st + c.sig, KS * ks + E * c.hl), qf[ks], s[st]);
