@@ -22,6 +22,7 @@ LIB = os.path.join(HERE, "librelpos_attn.so")
 SOURCES = [
     "api.cpp",
     "proj.hip",
+    "prep.hip",
     "attn_fwd.hip",
     "attn_bwd_q.hip",
     "attn_bwd_k.hip",

@@ -6,7 +6,8 @@
 //   map tables (T5 unfold) -> relation projection of the reachable window ->
 //   fused tiled forward.
 // Backward (backward section of the same page):
-//   D preprocess -> query-parallel pass -> key-parallel pass ->
+//   token-contiguous operand copies and the padded row terms (LSE, D) ->
+//   query-parallel pass -> key-parallel pass ->
 //   dZ . table into dQ / dK -> dZ^T . Q / K into the table gradients ->
 //   fold of copied bucket columns.
 #include <hip/hip_runtime.h>
@@ -21,7 +22,8 @@
 
 namespace relpos {
 hipError_t launch_fwd(int dtype, const AttnArgs& a, hipStream_t st);
-hipError_t launch_pre(int dtype, const PreArgs& p, hipStream_t st);
+hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st);
+hipError_t launch_rowterm(int dtype, const RowTermArgs& a, hipStream_t st);
 hipError_t launch_bwd_q(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_bwd_k(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_phi_rows(const PhiArgs& p, int32_t* rows, hipStream_t st);
@@ -55,6 +57,7 @@ int elem_size(int dtype) { return dtype == RELPOS_F32 ? 4 : 2; }
 struct Plan {
   int dtype = 0, esz = 0;
   int B = 0, H = 0, N = 0;
+  int Np = 0;      // N rounded up to the 64-token tile
   Geo geo{};
   PhiArgs phi{};
   int R = 0;       // rows of the caller's tables
@@ -142,6 +145,7 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   pl.B = (int)prob->B;
   pl.H = (int)prob->H;
   pl.N = (int)prob->N;
+  pl.Np = (pl.N + 63) / 64 * 64;
   pl.has_aq = terms & RELPOS_TERM_AQ;
   pl.has_ak = terms & RELPOS_TERM_AK;
   pl.has_b = terms & RELPOS_TERM_B;
@@ -219,6 +223,9 @@ relpos_status check_tensor(const Plan& pl, const relpos_problem* prob, int role,
   }
   if (prob->strides[role][2] < kHeadDim && pl.N > 1)
     return fail(RELPOS_ERR_INVALID_ARG, std::string("row stride smaller than d: ") + name);
+  // a 64-row tile is addressed with 32-bit byte offsets
+  if (prob->strides[role][2] > (int64_t(1) << 24))
+    return fail(RELPOS_ERR_UNSUPPORTED, std::string("row stride above 2^24 elements: ") + name);
   return RELPOS_OK;
 }
 
@@ -244,6 +251,7 @@ struct WsFwd {
   float* bunf = nullptr;
   float* zq = nullptr;
   float* zk = nullptr;
+  void* vt = nullptr;  // V^T copy [B*H][64][Np] (16-bit types)
 };
 
 struct WsBwd {
@@ -253,7 +261,11 @@ struct WsBwd {
   float* bunf = nullptr;
   float* zq = nullptr;
   float* zk = nullptr;
-  float* D = nullptr;
+  float* L2 = nullptr;  // [B*H][Np]
+  float* D = nullptr;   // [B*H][Np]
+  void* kt = nullptr;   // K^T, Q^T, dO^T copies [B*H][64][Np] (16-bit types)
+  void* qt = nullptr;
+  void* dot = nullptr;
   float* dq_part = nullptr;
   float* dk_part = nullptr;
   float* dzq = nullptr;
@@ -273,6 +285,7 @@ size_t carve_fwd(const Plan& pl, bool zsave_given, void* base, WsFwd& w) {
     if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
     if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
   }
+  if (pl.esz == 2) w.vt = c.take<char>(2 * (size_t)pl.B * pl.H * kHeadDim * pl.Np);
   return c.off;
 }
 
@@ -289,7 +302,14 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
     if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
     if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
   }
-  w.D = c.take<float>(sizeof(float) * bhn);
+  const size_t bhnp = (size_t)pl.B * pl.H * pl.Np;
+  w.L2 = c.take<float>(sizeof(float) * bhnp);
+  w.D = c.take<float>(sizeof(float) * bhnp);
+  if (pl.esz == 2) {
+    w.kt = c.take<char>(2 * bhnp * kHeadDim);
+    w.qt = c.take<char>(2 * bhnp * kHeadDim);
+    w.dot = c.take<char>(2 * bhnp * kHeadDim);
+  }
   if (pl.has_aq) w.dq_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_ak) w.dk_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_aq || pl.has_b) w.dzq = c.take<float>(sizeof(float) * pl.z_elems);
@@ -400,6 +420,7 @@ AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask
             (pl.keypad ? F_KEYPAD : 0) | ((pl.has_aq || pl.has_b) ? F_ZQ_NEEDED : 0);
   a.bunf_hs = pl.b_hs == 0 ? 0 : pl.Runf;
   a.nblk = pl.nblk;
+  a.Np = pl.Np;
   return a;
 }
 
@@ -541,6 +562,11 @@ relpos_status relpos_attn_fwd_stages(const relpos_problem* prob, const relpos_ph
   a.zq = w.zq;
   a.zk = w.zk;
   a.bunf = w.bunf;
+  if (pl.esz == 2) {
+    TransposeArgs t{V, str_of(prob, RELPOS_T_V), w.vt, pl.B, pl.H, pl.N, pl.Np};
+    if ((s = hip_check(launch_transpose(pl.dtype, t, st), "forward (V^T)")) != RELPOS_OK) return s;
+    a.vt = w.vt;
+  }
   return hip_check(launch_fwd(pl.dtype, a, st), "forward");
 }
 
@@ -623,7 +649,11 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   a.o = O;
   a.lse = const_cast<float*>(lse);
   a.dO = dO;
+  a.L2 = w.L2;
   a.D = w.D;
+  a.kt = w.kt;
+  a.qt = w.qt;
+  a.dot = w.dot;
   a.zq = w.zq;
   a.zk = w.zk;
   a.bunf = w.bunf;
@@ -633,9 +663,20 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   a.dzq = w.dzq;
   a.dzk = w.dzk;
   if (stages & RELPOS_BWD_PREPARE) {
-    PreArgs p{O, dO, str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), w.D, pl.B, pl.H, pl.N};
-    if ((s = hip_check(launch_pre(pl.dtype, p, st), "backward (row terms)")) != RELPOS_OK)
+    RowTermArgs r{O,   dO,  str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), lse, w.L2, w.D,
+                  pl.B, pl.H, pl.N, pl.Np};
+    if ((s = hip_check(launch_rowterm(pl.dtype, r, st), "backward (row terms)")) != RELPOS_OK)
       return s;
+    if (pl.esz == 2) {
+      const struct { const void* x; int role; void* xt; } cp[3] = {
+          {K, RELPOS_T_K, w.kt}, {Q, RELPOS_T_Q, w.qt}, {dO, RELPOS_T_DO, w.dot}};
+      for (const auto& c : cp) {
+        TransposeArgs t{c.x, str_of(prob, c.role), c.xt, pl.B, pl.H, pl.N, pl.Np};
+        if ((s = hip_check(launch_transpose(pl.dtype, t, st), "backward (operand copies)")) !=
+            RELPOS_OK)
+          return s;
+      }
+    }
   }
   if (stages & RELPOS_BWD_QUERY_PASS) {
     if ((s = hip_check(launch_bwd_q(pl.dtype, a, st), "backward (query pass)")) != RELPOS_OK)

@@ -9,58 +9,163 @@
 // block that owns the query (single writer, no atomics, fixed order); the two
 // saturated rows collect into two on-chip sums per query.
 //
-// D_i = sum_d dO_id O_id (the row term of dS = P (dP - D)) is the standard
-// FlashAttention backward preprocess, computed by pre_kernel.
+// One workgroup = one (batch, head, 128-query block); 4 waves x 32 queries;
+// per 64-key tile K, K^T (from a key-contiguous copy) and V are loaded
+// straight into LDS; the key loop runs in three segments like the forward.
 #include "qside.hpp"
 
 namespace relpos {
 
-// D[bh][i] = sum_d dO[i][d] * O[i][d]; 8 lanes per row.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void pre_kernel(PreArgs a) {
-  using C = TileCfg<T>;
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
-  const int part = threadIdx.x & 7;
-  float acc = 0.f;
-  if (row < rows) {
-    const int i = (int)(row % a.N);
-    const int64_t bh = row / a.N;
-    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-    const T* o = (const T*)a.o + b * a.so.b + h * a.so.h + (int64_t)i * a.so.n + 8 * part;
-    const T* d = (const T*)a.dO + b * a.sdo.b + h * a.sdo.h + (int64_t)i * a.sdo.n + 8 * part;
-    if constexpr (C::kHalf) {
-      typename MT<T>::frag x = *reinterpret_cast<const typename MT<T>::frag*>(o);
-      typename MT<T>::frag y = *reinterpret_cast<const typename MT<T>::frag*>(d);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc = fmaf(MT<T>::to_f(x[t]), MT<T>::to_f(y[t]), acc);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc = fmaf(o[t], d[t], acc);
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  if (row < rows && part == 0) a.D[row] = acc;
-}
+__device__ inline int floor_div_q(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+__device__ inline int ceil_div_q(int a, int b) { return -floor_div_q(-a, b); }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_q_kernel(AttnArgs a) {
+struct BwdQ {
   using M = MT<T>;
   using frag = typename M::frag;
-  using C = TileCfg<T>;
-  constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS, NSK = kTile / KS;
-  constexpr float kLog2e = 1.4426950408889634f;
+  static constexpr bool kHalf = sizeof(T) == 2;
+  static constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
+  static constexpr int KPS = 32 / KS;  // MFMA k-steps per 32-key half
+  static constexpr int TB = DTile<T>::BYTES;
 
-  __shared__ __align__(16) T sK[2][C::ELEMS];
-  __shared__ __align__(16) T sKt[C::kHalf ? 2 : 1][C::kHalf ? C::ELEMS : 1];
-  __shared__ __align__(16) T sV[2][C::ELEMS];
-  __shared__ __align__(16) float sZK[2][2 * kTile];
+  char* sK;     // [2][TB] K rows
+  char* sKt;    // [2][TB] K^T (16-bit) -- unused for fp32 (K read transposed)
+  char* sV;     // [2][TB] V rows
+  float* sZK;   // [2][2 * kTile]
 
-  const Geo g = a.geo;
+  Geo g;
+  QCtx c;
+  int w, lane, hl, l32, iw0, nkt, N, kv_lim;
+  float cst_lo, cst_hi, sc2, tau, lse2, Dl;
+  bool need_dz;
+  const T* Kb;
+  const T* Ktb;
+  const T* Vb;
+  int64_t sk, sv, Np;
+  DLoader<T> ldK, ldKt, ldV;
+  frag qf[NSD], df[NSD];
+  f32x16 dq[2];
+  float acc_lo, acc_hi;
+  float* dz_row;
+
+  __device__ __forceinline__ void issue(int t, int buf) {
+    const int j0 = t * kTile;
+    ldK.load(sK + buf * TB, Kb + (int64_t)j0 * sk, N - j0, lane);
+    if constexpr (kHalf) ldKt.load(sKt + buf * TB, Ktb + j0, 64, lane);
+    ldV.load(sV + buf * TB, Vb + (int64_t)j0 * sv, N - j0, lane);
+    if (c.has_zk && w < 2) {
+      const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
+      dword_direct((char*)(sZK + buf * 2 * kTile + w * kTile), p, p != nullptr, lane);
+    }
+  }
+
+  template <int SEG>
+  __device__ __forceinline__ void tile(int t, int buf) {
+    const int j0 = t * kTile;
+    if (iw0 >= N || (g.causal && j0 > iw0 + 31)) return;
+    const int kind = SEG == KIND_BAND ? tile_kind_q(g, j0, iw0) : SEG;
+    const bool needmask = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0);
+    const char* tK = sK + buf * TB;
+    const char* tKt = kHalf ? sKt + buf * TB : tK;
+    const char* tV = sV + buf * TB;
+    const float* zk = sZK + buf * 2 * kTile;
+    const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
+    const float off = cst * sc2 - lse2;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x16 s;
+      if (SEG == KIND_BAND && kind == KIND_BAND)
+        s = qside_scores<T>(g, c, tK, zk, qf, KIND_BAND, j0, st, needmask);
+      else
+        s = qside_scores<T>(g, c, tK, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
+                            needmask);
+      f32x16 dp = M::mma(dfrag<T>(tV, 32 * st + c.sig, E * hl), df[0], zero16());
+#pragma unroll
+      for (int ks = 1; ks < NSD; ++ks)
+        dp = M::mma(dfrag<T>(tV, 32 * st + c.sig, KS * ks + E * hl), df[ks], dp);
+
+      float ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2_fast(fmaf(s[e], sc2, off));
+        ds[e] = p * (dp[e] - Dl);
+      }
+      if (need_dz) {
+        if (SEG != KIND_BAND || kind != KIND_BAND) {
+          float tsum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) tsum += ds[e];
+          if (kind == KIND_LO) acc_lo += tsum; else acc_hi += tsum;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = j0 + 32 * st + kappa<T>(hl, e);
+            const int o = j - c.iq;
+            if (o <= g.lo) {
+              acc_lo += ds[e];
+            } else if (o >= g.hi) {
+              acc_hi += ds[e];
+            } else if (c.iq < N && j < N && !(g.causal && j > c.iq)) {
+              dz_row[o - g.lo - c.wsq] = tau * ds[e];
+            }
+          }
+        }
+      }
+      frag sf[KPS];
+#pragma unroll
+      for (int kk = 0; kk < KPS; ++kk) sf[kk] = M::pack(&ds[kk * E]);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < KPS; ++kk) {
+          const int col = KS * (KPS * st + kk) + E * hl;
+          frag kf;
+          if constexpr (kHalf) {
+            kf = dfrag<T>(tKt, 32 * dt + l32, col);
+          } else {
+            kf = dfrag_t32(tK, 32 * dt + l32, col);
+          }
+          dq[dt] = M::mma(kf, sf[kk], dq[dt]);
+        }
+    }
+  }
+
+  template <int SEG>
+  __device__ __forceinline__ void segment(int tb, int te) {
+    for (int t = tb; t < te; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < nkt) issue(t + 1, buf ^ 1);
+      tile<SEG>(t, buf);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
+  using M = MT<T>;
+  using B = BwdQ<T>;
+  constexpr int TB = DTile<T>::BYTES;
+  __shared__ __align__(16) char sK[2 * TB];
+  __shared__ __align__(16) char sKt[B::kHalf ? 2 * TB : 16];
+  __shared__ __align__(16) char sV[2 * TB];
+  __shared__ __align__(16) float sZK[2 * 2 * kTile];
+
+  B q;
+  q.sK = sK;
+  q.sKt = sKt;
+  q.sV = sV;
+  q.sZK = sZK;
+  q.g = a.geo;
+  const Geo& g = q.g;
   const int N = g.N;
+  q.N = N;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  q.w = w;
+  q.lane = lane;
+  q.hl = hl;
+  q.l32 = l32;
   const int total = a.B * a.H * a.nblk;
   const int lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / a.nblk;
@@ -68,20 +173,29 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(AttnArgs a) {
   if (g.causal) qb = a.nblk - 1 - qb;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
+  q.iw0 = iw0;
 
   int kv_end = N;
   if (a.flags & F_KEYPAD) kv_end = imax(0, imin(N, a.key_len[bb]));
   int kv_blk = kv_end;
   if (g.causal) kv_blk = imin(kv_blk, i0 + kBlockRows);
   const int nkt = kv_blk > 0 ? (kv_blk + kTile - 1) / kTile : 0;
-  const int kv_lim = imin(N, nkt * kTile);  // keys written by the band stores
+  q.nkt = nkt;
+  q.kv_lim = imin(N, nkt * kTile);  // keys written by the band stores
 
-  const T* Qp = (const T*)a.q + bb * a.sq.b + hh * a.sq.h;
-  const T* Kp = (const T*)a.k + bb * a.sk.b + hh * a.sk.h;
-  const T* Vp = (const T*)a.v + bb * a.sv.b + hh * a.sv.h;
-  const T* dOp = (const T*)a.dO + bb * a.sdo.b + hh * a.sdo.h;
+  q.Kb = (const T*)a.k + bb * a.sk.b + hh * a.sk.h;
+  q.Vb = (const T*)a.v + bb * a.sv.b + hh * a.sv.h;
+  q.sk = a.sk.n;
+  q.sv = a.sv.n;
+  q.Np = a.Np;
+  q.ldK.init(a.sk.n, w, lane);
+  q.ldV.init(a.sv.n, w, lane);
+  if constexpr (B::kHalf) {
+    q.Ktb = (const T*)a.kt + (int64_t)bh * kHeadDim * a.Np;
+    q.ldKt.init(a.Np, w, lane);
+  }
 
-  QCtx c;
+  QCtx& c = q.c;
   c.iq = iq;
   c.hl = hl;
   c.sig = sigma<T>(l32);
@@ -93,130 +207,38 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(AttnArgs a) {
   c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + iq) * g.W : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.W : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
-  const bool need_dz = a.flags & F_ZQ_NEEDED;
-  float cst_lo, cst_hi;
-  qside_consts(g, c, qb, cst_lo, cst_hi);
+  q.need_dz = a.flags & F_ZQ_NEEDED;
+  qside_consts(g, c, qb, q.cst_lo, q.cst_hi);
+  q.sc2 = a.scale2;
+  q.tau = a.tau;
 
-  frag qf[NSD], df[NSD];
-  float lse2 = INFINITY, Dl = 0.f;
   {
-    const T* qrow = Qp + (int64_t)iq * a.sq.n;
-    const T* drow = dOp + (int64_t)iq * a.sdo.n;
+    const T* qrow = (const T*)a.q + bb * a.sq.b + hh * a.sq.h + (int64_t)iq * a.sq.n;
+    const T* drow = (const T*)a.dO + bb * a.sdo.b + hh * a.sdo.h + (int64_t)iq * a.sdo.n;
 #pragma unroll
-    for (int ks = 0; ks < NSD; ++ks) {
-      qf[ks] = iq < N ? frag_g<T>(qrow, KS * ks + E * hl) : M::zero();
-      df[ks] = iq < N ? frag_g<T>(drow, KS * ks + E * hl) : M::zero();
+    for (int ks = 0; ks < B::NSD; ++ks) {
+      q.qf[ks] = iq < N ? frag_g<T>(qrow, B::KS * ks + B::E * hl) : M::zero();
+      q.df[ks] = iq < N ? frag_g<T>(drow, B::KS * ks + B::E * hl) : M::zero();
     }
-    if (iq < N) {
-      const float L = a.lse[(int64_t)bh * N + iq];
-      lse2 = L == -INFINITY ? INFINITY : L * kLog2e;  // a dead row gives P = 0
-      Dl = a.D[(int64_t)bh * N + iq];
-    }
+    // padded row terms: +inf / 0 beyond N and for rows with every key masked
+    q.lse2 = a.L2[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
+    q.Dl = a.D[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
   }
-  float* dz_row = need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.W : nullptr;
+  q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.W : nullptr;
+  q.dq[0] = zero16();
+  q.dq[1] = zero16();
+  q.acc_lo = 0.f;
+  q.acc_hi = 0.f;
 
-  Chunk rk[C::NCH], rv[C::NCH];
-  float rz0 = 0.f, rz1 = 0.f;
-  auto gload = [&](int t) {
-    const int j0 = t * kTile;
-    tile_load<T, C::kHalf>(rk, Kp, a.sk.n, j0, N, tid);
-    tile_load<T, false>(rv, Vp, a.sv.n, j0, N, tid);
-    if (c.has_zk && tid < kTile) kside_sat(g, c.zkb, j0 + tid, rz0, rz1);
-  };
-  auto sstore = [&](int buf) {
-    tile_store_rm<T, C::kHalf>(sK[buf], rk, tid);
-    if constexpr (C::kHalf) tile_store_tr<T>(sKt[buf], rk, tid);
-    tile_store_rm<T, false>(sV[buf], rv, tid);
-    if (c.has_zk && tid < kTile) {
-      sZK[buf][tid] = rz0;
-      sZK[buf][kTile + tid] = rz1;
-    }
-  };
+  const int t1 = imin(nkt, imax(0, floor_div_q(g.lo + i0 - (kTile - 1), kTile) + 1));
+  const int t2 = imin(nkt, imax(t1, ceil_div_q(g.hi + i0 + kBlockRows - 1, kTile)));
 
-  f32x16 dq[2];
-  dq[0] = zero16();
-  dq[1] = zero16();
-  float acc_lo = 0.f, acc_hi = 0.f;
-  const float sc2 = a.scale2;
-
-  if (nkt > 0) {
-    gload(0);
-    sstore(0);
-  }
+  if (nkt > 0) q.issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nkt) gload(t + 1);
-    const int j0 = t * kTile;
-    const bool active = iw0 < N && !(g.causal && j0 > iw0 + 31);
-    if (active) {
-      const int kind = tile_kind_q(g, j0, iw0);
-      const bool needmask = (j0 + kTile > kv_end) || (g.causal && j0 + kTile - 1 > iw0);
-      f32x16 s[2];
-      qside_scores<T>(s, g, c, sK[buf], sZK[buf], qf, kind, j0, needmask);
-      const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
-      const float off = cst * sc2 - lse2;
-
-      f32x16 dp[2];
-      dp[0] = zero16();
-      dp[1] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < NSD; ++ks)
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-          dp[st] = M::mma(frag_rm<T>(sV[buf], 32 * st + c.sig, KS * ks + E * hl), df[ks], dp[st]);
-
-      float ds[2][16];
-      float tsum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2_fast(fmaf(s[st][e], sc2, off));
-          ds[st][e] = p * (dp[st][e] - Dl);
-          tsum += ds[st][e];
-        }
-
-      if (need_dz) {
-        if (kind == KIND_LO) {
-          acc_lo += tsum;
-        } else if (kind == KIND_HI) {
-          acc_hi += tsum;
-        } else {
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int j = j0 + 32 * st + kappa<T>(hl, e);
-              const int o = j - iq;
-              if (o <= g.lo) {
-                acc_lo += ds[st][e];
-              } else if (o >= g.hi) {
-                acc_hi += ds[st][e];
-              } else if (iq < N && j < N && !(g.causal && j > iq)) {
-                dz_row[o - g.lo - c.wsq] = a.tau * ds[st][e];
-              }
-            }
-        }
-      }
-
-      frag sf[NSK];
-#pragma unroll
-      for (int ks = 0; ks < NSK; ++ks) {
-        const int st = (ks * KS) / 32, e0 = ((ks * KS) % 32) / KS * E;
-        sf[ks] = M::pack(&ds[st][e0]);
-      }
-      const T* kt = C::kHalf ? sKt[C::kHalf ? buf : 0] : sK[buf];
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < NSK; ++ks)
-          dq[dt] = M::mma(frag_t<T>(kt, 32 * dt + l32, KS * ks + E * hl), sf[ks], dq[dt]);
-    }
-    if (t + 1 < nkt) sstore(buf ^ 1);
-    __syncthreads();
-  }
+  q.template segment<KIND_LO>(0, t1);
+  q.template segment<KIND_BAND>(t1, t2);
+  q.template segment<KIND_HI>(t2, nkt);
 
   if (iq < N) {
     // dQ = tau * dS K  (plus dZ^Q aQ added by the contraction when aQ is present)
@@ -227,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(AttnArgs a) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int d = 32 * dt + 8 * e4 + 4 * hl;
-          store4<float>(prow + d, a.tau * dq[dt][4 * e4], a.tau * dq[dt][4 * e4 + 1],
-                        a.tau * dq[dt][4 * e4 + 2], a.tau * dq[dt][4 * e4 + 3]);
+          store4<float>(prow + d, a.tau * q.dq[dt][4 * e4], a.tau * q.dq[dt][4 * e4 + 1],
+                        a.tau * q.dq[dt][4 * e4 + 2], a.tau * q.dq[dt][4 * e4 + 3]);
         }
     } else {
       T* orow = (T*)a.dq + bb * a.sdq.b + hh * a.sdq.h + (int64_t)iq * a.sdq.n;
@@ -237,15 +259,16 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(AttnArgs a) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int d = 32 * dt + 8 * e4 + 4 * hl;
-          store4<T>(orow + d, a.tau * dq[dt][4 * e4], a.tau * dq[dt][4 * e4 + 1],
-                    a.tau * dq[dt][4 * e4 + 2], a.tau * dq[dt][4 * e4 + 3]);
+          store4<T>(orow + d, a.tau * q.dq[dt][4 * e4], a.tau * q.dq[dt][4 * e4 + 1],
+                    a.tau * q.dq[dt][4 * e4 + 2], a.tau * q.dq[dt][4 * e4 + 3]);
         }
     }
   }
 
-  if (need_dz) {
-    acc_lo += __shfl_xor(acc_lo, 32);
-    acc_hi += __shfl_xor(acc_hi, 32);
+  if (q.need_dz) {
+    float acc_lo = q.acc_lo + __shfl_xor(q.acc_lo, 32);
+    float acc_hi = q.acc_hi + __shfl_xor(q.acc_hi, 32);
+    float* dz_row = q.dz_row;
     if (iq < N) {
       int cb, ce;
       cols_q(g, qb, cb, ce);
@@ -265,17 +288,9 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(AttnArgs a) {
       const int shift = iq + g.lo + ws;  // key of column col is col + shift
       const int a_end = imin(ie, -shift);
       for (int col = ib + hl; col < a_end; col += 2) dz_row[col] = 0.f;
-      for (int col = imax(ib, kv_lim - shift) + hl; col < ie; col += 2) dz_row[col] = 0.f;
+      for (int col = imax(ib, q.kv_lim - shift) + hl; col < ie; col += 2) dz_row[col] = 0.f;
     }
   }
-}
-
-template <typename T>
-static hipError_t launch_pre_t(const PreArgs& p, hipStream_t st) {
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
-  const int pre_blocks = (int)((rows + kThreads / 8 - 1) / (kThreads / 8));
-  hipLaunchKernelGGL(pre_kernel<T>, dim3(pre_blocks), dim3(kThreads), 0, st, p);
-  return hipGetLastError();
 }
 
 template <typename T>
@@ -283,14 +298,6 @@ static hipError_t launch_bwd_q_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
   hipLaunchKernelGGL(bwd_q_kernel<T>, dim3(total), dim3(kThreads), 0, st, a);
   return hipGetLastError();
-}
-
-hipError_t launch_pre(int dtype, const PreArgs& p, hipStream_t st) {
-  switch (dtype) {
-    case 0: return launch_pre_t<float>(p, st);
-    case 1: return launch_pre_t<_Float16>(p, st);
-    default: return launch_pre_t<__bf16>(p, st);
-  }
 }
 
 hipError_t launch_bwd_q(int dtype, const AttnArgs& a, hipStream_t st) {

@@ -139,4 +139,8 @@ __device__ inline int xcd_remap(int bid, int total) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate for "vmcnt(0)" with the other counters left alone
+// (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 }  // namespace relpos

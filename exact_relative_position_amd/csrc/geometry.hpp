@@ -120,7 +120,13 @@ struct AttnArgs {
   void* o_out;     // forward output pointer
   float* lse;      // [B*H][N]
   const void* dO;
-  const float* D;  // [B*H][N]
+  const float* L2; // [B*H][Np] padded log2-domain LSE (backward)
+  const float* D;  // [B*H][Np] padded row terms (backward)
+  const void* vt;  // [B*H][64][Np] token-contiguous copies (16-bit types)
+  const void* kt;
+  const void* qt;
+  const void* dot;
+  int Np;          // N rounded up to 64
   const float* zq; // [B*H][N][W] or null
   const float* zk;
   const float* bunf;  // [Hb][R] fp32 unfolded scalar bias, or null
@@ -140,12 +146,21 @@ struct AttnArgs {
   int nblk;        // blocks per (b, h) along the parallel dimension
 };
 
-struct PreArgs {
+struct TransposeArgs {   // X [B, H, N, 64] -> Xt [B*H][64][Np], zero beyond N
+  const void* x;
+  Str sx;
+  void* xt;
+  int B, H, N, Np;
+};
+
+struct RowTermArgs {     // padded backward row terms
   const void* o;
   const void* dO;
   Str so, sdo;
-  float* D;
-  int B, H, N;
+  const float* lse;      // [B*H][N]
+  float* L2;             // [B*H][Np]  LSE * log2(e), +inf for dead and padded rows
+  float* D;              // [B*H][Np]  sum_d dO O, 0 for padded rows
+  int B, H, N, Np;
 };
 
 struct RowsArgs {       // dX = part + dZ . table   (per row)

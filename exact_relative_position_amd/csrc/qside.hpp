@@ -54,61 +54,50 @@ __device__ inline float band_rel(const Geo& g, const QCtx& c, int j, int i) {
   return v;
 }
 
-// Raw scores of keys [j0, j0 + 64) for this lane's query, masked entries = -inf.
-// s[st][e] <-> key j0 + 32*st + kappa(hl, e).  The per-query constant of a
-// saturated tile (Z^Q of the saturated row plus b) is NOT included.
+// Raw scores of the 32 keys [j0 + 32 st, j0 + 32 st + 32) for this lane's
+// query, masked entries = -inf; element e <-> key j0 + 32 st + kappa(hl, e).
+// The per-query constant of a saturated tile (Z^Q of the saturated row plus
+// b) is NOT included.
 template <typename T>
-__device__ inline void qside_scores(f32x16 (&s)[2], const Geo& g, const QCtx& c, const T* sK,
-                                    const float* sZK, const typename MT<T>::frag* qf, int kind,
-                                    int j0, bool needmask) {
+__device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c, const char* sK,
+                                               const float* sZK,
+                                               const typename MT<T>::frag* qf, int kind,
+                                               int j0, int st, bool needmask) {
   using M = MT<T>;
   constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
+  f32x16 s;
   int ks0 = 0;
   if (kind != KIND_BAND && !c.has_zk) {
     // constant tile without a key term: the accumulator starts at literal zero
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-      s[st] = M::mma(frag_rm<T>(sK, 32 * st + c.sig, E * c.hl), qf[0], zero16());
+    s = M::mma(dfrag<T>(sK, 32 * st + c.sig, E * c.hl), qf[0], zero16());
     ks0 = 1;
   } else if (kind != KIND_BAND) {
     // constant tile: one Z^K scalar per key seeds the accumulator
-    const float* z = sZK + (kind == KIND_LO ? 0 : kTile);
+    float v[16];
+    lds_rows16<T>(sZK + (kind == KIND_LO ? 0 : kTile) + 32 * st, c.hl, v);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      float v[16];
-      lds_rows16<T>(z + 32 * st, c.hl, v);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[st][e] = v[e];
-    }
+    for (int e = 0; e < 16; ++e) s[e] = v[e];
   } else {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int j = j0 + 32 * st + kappa<T>(c.hl, e);
-        bool live = c.iq < g.N && j < c.kv_end && !(g.causal && j > c.iq);
-        s[st][e] = live ? band_rel(g, c, j, c.iq) : 0.f;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + 32 * st + kappa<T>(c.hl, e);
+      const bool live = c.iq < g.N && j < c.kv_end && !(g.causal && j > c.iq);
+      s[e] = live ? band_rel(g, c, j, c.iq) : 0.f;
     }
   }
 #pragma unroll
   for (int ks = 0; ks < NSD; ++ks) {
     if (ks < ks0) continue;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = M::mma(frag_rm<T>(sK, 32 * st + c.sig, KS * ks + E * c.hl), qf[ks], s[st]);
-    }
+    s = M::mma(dfrag<T>(sK, 32 * st + c.sig, KS * ks + E * c.hl), qf[ks], s);
   }
   if (needmask) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int j = j0 + 32 * st + kappa<T>(c.hl, e);
-        if (j >= c.kv_end || (g.causal && j > c.iq)) s[st][e] = -INFINITY;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int j = j0 + 32 * st + kappa<T>(c.hl, e);
+      if (j >= c.kv_end || (g.causal && j > c.iq)) s[e] = -INFINITY;
     }
   }
+  return s;
 }
 
 // Saturated-row constants of this lane's query: Z^Q[i, first/last row] + b.
@@ -131,21 +120,31 @@ __device__ inline void qside_consts(const Geo& g, const QCtx& c, int grp, float&
   }
 }
 
-// Key-side saturated scalars of key j (Z^K[j, first/last row]); 0 outside the
-// key group's live window or beyond N.
-__device__ inline void kside_sat(const Geo& g, const float* zkb, int j, float& z0, float& z1) {
-  z0 = 0.f;
-  z1 = 0.f;
-  if (j < g.N) {
-    int grp = j / kGroup;
-    int wk = win_k(g, grp);
-    int cb, ce;
-    cols_k(g, grp, cb, ce);
-    const float* zr = zkb + (int64_t)j * g.W;
-    int c0 = 0 - wk, c1 = g.R - 1 - wk;
-    if (c0 >= cb && c0 < ce) z0 = zr[c0];
-    if (c1 >= cb && c1 < ce) z1 = zr[c1];
-  }
+// Address of the key-side saturated scalar Z^K[j, first (side 0) / last row]
+// of key j, or null when j >= N or the column is outside the key group's
+// live window (then no live entry uses it).
+__device__ __forceinline__ const float* kside_sat_ptr(const Geo& g, const float* zkb, int j,
+                                                      int side) {
+  if (j >= g.N) return nullptr;
+  const int grp = j / kGroup;
+  const int wk = win_k(g, grp);
+  int cb, ce;
+  cols_k(g, grp, cb, ce);
+  const int col = (side == 0 ? 0 : g.R - 1) - wk;
+  if (col < cb || col >= ce) return nullptr;
+  return zkb + (int64_t)j * g.W + col;
+}
+// Same for the query side: Z^Q[i, first / last row] of query i.
+__device__ __forceinline__ const float* qside_sat_ptr(const Geo& g, const float* zqb, int i,
+                                                      int side) {
+  if (i >= g.N) return nullptr;
+  const int grp = i / kGroup;
+  const int wq = win_q(g, grp);
+  int cb, ce;
+  cols_q(g, grp, cb, ce);
+  const int col = (side == 0 ? 0 : g.R - 1) - wq;
+  if (col < cb || col >= ce) return nullptr;
+  return zqb + (int64_t)i * g.W + col;
 }
 
 }  // namespace relpos

@@ -62,6 +62,40 @@ __device__ inline void tile_load(Chunk (&r)[TileCfg<T>::NCH], const T* base, int
   }
 }
 
+// Per-thread view of the 64-row tiles of one [N, 64] matrix: the chunk
+// offsets inside a tile are computed once; a tile load is one scalar row
+// offset plus NCH vector loads (bounds checks only on a partial last tile).
+template <typename T, bool COLMAP>
+struct TileReader {
+  const T* base;
+  int64_t sn;
+  int off[TileCfg<T>::NCH];
+  int row[TileCfg<T>::NCH];
+  __device__ inline void init(const T* b, int64_t sn_, int tid) {
+    base = b;
+    sn = sn_;
+#pragma unroll
+    for (int u = 0; u < TileCfg<T>::NCH; ++u) {
+      int r, c;
+      chunk_pos<T, COLMAP>(tid + kThreads * u, r, c);
+      row[u] = r;
+      off[u] = r * (int)sn_ + c;
+    }
+  }
+  __device__ inline void load(Chunk (&r)[TileCfg<T>::NCH], int row0, int nrows) const {
+    const T* p = base + (int64_t)row0 * sn;
+    if (row0 + 64 <= nrows) {
+#pragma unroll
+      for (int u = 0; u < TileCfg<T>::NCH; ++u) r[u] = *reinterpret_cast<const Chunk*>(p + off[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < TileCfg<T>::NCH; ++u)
+        r[u] = (row0 + row[u] < nrows) ? *reinterpret_cast<const Chunk*>(p + off[u])
+                                       : Chunk{{0u, 0u, 0u, 0u}};
+    }
+  }
+};
+
 template <typename T, bool COLMAP>
 __device__ inline void tile_store_rm(T* lds, const Chunk (&r)[TileCfg<T>::NCH], int tid) {
   constexpr int P = TileCfg<T>::PITCH;
@@ -91,6 +125,90 @@ __device__ inline void tile_store_tr(T* lds, const Chunk (&r)[TileCfg<T>::NCH], 
     const T* e = reinterpret_cast<const T*>(&r[u]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) lds[(col + t) * P + row] = e[t];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS tiles.  A tile of 64 rows x 64 elements is written into LDS by
+// global_load_lds_dwordx4: each lane's 16 bytes land at lds_base + 16 * lane,
+// so the LDS position is set by which lane loads which chunk.  Rows are
+// stored unpadded (ROWB bytes); inside a row the 16-byte chunks are permuted
+// by an XOR with swz(row) so that the 8 rows read together by the
+// sigma-permuted MFMA operand loads fall on 8 different bank groups.
+// Rows beyond the valid count are zero-filled with ordinary LDS stores.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <typename T>
+struct DTile {
+  static constexpr int ROWB = 64 * (int)sizeof(T);  // bytes per row
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
+  static constexpr int BYTES = 64 * ROWB;
+  static constexpr int PER_WAVE = 64 * CPR / 64 / 4;  // 64-lane loads per wave per tile
+};
+
+template <typename T>
+__device__ __forceinline__ int swz(int r) {
+  return (r + ((r >> 3) << 2)) & (DTile<T>::CPR - 1);
+}
+
+// Byte offset of element (r, c) inside a direct tile.
+template <typename T>
+__device__ __forceinline__ int dt_off(int r, int c) {
+  constexpr int EPC = DTile<T>::EPC;
+  return r * DTile<T>::ROWB + (((c / EPC) ^ swz<T>(r)) << 4) + (c % EPC) * (int)sizeof(T);
+}
+
+// Per-lane plan of the direct loads of one 64 x 64 tile.
+template <typename T>
+struct DLoader {
+  static constexpr int PW = DTile<T>::PER_WAVE;
+  int off[PW];   // element offset of the lane's chunk, relative to the tile's first row
+  int row[PW];
+  int blk0;      // first 64-slot block of this wave
+  __device__ __forceinline__ void init(int64_t sn, int w, int lane) {
+    blk0 = w * PW;
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int p = (blk0 + u) * 64 + lane;
+      const int r = p / DTile<T>::CPR, cs = p % DTile<T>::CPR;
+      const int cg = cs ^ swz<T>(r);
+      row[u] = r;
+      off[u] = r * (int)sn + cg * DTile<T>::EPC;
+    }
+  }
+  // Load rows [0, nvalid) of the tile starting at src; zero the others.
+  __device__ __forceinline__ void load(char* lds, const T* src, int nvalid, int lane) const {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      char* dst = lds + (blk0 + u) * 1024;
+      if (nvalid >= 64 || row[u] < nvalid) {
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off[u]), (lds_void_t*)dst, 16, 0, 0);
+      } else {
+        *reinterpret_cast<Chunk*>(dst + lane * 16) = Chunk{{0u, 0u, 0u, 0u}};
+      }
+    }
+  }
+};
+
+// Fragment (row, columns [col, col + E)) of a direct tile.
+template <typename T>
+__device__ __forceinline__ typename MT<T>::frag dfrag(const char* lds, int row, int col) {
+  return *reinterpret_cast<const typename MT<T>::frag*>(lds + dt_off<T>(row, col));
+}
+// Fragment of the transposed view of a direct tile (fp32 only: one element).
+__device__ __forceinline__ float dfrag_t32(const char* lds, int row, int col) {
+  return *reinterpret_cast<const float*>(lds + dt_off<float>(col, row));
+}
+
+// One 4-byte value per lane, written to lds + 4 * lane (when valid, else 0).
+__device__ __forceinline__ void dword_direct(char* lds, const float* src, bool valid, int lane) {
+  if (valid) {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds, 4, 0, 0);
+  } else {
+    reinterpret_cast<float*>(lds)[lane] = 0.f;
   }
 }
 
