@@ -16,7 +16,8 @@ live; the dominant attention kernel gives the roofline figure.
 FLOP convention (FlashAttention): forward 4 d per live (query, key) pair,
 backward 10 d; each backward kernel's own count is its GEMM work (query pass
 6 d, key pass 8 d per pair).  The CPU baseline is the fp64 oracle on a
-bounded sample (one head of the same workload), timed on the host cores.
+bounded sample (whole (batch, head) slices of the same workload, about ten
+seconds of work), timed on the host cores.
 
 Prints one JSON line.
 """
@@ -67,8 +68,9 @@ def describe(w):
             "terms": terms or "none", "mask": mask or "none", "tau": round(w.tau, 6)}
 
 
-def cpu_baseline(w, x, pairs_per_head):
-    """fp64 oracle, forward + backward of (batch 0, head 0) at the full length."""
+def cpu_baseline(w, x, min_seconds=10.0):
+    """fp64 oracle, forward + backward of whole (batch, head) slices at the full
+    length, taken in order until about `min_seconds` of CPU work is done."""
     import numpy as np  # noqa: F401
 
     import oracle
@@ -80,18 +82,36 @@ def cpu_baseline(w, x, pairs_per_head):
         threads = 1
     f = {k: as_f64(v) for k, v in x.items() if k != "key_len"}
     kl = None if x["key_len"] is None else x["key_len"].numpy()
+    slices = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = []
+    flops = 0.0
     t0 = time.perf_counter()
-    oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi, tau=w.tau,
-                   causal=w.causal, key_len=kl, bh=[(0, 0)])
-    oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"], phi=w.phi,
-                    tau=w.tau, causal=w.causal, key_len=kl, bh=[(0, 0)])
+    for bh in slices:
+        oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi, tau=w.tau,
+                       causal=w.causal, key_len=kl, bh=[bh])
+        oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"],
+                        phi=w.phi, tau=w.tau, causal=w.causal, key_len=kl, bh=[bh])
+        done.append(bh)
+        flops += 14.0 * w.d * live_pairs(w.with_(B=1), None if kl is None else kl[bh[0]:bh[0] + 1])
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
-    pairs0 = live_pairs(w.with_(B=1), None if kl is None else kl[:1])
-    flops = 14.0 * w.d * pairs0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"forward+backward of 1 of {w.B * w.H} (batch, head) slices "
-                      f"(b=0, h=0) at full N={w.N}, fp64 NumPy"}
+            "sample": f"forward+backward of {len(done)} of {len(slices)} (batch, head) slices "
+                      f"at full N={w.N}, fp64 NumPy"}
+
+
+def copy_probe(torch, dev, mib):
+    """One plain device-to-device copy of `mib` MiB, outside the timed region:
+    its HBM counter readings calibrate the counters of the other kernels."""
+    n = mib * (1 << 20) // 2
+    a = torch.empty(n, dtype=torch.float16, device=dev).fill_(1.0)
+    c = torch.empty_like(a)
+    torch.cuda.synchronize(dev)
+    c.copy_(a)
+    torch.cuda.synchronize(dev)
+    del a, c
 
 
 def main():
@@ -101,6 +121,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="shaw_n8192_f16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain copy of this many MiB before the warmup "
+                         "(calibration of HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is a "
@@ -115,6 +138,8 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     x = make_inputs(w)
+    if args.copy_probe_mib > 0:
+        copy_probe(torch, dev, args.copy_probe_mib)
     t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
     torch.cuda.synchronize(dev)
     mem_inputs = torch.cuda.memory_allocated(dev)
@@ -205,7 +230,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x, pairs / w.H / w.B)
+        out["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(out), flush=True)
 
 

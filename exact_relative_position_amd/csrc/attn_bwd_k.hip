@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   const Geo& g = k.g;
   const int N = g.N;
   k.N = N;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   k.w = w;
   k.lane = lane;
   k.hl = hl;

@@ -28,14 +28,16 @@ struct BwdQ {
   static constexpr int KPS = 32 / KS;  // MFMA k-steps per 32-key half
   static constexpr int TB = DTile<T>::BYTES;
 
-  char* sK;     // [2][TB] K rows
-  char* sKt;    // [2][TB] K^T (16-bit) -- unused for fp32 (K read transposed)
-  char* sV;     // [2][TB] V rows
-  float* sZK;   // [2][2 * kTile]
+  // LDS buffers, two of each (separate arrays, so that the compiler can tell
+  // the asynchronous loads into one buffer from the reads of the other)
+  char* sK[2];     // K rows
+  char* sKt[2];    // K^T (16-bit) -- unused for fp32 (K read transposed)
+  char* sV[2];     // V rows
+  float* sZK[2];   // saturated Z^K scalars [2][kTile]
 
   Geo g;
   QCtx c;
-  int w, lane, hl, l32, iw0, nkt, N, kv_lim;
+  int w, lane, hl, l32, i0, iw0, nkt, N, kv_lim;
   float cst_lo, cst_hi, sc2, tau, lse2, Dl;
   bool need_dz;
   const T* Kb;
@@ -43,46 +45,57 @@ struct BwdQ {
   const T* Vb;
   int64_t sk, sv, Np;
   DLoader<T> ldK, ldKt, ldV;
+  // per-lane LDS byte offsets of the 16-bit operand fragments (buffer 0):
+  // K / V row sigma(l32) at k-step ks; K^T row l32 at key chunk column c4
+  int kofs[kHalf ? NSD : 1];
+  int tofs[kHalf ? 2 * KPS : 1];
   frag qf[NSD], df[NSD];
   f32x16 dq[2];
   float acc_lo, acc_hi;
   float* dz_row;
 
-  __device__ __forceinline__ void issue(int t, int buf) {
+  template <int BUF>
+  __device__ __forceinline__ void issue(int t) {
     const int j0 = t * kTile;
-    ldK.load(sK + buf * TB, Kb + (int64_t)j0 * sk, N - j0, lane);
-    if constexpr (kHalf) ldKt.load(sKt + buf * TB, Ktb + j0, 64, lane);
-    ldV.load(sV + buf * TB, Vb + (int64_t)j0 * sv, N - j0, lane);
+    ldK.load(sK[BUF], Kb + (int64_t)j0 * sk, N - j0, lane);
+    if constexpr (kHalf) ldKt.load(sKt[BUF], Ktb + j0, 64, lane);
+    ldV.load(sV[BUF], Vb + (int64_t)j0 * sv, N - j0, lane);
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
-      dword_direct((char*)(sZK + buf * 2 * kTile + w * kTile), p, p != nullptr, lane);
+      dword_direct((char*)(sZK[BUF] + w * kTile), p, p != nullptr, lane);
     }
   }
 
-  template <int SEG>
-  __device__ __forceinline__ void tile(int t, int buf) {
+  // One 64-key tile from LDS buffer BUF; BAND: the block's tile crosses the
+  // band, otherwise it is saturated on side `sat`.
+  template <bool BAND, int BUF>
+  __device__ __forceinline__ void tile(int t, int sat) {
     const int j0 = t * kTile;
     if (iw0 >= N || (g.causal && j0 > iw0 + 31)) return;
-    const int kind = SEG == KIND_BAND ? tile_kind_q(g, j0, iw0) : SEG;
-    const bool needmask = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0);
-    const char* tK = sK + buf * TB;
-    const char* tKt = kHalf ? sKt + buf * TB : tK;
-    const char* tV = sV + buf * TB;
-    const float* zk = sZK + buf * 2 * kTile;
+    const int kind = BAND ? tile_kind_q(g, j0, iw0) : sat;
+    // masks are only applied in the band body (a saturated body is only
+    // used for tiles that need no mask anywhere in the block)
+    const bool needmask = BAND && ((j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0));
+    const char* tK = sK[BUF];
+    const char* tKt = kHalf ? sKt[BUF] : tK;
+    const char* tV = sV[BUF];
+    const float* zk = sZK[BUF];
     const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
     const float off = cst * sc2 - lse2;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      f32x16 s;
-      if (SEG == KIND_BAND && kind == KIND_BAND)
-        s = qside_scores<T>(g, c, tK, zk, qf, KIND_BAND, j0, st, needmask);
-      else
-        s = qside_scores<T>(g, c, tK, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
-                            needmask);
-      f32x16 dp = M::mma(dfrag<T>(tV, 32 * st + c.sig, E * hl), df[0], zero16());
+      frag kf[NSD];
 #pragma unroll
-      for (int ks = 1; ks < NSD; ++ks)
-        dp = M::mma(dfrag<T>(tV, 32 * st + c.sig, KS * ks + E * hl), df[ks], dp);
+      for (int ks = 0; ks < NSD; ++ks) kf[ks] = kfrag<T>(tK, kofs, c, st, ks);
+      f32x16 s;
+      if (BAND && kind == KIND_BAND)
+        s = qside_scores<T>(g, c, kf, zk, qf, KIND_BAND, j0, st, needmask);
+      else
+        s = qside_scores<T>(g, c, kf, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
+                            needmask);
+      f32x16 dp = M::mma(kfrag<T>(tV, kofs, c, st, 0), df[0], zero16());
+#pragma unroll
+      for (int ks = 1; ks < NSD; ++ks) dp = M::mma(kfrag<T>(tV, kofs, c, st, ks), df[ks], dp);
 
       float ds[16];
 #pragma unroll
@@ -91,7 +104,7 @@ struct BwdQ {
         ds[e] = p * (dp[e] - Dl);
       }
       if (need_dz) {
-        if (SEG != KIND_BAND || kind != KIND_BAND) {
+        if (!BAND || kind != KIND_BAND) {
           float tsum = 0.f;
 #pragma unroll
           for (int e = 0; e < 16; ++e) tsum += ds[e];
@@ -118,50 +131,69 @@ struct BwdQ {
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int kk = 0; kk < KPS; ++kk) {
-          const int col = KS * (KPS * st + kk) + E * hl;
           frag kf;
           if constexpr (kHalf) {
-            kf = dfrag<T>(tKt, 32 * dt + l32, col);
+            kf = *reinterpret_cast<const frag*>(tKt + tofs[KPS * st + kk] +
+                                                dt * 32 * DTile<T>::ROWB);
           } else {
-            kf = dfrag_t32(tK, 32 * dt + l32, col);
+            kf = dfrag_t32(tK, 32 * dt + l32, KS * (KPS * st + kk) + E * hl);
           }
           dq[dt] = M::mma(kf, sf[kk], dq[dt]);
         }
     }
   }
 
-  template <int SEG>
-  __device__ __forceinline__ void segment(int tb, int te) {
-    for (int t = tb; t < te; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < nkt) issue(t + 1, buf ^ 1);
-      tile<SEG>(t, buf);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
+  // Tile t from buffer BUF with the loads of tile t + 1 in flight; tiles
+  // [0, t1) are left-saturated, [t2, nkt) right-saturated.
+  template <int BUF>
+  __device__ __forceinline__ void step(int t, int t1, int t2) {
+    if (t + 1 < nkt) issue<BUF ^ 1>(t + 1);
+    // tiles with masked entries also take the band body
+    const int j0 = t * kTile;
+    const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
+    if ((t >= t1 && t < t2) || masked)
+      tile<true, BUF>(t, KIND_BAND);
+    else
+      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+
+  __device__ __forceinline__ void run(int t1, int t2) {
+    if (nkt > 0) issue<0>(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    for (int t = 0; t < nkt; t += 2) {
+      step<0>(t, t1, t2);
+      if (t + 1 < nkt) step<1>(t + 1, t1, t2);
     }
   }
 };
 
-template <typename T>
+// ZK: whether the key-side relation term is present (compile-time switch).
+template <typename T, bool ZK>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   using M = MT<T>;
   using B = BwdQ<T>;
   constexpr int TB = DTile<T>::BYTES;
-  __shared__ __align__(16) char sK[2 * TB];
-  __shared__ __align__(16) char sKt[B::kHalf ? 2 * TB : 16];
-  __shared__ __align__(16) char sV[2 * TB];
-  __shared__ __align__(16) float sZK[2 * 2 * kTile];
+  __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
+  __shared__ __align__(16) char sKt0[B::kHalf ? TB : 16], sKt1[B::kHalf ? TB : 16];
+  __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
 
   B q;
-  q.sK = sK;
-  q.sKt = sKt;
-  q.sV = sV;
-  q.sZK = sZK;
+  q.sK[0] = sK0;
+  q.sK[1] = sK1;
+  q.sKt[0] = sKt0;
+  q.sKt[1] = sKt1;
+  q.sV[0] = sV0;
+  q.sV[1] = sV1;
+  q.sZK[0] = sZK0;
+  q.sZK[1] = sZK1;
   q.g = a.geo;
   const Geo& g = q.g;
   const int N = g.N;
   q.N = N;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   q.w = w;
   q.lane = lane;
   q.hl = hl;
@@ -173,6 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   if (g.causal) qb = a.nblk - 1 - qb;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
+  q.i0 = i0;
   q.iw0 = iw0;
 
   int kv_end = N;
@@ -193,6 +226,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   if constexpr (B::kHalf) {
     q.Ktb = (const T*)a.kt + (int64_t)bh * kHeadDim * a.Np;
     q.ldKt.init(a.Np, w, lane);
+    const int sig = sigma<T>(l32);
+#pragma unroll
+    for (int ks = 0; ks < B::NSD; ++ks) q.kofs[ks] = dt_off<T>(sig, B::KS * ks + B::E * hl);
+#pragma unroll
+    for (int c4 = 0; c4 < 2 * B::KPS; ++c4) q.tofs[c4] = dt_off<T>(l32, B::KS * c4 + B::E * hl);
   }
 
   QCtx& c = q.c;
@@ -201,10 +239,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   c.sig = sigma<T>(l32);
   c.kv_end = kv_end;
   c.has_zq = a.flags & F_ZQ;
-  c.has_zk = a.flags & F_ZK;
+  c.has_zk = ZK;
   c.has_b = a.flags & F_B;
   c.wsq = win_q(g, qb);
-  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + iq) * g.W : nullptr;
+  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.W : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.W : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   q.need_dz = a.flags & F_ZQ_NEEDED;
@@ -233,12 +271,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   const int t1 = imin(nkt, imax(0, floor_div_q(g.lo + i0 - (kTile - 1), kTile) + 1));
   const int t2 = imin(nkt, imax(t1, ceil_div_q(g.hi + i0 + kBlockRows - 1, kTile)));
 
-  if (nkt > 0) q.issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  q.template segment<KIND_LO>(0, t1);
-  q.template segment<KIND_BAND>(t1, t2);
-  q.template segment<KIND_HI>(t2, nkt);
+  q.run(t1, t2);
 
   if (iq < N) {
     // dQ = tau * dS K  (plus dZ^Q aQ added by the contraction when aQ is present)
@@ -266,8 +299,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   }
 
   if (q.need_dz) {
-    float acc_lo = q.acc_lo + __shfl_xor(q.acc_lo, 32);
-    float acc_hi = q.acc_hi + __shfl_xor(q.acc_hi, 32);
+    float acc_lo = sum_xor32(q.acc_lo);
+    float acc_hi = sum_xor32(q.acc_hi);
     float* dz_row = q.dz_row;
     if (iq < N) {
       int cb, ce;
@@ -296,7 +329,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
 template <typename T>
 static hipError_t launch_bwd_q_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
-  hipLaunchKernelGGL(bwd_q_kernel<T>, dim3(total), dim3(kThreads), 0, st, a);
+  if (a.flags & F_ZK)
+    hipLaunchKernelGGL((bwd_q_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_q_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -40,62 +40,104 @@ struct Fwd {
   static constexpr int KPS = 32 / KS;  // MFMA k-steps per 32-key half
   static constexpr int TB = DTile<T>::BYTES;
 
-  char* sK;    // [2][TB]
-  char* sV;    // [2][TB]  V^T (16-bit) or V (fp32)
-  float* sZK;  // [2][2 * kTile]
+  // LDS buffers, two of each (separate arrays, so that the compiler can tell
+  // the asynchronous loads into one buffer from the reads of the other)
+  char* sK[2];    // K tile
+  char* sV[2];    // V^T (16-bit) or V (fp32) tile
+  float* sZK[2];  // saturated Z^K scalars of the tile's keys [2][kTile]
 
   Geo g;
   QCtx c;
-  int tid, w, lane, hl, l32, iw0, nkt, N;
+  int tid, w, lane, hl, l32, i0, iw0, nkt, N;
   float cst_lo, cst_hi, sc2;
   const T* Kb;   // K of this (b, h)
   const T* Vb;   // V^T copy (16-bit, row stride Np) or V (fp32)
   int64_t sk, Np;
   DLoader<T> ldK, ldV;
+  // per-lane LDS byte offsets of the 16-bit operand fragments (buffer 0):
+  // K row sigma(l32) at k-step ks; V^T row l32 at key chunk column c4
+  int kofs[kHalf ? NSD : 1];
+  int vofs[kHalf ? 2 * KPS : 1];
   frag qf[NSD];
   f32x16 oacc[2];
   float m_used, lsum;
 
-  // Issue the loads of tile t into LDS buffer buf (asynchronous).
-  __device__ __forceinline__ void issue(int t, int buf) {
+  // Issue the loads of tile t into LDS buffer BUF (asynchronous).
+  template <int BUF>
+  __device__ __forceinline__ void issue(int t) {
     const int j0 = t * kTile;
-    ldK.load(sK + buf * TB, Kb + (int64_t)j0 * sk, N - j0, lane);
+    ldK.load(sK[BUF], Kb + (int64_t)j0 * sk, N - j0, lane);
     if constexpr (kHalf) {
-      ldV.load(sV + buf * TB, Vb + j0, 64, lane);
+      ldV.load(sV[BUF], Vb + j0, 64, lane);
     } else {
-      ldV.load(sV + buf * TB, Vb + (int64_t)j0 * Np, N - j0, lane);
+      ldV.load(sV[BUF], Vb + (int64_t)j0 * Np, N - j0, lane);
     }
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
-      dword_direct((char*)(sZK + buf * 2 * kTile + w * kTile), p, p != nullptr, lane);
+      dword_direct((char*)(sZK[BUF] + w * kTile), p, p != nullptr, lane);
     }
   }
 
-  // One 64-key tile for this wave; SEG is the block-level kind of the tile.
-  template <int SEG>
-  __device__ __forceinline__ void tile(int t, int buf) {
+  // V^T fragment (rows d = 32 dt + l32, keys of chunk column c4) of P V.
+  __device__ __forceinline__ frag vfrag(const char* tV, int dt, int c4) const {
+    if constexpr (kHalf) {
+      return *reinterpret_cast<const frag*>(tV + vofs[c4] + dt * 32 * DTile<T>::ROWB);
+    } else {
+      return dfrag_t32(tV, 32 * dt + l32, KS * c4 + E * hl);
+    }
+  }
+
+  // One 64-key tile for this wave, read from LDS buffer BUF.  BAND: the
+  // block's tile crosses the band (each wave refines the kind for its own
+  // queries); otherwise the whole tile is saturated on side `sat`.
+  template <bool BAND, int BUF>
+  __device__ __forceinline__ void tile(int t, int sat) {
     const int j0 = t * kTile;
-    if (iw0 >= N || (g.causal && j0 > iw0 + 31)) return;
-    const int kind = SEG == KIND_BAND ? tile_kind_q(g, j0, iw0) : SEG;
-    const bool needmask = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0);
-    const char* tK = sK + buf * TB;
-    const char* tV = sV + buf * TB;
-    const float* zk = sZK + buf * 2 * kTile;
+    // (a saturated body also runs for a wave whose queries are all beyond N:
+    // its results are discarded, and skipping would cost a branch and
+    // register copies in every tile)
+    if (BAND && (iw0 >= N || (g.causal && j0 > iw0 + 31))) return;
+    const int kind = BAND ? tile_kind_q(g, j0, iw0) : sat;
+    // masks are only applied in the band body (a saturated body is only
+    // used for tiles that need no mask anywhere in the block)
+    const bool needmask = BAND && ((j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0));
+    const char* tK = sK[BUF];
+    const char* tV = sV[BUF];
+    const float* zk = sZK[BUF];
     const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
-    // the two 32-key halves of the tile, one after the other (each its own
-    // online-softmax step)
+    // 16-bit types: every operand fragment of the tile is read from LDS up
+    // front (one batch of ds_read_b128), so the reads of the second half
+    // overlap the first half's MFMAs and softmax
+    frag kf[2][NSD], vf[2][2 * KPS];
+    if constexpr (kHalf) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int ks = 0; ks < NSD; ++ks) kf[st][ks] = kfrag<T>(tK, kofs, c, st, ks);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int kk = 0; kk < KPS; ++kk) vf[st][dt * KPS + kk] = vfrag(tV, dt, KPS * st + kk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
+      if constexpr (!kHalf) {
+#pragma unroll
+        for (int ks = 0; ks < NSD; ++ks) kf[st][ks] = kfrag<T>(tK, kofs, c, st, ks);
+      }
       f32x16 s;
-      if (SEG == KIND_BAND && kind == KIND_BAND)
-        s = qside_scores<T>(g, c, tK, zk, qf, KIND_BAND, j0, st, needmask);
+      if (BAND && kind == KIND_BAND)
+        s = qside_scores<T>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask);
       else
-        s = qside_scores<T>(g, c, tK, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
+        s = qside_scores<T>(g, c, kf[st], zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
                             needmask);
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(mx);
       const float mt = (mx + cst) * sc2;
       const bool need = mt > m_used + 8.f;
       if (__any(need)) {
@@ -115,61 +157,74 @@ struct Fwd {
       // P is rounded to the input type for P V; the normaliser sums the same
       // rounded values
       frag pf[KPS];
-      float part[KPS];
 #pragma unroll
       for (int kk = 0; kk < KPS; ++kk) {
         pf[kk] = M::pack(&p[kk * E]);
-        part[kk] = M::sum_acc(pf[kk], 0.f);
+        lsum = M::sum_acc(pf[kk], lsum);
       }
-#pragma unroll
-      for (int kk = 0; kk < KPS; ++kk) lsum += part[kk];
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int kk = 0; kk < KPS; ++kk) {
-          const int col = KS * (KPS * st + kk) + E * hl;
-          frag vf;
-          if constexpr (kHalf) {
-            vf = dfrag<T>(tV, 32 * dt + l32, col);
-          } else {
-            vf = dfrag_t32(tV, 32 * dt + l32, col);
-          }
-          oacc[dt] = M::mma(vf, pf[kk], oacc[dt]);
-        }
+        for (int kk = 0; kk < KPS; ++kk)
+          oacc[dt] = M::mma(kHalf ? vf[st][dt * KPS + kk] : vfrag(tV, dt, KPS * st + kk), pf[kk],
+                            oacc[dt]);
     }
   }
 
-  template <int SEG>
-  __device__ __forceinline__ void segment(int tb, int te) {
-    for (int t = tb; t < te; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < nkt) issue(t + 1, buf ^ 1);
-      tile<SEG>(t, buf);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of tile t+1 landed
-      __syncthreads();
+  // Tile t from buffer BUF, with the loads of tile t + 1 into the other
+  // buffer in flight.  Tiles [0, t1) are left-saturated, [t2, nkt)
+  // right-saturated, the rest cross the band; tiles with masked entries
+  // (the key-length edge, the causal diagonal) also take the band body.
+  template <int BUF>
+  __device__ __forceinline__ void step(int t, int t1, int t2) {
+    if (t + 1 < nkt) issue<BUF ^ 1>(t + 1);
+    const int j0 = t * kTile;
+    const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
+    if ((t >= t1 && t < t2) || masked)
+      tile<true, BUF>(t, KIND_BAND);
+    else
+      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of tile t+1 landed
+    __syncthreads();
+  }
+
+  __device__ __forceinline__ void run(int t1, int t2) {
+    if (nkt > 0) issue<0>(0);
+    // every load issued so far (Q fragments, tile 0) has landed: inside the
+    // loop a wave only waits for its own next-tile loads, before the barrier
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    for (int t = 0; t < nkt; t += 2) {
+      step<0>(t, t1, t2);
+      if (t + 1 < nkt) step<1>(t + 1, t1, t2);
     }
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 3) void fwd_kernel(AttnArgs a) {
+// ZK: whether the key-side relation term is present (a compile-time switch, so
+// that saturated tiles without it seed their MFMA accumulators with zero and
+// carry no branch).
+template <typename T, bool ZK>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnArgs a) {
   using M = MT<T>;
   constexpr float kLn2 = 0.693147180559945309f;
   constexpr int TB = DTile<T>::BYTES;
 
-  __shared__ __align__(16) char sK[2 * TB];
-  __shared__ __align__(16) char sV[2 * TB];
-  __shared__ __align__(16) float sZK[2 * 2 * kTile];
+  __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
+  __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
 
   Fwd<T> f;
-  f.sK = sK;
-  f.sV = sV;
-  f.sZK = sZK;
+  f.sK[0] = sK0;
+  f.sK[1] = sK1;
+  f.sV[0] = sV0;
+  f.sV[1] = sV1;
+  f.sZK[0] = sZK0;
+  f.sZK[1] = sZK1;
   f.g = a.geo;
   const Geo& g = f.g;
   const int N = g.N;
   f.N = N;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   f.tid = tid;
   f.w = w;
   f.lane = lane;
@@ -182,6 +237,7 @@ __global__ __launch_bounds__(kThreads, 3) void fwd_kernel(AttnArgs a) {
   if (g.causal) qb = a.nblk - 1 - qb;  // longest rows first
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
+  f.i0 = i0;
   f.iw0 = iw0;
 
   int kv_end = N;
@@ -204,6 +260,15 @@ __global__ __launch_bounds__(kThreads, 3) void fwd_kernel(AttnArgs a) {
     f.ldV.init(a.sv.n, w, lane);
   }
   f.ldK.init(a.sk.n, w, lane);
+  if constexpr (Fwd<T>::kHalf) {
+    const int sig = sigma<T>(l32);
+#pragma unroll
+    for (int ks = 0; ks < Fwd<T>::NSD; ++ks)
+      f.kofs[ks] = dt_off<T>(sig, Fwd<T>::KS * ks + Fwd<T>::E * hl);
+#pragma unroll
+    for (int c4 = 0; c4 < 2 * Fwd<T>::KPS; ++c4)
+      f.vofs[c4] = dt_off<T>(l32, Fwd<T>::KS * c4 + Fwd<T>::E * hl);
+  }
 
   QCtx& c = f.c;
   c.iq = iq;
@@ -211,10 +276,10 @@ __global__ __launch_bounds__(kThreads, 3) void fwd_kernel(AttnArgs a) {
   c.sig = sigma<T>(l32);
   c.kv_end = kv_end;
   c.has_zq = a.flags & F_ZQ;
-  c.has_zk = a.flags & F_ZK;
+  c.has_zk = ZK;
   c.has_b = a.flags & F_B;
   c.wsq = win_q(g, qb);
-  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + iq) * g.W : nullptr;
+  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.W : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.W : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
@@ -236,16 +301,9 @@ __global__ __launch_bounds__(kThreads, 3) void fwd_kernel(AttnArgs a) {
   const int t1 = imin(nkt, imax(0, floor_div(g.lo + i0 - (kTile - 1), kTile) + 1));
   const int t2 = imin(nkt, imax(t1, ceil_div(g.hi + i0 + kBlockRows - 1, kTile)));
 
-  if (nkt > 0) f.issue(0, 0);
-  // every load issued so far (Q fragments, tile 0) has landed: inside the
-  // loops a wave only waits for its own next-tile loads, before the barrier
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  f.template segment<KIND_LO>(0, t1);
-  f.template segment<KIND_BAND>(t1, t2);
-  f.template segment<KIND_HI>(t2, nkt);
+  f.run(t1, t2);
 
-  const float ltot = f.lsum + __shfl_xor(f.lsum, 32);
+  const float ltot = sum_xor32(f.lsum);
   if (iq < N) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     T* orow = (T*)a.o_out + bb * a.so.b + hh * a.so.h + (int64_t)iq * a.so.n;
@@ -265,7 +323,10 @@ __global__ __launch_bounds__(kThreads, 3) void fwd_kernel(AttnArgs a) {
 template <typename T>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
-  hipLaunchKernelGGL(fwd_kernel<T>, dim3(total), dim3(kThreads), 0, st, a);
+  if (a.flags & F_ZK)
+    hipLaunchKernelGGL((fwd_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

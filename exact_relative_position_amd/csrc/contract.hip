@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   const int lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / a.nblk, rb = lid - bh * a.nblk;
   const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int i0 = rb * kBlockRows;
   int cb, ce, ws;
   if (a.key_side) {
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
   const Geo g = a.geo;
   const int N = g.N;
   const int rt = blockIdx.x, sp = blockIdx.y, ho = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int u = 32 * rt + l32;  // unfolded row of this lane (operand A row)
   const int nseg = a.shared ? a.B * a.H : a.B;
   const int64_t nrows = (int64_t)nseg * N;

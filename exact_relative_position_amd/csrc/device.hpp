@@ -129,6 +129,12 @@ __device__ inline f32x16 zero16() {
   return z;
 }
 
+// Index of this thread's wavefront in the workgroup, as a wave-uniform value
+// (readfirstlane), so that the compiler keeps everything derived from it --
+// tile kinds, mask decisions, segment bounds -- in scalar registers and
+// branches on it with scalar branches.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that blocks
 // consecutive in the logical order run on the same XCD (and share its L2).
 __device__ inline int xcd_remap(int bid, int total) {
@@ -138,6 +144,19 @@ __device__ inline int xcd_remap(int bid, int total) {
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine a value with the one of lane l ^ 32 (v_permlane32_swap: one VALU
+// operation, no trip through the LDS crossbar).
+__device__ inline float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // s_waitcnt immediate for "vmcnt(0)" with the other counters left alone
 // (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   }
   const int c0 = cb + ct * 64;
   if (c0 >= ce) return;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int i = grp * kBlockRows + 32 * w + l32;  // row loaded by this lane (operand A)
 
   const T* xrow = (const T*)a.x + bb * a.sx.b + hh * a.sx.h + (int64_t)i * a.sx.n;

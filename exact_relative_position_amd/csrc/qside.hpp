@@ -38,38 +38,87 @@ struct QCtx {
   int sig;               // sigma(l % 32)
   int kv_end;            // keys >= kv_end are masked
   int wsq;               // first unfolded row of this group's Z^Q window
-  const float* zq_row;   // Z^Q row of iq (valid when has_zq and iq < N)
+  const float* zq_row;   // Z^Q row of min(iq, N - 1) (when has_zq)
   const float* zkb;      // Z^K of this (b, h)
   const float* bun;      // unfolded b of this head
   bool has_zq, has_zk, has_b;
 };
 
-// Relation response rel(i, j) for a band entry (0 for masked entries).
-__device__ inline float band_rel(const Geo& g, const QCtx& c, int j, int i) {
-  float v = 0.f;
-  int r = rrow(g, j - i);
-  if (c.has_zq) v += c.zq_row[r - c.wsq];
-  if (c.has_zk) v += c.zkb[(int64_t)j * g.W + r - win_k(g, j / kGroup)];
-  if (c.has_b) v += c.bun[r];
-  return v;
+// Key offset, inside a 32-key subtile, of result element e of lane-half h
+// (= kappa(h, e)) split into its lane-independent part.
+template <typename T>
+__device__ constexpr int kap0(int e) {
+  return MT<T>::KS * (e / MT<T>::E) + e % MT<T>::E;
+}
+
+// Relation response of the 16 band entries of this lane (keys
+// jb + kap0(e), jb = j0 + 32 st + E * hl).  Every load is issued without a
+// branch at an address clamped into its row, so the 16 (or 32, 48) loads of
+// a subtile are in flight together.  Entries that are not live (key beyond
+// the valid keys, causal future, query beyond N) are either replaced by -inf
+// afterwards or belong to a discarded row, so what such a clamped load
+// returns never reaches a result.  For a live entry the clamp is the
+// identity: its unfolded row lies inside the group's window.
+template <typename T>
+__device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, int wk,
+                                          f32x16& s) {
+  const int Wm = g.W - 1;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = 0.f;
+  if (c.has_zq) {
+    const int base = jb - c.iq - g.lo - c.wsq;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = c.zq_row[imin(imax(base + kap0<T>(e), 0), Wm)];
+  }
+  if (c.has_zk) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = imin(jb + kap0<T>(e), g.N - 1);
+      const int col = imin(imax(j - c.iq - g.lo - wk, 0), Wm);
+      v[e] += c.zkb[(int64_t)j * g.W + col];
+    }
+  }
+  if (c.has_b) {
+    const int base = jb - c.iq - g.lo;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] += c.bun[imin(imax(base + kap0<T>(e), 0), g.R - 1)];
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s[e] = v[e];
+}
+
+// K fragment of k-step ks for the A operand of S^T = K Q^T: tile row
+// 32 st + sigma(l % 32).  16-bit types read at the lane's precomputed byte
+// offset kofs[ks] (row sigma, swizzled chunk), shifted by 32 st rows.
+template <typename T>
+__device__ __forceinline__ typename MT<T>::frag kfrag(const char* sK, const int* kofs,
+                                                      const QCtx& c, int st, int ks) {
+  constexpr int ROWB = DTile<T>::ROWB;
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const typename MT<T>::frag*>(sK + kofs[ks] + 32 * st * ROWB);
+  } else {
+    return dfrag<T>(sK, 32 * st + c.sig, MT<T>::KS * ks + MT<T>::E * c.hl);
+  }
 }
 
 // Raw scores of the 32 keys [j0 + 32 st, j0 + 32 st + 32) for this lane's
 // query, masked entries = -inf; element e <-> key j0 + 32 st + kappa(hl, e).
 // The per-query constant of a saturated tile (Z^Q of the saturated row plus
 // b) is NOT included.
+// kf: the NSD K fragments of this subtile (kfrag), already read from LDS.
 template <typename T>
-__device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c, const char* sK,
-                                               const float* sZK,
+__device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c,
+                                               const typename MT<T>::frag* kf, const float* sZK,
                                                const typename MT<T>::frag* qf, int kind,
                                                int j0, int st, bool needmask) {
   using M = MT<T>;
-  constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
+  constexpr int NSD = kHeadDim / M::KS;
   f32x16 s;
   int ks0 = 0;
   if (kind != KIND_BAND && !c.has_zk) {
     // constant tile without a key term: the accumulator starts at literal zero
-    s = M::mma(dfrag<T>(sK, 32 * st + c.sig, E * c.hl), qf[0], zero16());
+    s = M::mma(kf[0], qf[0], zero16());
     ks0 = 1;
   } else if (kind != KIND_BAND) {
     // constant tile: one Z^K scalar per key seeds the accumulator
@@ -78,17 +127,12 @@ __device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c, cons
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = v[e];
   } else {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = j0 + 32 * st + kappa<T>(c.hl, e);
-      const bool live = c.iq < g.N && j < c.kv_end && !(g.causal && j > c.iq);
-      s[e] = live ? band_rel(g, c, j, c.iq) : 0.f;
-    }
+    band_seed<T>(g, c, j0 + 32 * st + MT<T>::E * c.hl, win_k(g, j0 / kGroup), s);
   }
 #pragma unroll
   for (int ks = 0; ks < NSD; ++ks) {
     if (ks < ks0) continue;
-    s = M::mma(dfrag<T>(sK, 32 * st + c.sig, KS * ks + E * c.hl), qf[ks], s);
+    s = M::mma(kf[ks], qf[ks], s);
   }
   if (needmask) {
 #pragma unroll

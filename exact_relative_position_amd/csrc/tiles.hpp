@@ -133,8 +133,12 @@ __device__ inline void tile_store_tr(T* lds, const Chunk (&r)[TileCfg<T>::NCH], 
 // global_load_lds_dwordx4: each lane's 16 bytes land at lds_base + 16 * lane,
 // so the LDS position is set by which lane loads which chunk.  Rows are
 // stored unpadded (ROWB bytes); inside a row the 16-byte chunks are permuted
-// by an XOR with swz(row) so that the 8 rows read together by the
-// sigma-permuted MFMA operand loads fall on 8 different bank groups.
+// by an XOR with swz(row).  The MFMA operand reads are ds_read_b128 of one
+// chunk column over 16 rows at a time, either 16 consecutive rows or the
+// sigma-permuted set {0-3, 8-11, 4-7, 12-15}; with 128-byte rows (16-bit
+// types) the swizzle below puts each such group of 16 rows, and each group
+// of 8 consecutive lanes within it, on distinct 16-byte bank groups of a
+// 256-byte LDS window, so the reads are free of bank conflicts.
 // Rows beyond the valid count are zero-filled with ordinary LDS stores.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -149,9 +153,16 @@ struct DTile {
   static constexpr int PER_WAVE = 64 * CPR / 64 / 4;  // 64-lane loads per wave per tile
 };
 
+// Chunk permutation of row r.  16-bit: r & 7, with 5 XORed in for the odd
+// 8-row half (a linear map of the row bits whose restrictions to the even
+// rows, to the odd rows, to rows {0-3, 8-11} and to rows 0-7 are bijective).
 template <typename T>
 __device__ __forceinline__ int swz(int r) {
-  return (r + ((r >> 3) << 2)) & (DTile<T>::CPR - 1);
+  if constexpr (sizeof(T) == 2) {
+    return (r & 7) ^ (((r >> 3) & 1) * 5);
+  } else {
+    return (r + ((r >> 3) << 2)) & (DTile<T>::CPR - 1);
+  }
 }
 
 // Byte offset of element (r, c) inside a direct tile.
