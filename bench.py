@@ -102,6 +102,42 @@ def cpu_baseline(w, x, min_seconds=10.0):
                       f"at full N={w.N}, fp64 NumPy"}
 
 
+KERNEL_SOURCES = {
+    name: (src, "qside.hpp", "tiles.hpp", "device.hpp", "geometry.hpp")
+    for name, src in (("fwd_kernel", "attn_fwd.hip"), ("bwd_q_kernel", "attn_bwd_q.hip"),
+                      ("bwd_k_kernel", "attn_bwd_k.hip"))
+}
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the HIP sources that define one attention kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_relative_position_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel's
+    source has changed since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    want = kernel_source_hash(kernel)
+    for line in lines:
+        f = line.split()
+        if len(f) == 5 and f[0] == "traffic" and f[1] == kernel and f[2] == workload:
+            kv = dict(x.split("=", 1) for x in f[3:])
+            if kv.get("sha256") == want:
+                return int(kv["bytes"])
+    return None
+
+
 def copy_probe(torch, dev, mib):
     """One plain device-to-device copy of `mib` MiB, outside the timed region:
     its HBM counter readings calibrate the counters of the other kernels."""
@@ -225,7 +261,8 @@ def main():
                                     + zbytes + run.ws_f.numel()),
         "roofline": {"bound": "mfma", "kernel": kern_name[dom], "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None, "flops_per_launch": kern_flops[dom],
+                     "traffic": measured_traffic(kern_name[dom], w.name),
+                     "flops_per_launch": kern_flops[dom],
                      "ms_per_launch": round(stage_ms[dom], 4)},
         "cpu_baseline": None,
     }

@@ -13,10 +13,11 @@ audio-paper-digest page, section on the score formula, Eq. (1):
     S_ij = tau * (q_i.k_j + q_i.aQ[phi(i,j)] + k_j.aK[phi(i,j)] + b[phi(i,j)]) + M_ij
 
 followed by a row softmax and O = P V, together with the exact gradients of
-O with respect to every input.  The method on that page is exact (it "does not
-change the mathematical result"), so the oracle is the definition itself: it
-uses none of the method's structure (no projection windows, no tiling, no
-unfolding of buckets, no per-offset storage).
+O with respect to every input.  The page presents the method as exact: every
+reorganisation it makes leaves the result of Eq. (1) unchanged.  So the oracle
+is the definition itself: it uses none of the method's structure (no
+projection windows, no tiling, no unfolding of buckets, no per-offset
+storage).
 
 Modules
 -------
