@@ -263,6 +263,7 @@ struct WsBwd {
   float* zk = nullptr;
   float* L2 = nullptr;  // [B*H][Np]
   float* D = nullptr;   // [B*H][Np]
+  float* kseed = nullptr;  // [4][B*H][Np]
   void* kt = nullptr;   // K^T, Q^T, dO^T copies [B*H][64][Np] (16-bit types)
   void* qt = nullptr;
   void* dot = nullptr;
@@ -305,6 +306,7 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
   const size_t bhnp = (size_t)pl.B * pl.H * pl.Np;
   w.L2 = c.take<float>(sizeof(float) * bhnp);
   w.D = c.take<float>(sizeof(float) * bhnp);
+  w.kseed = c.take<float>(sizeof(float) * 4 * bhnp);
   if (pl.esz == 2) {
     w.kt = c.take<char>(2 * bhnp * kHeadDim);
     w.qt = c.take<char>(2 * bhnp * kHeadDim);
@@ -651,6 +653,7 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   a.dO = dO;
   a.L2 = w.L2;
   a.D = w.D;
+  a.kseed = w.kseed;
   a.kt = w.kt;
   a.qt = w.qt;
   a.dot = w.dot;
@@ -663,8 +666,9 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   a.dzq = w.dzq;
   a.dzk = w.dzk;
   if (stages & RELPOS_BWD_PREPARE) {
-    RowTermArgs r{O,   dO,  str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), lse, w.L2, w.D,
-                  pl.B, pl.H, pl.N, pl.Np};
+    RowTermArgs r{O,      dO,    str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), lse,
+                  w.L2,   w.D,   w.kseed, w.zq, pl.geo, prob->tau * 1.4426950408889634f,
+                  pl.B,   pl.H,  pl.N,    pl.Np};
     if ((s = hip_check(launch_rowterm(pl.dtype, r, st), "backward (row terms)")) != RELPOS_OK)
       return s;
     if (pl.esz == 2) {

@@ -35,98 +35,137 @@ struct BwdK {
   static constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
   static constexpr int KPS = 32 / KS;  // MFMA k-steps per 32-query half
   static constexpr int TB = DTile<T>::BYTES;
+  static constexpr int ROWB = DTile<T>::ROWB;
 
-  char* sQ;     // [2][TB] Q rows
-  char* sQt;    // [2][TB] Q^T (16-bit)
-  char* sO;     // [2][TB] dO rows
-  char* sOt;    // [2][TB] dO^T (16-bit)
-  float* sL;    // [2][kTile] padded log2-domain LSE of the tile's queries
-  float* sD;    // [2][kTile]
-  float* sZQ;   // [2][2 * kTile]
+  // LDS buffers, two of each (separate arrays, so that the compiler can tell
+  // the asynchronous loads into one buffer from the reads of the other)
+  char* sQ[2];     // Q rows
+  char* sQt[2];    // Q^T (16-bit)
+  char* sO[2];     // dO rows
+  char* sOt[2];    // dO^T (16-bit)
+  float* sR[2];    // [4][kTile] per-query seeds of the tile (see RowTermArgs)
 
   Geo g;
-  int w, lane, hl, l32, jw0, jk, sig, ntq, N, kv_end, wsk;
+  int w, lane, hl, l32, j0b, jw0, jk, sig, ntq, N, kv_end, wsk;
   bool has_zq, has_zk, has_b;
-  float cst_lo, cst_hi, sc2, tau;
+  float off_lo, off_hi, sc2, tau;
   const T* Qb;
   const T* Qtb;
   const T* Ob;
   const T* Otb;
-  const float* L2b;
-  const float* Db;
+  const float* seeds;   // [4][B*H][Np]: LO seed, HI seed, band seed, -D
+  int64_t seed_stride;  // B*H*Np
   const float* zq_bh;
   const float* zk_row;
   const float* bun;
   float* dz_row;
   int64_t sq, so, Np;
-  DLoader<T> ldQ, ldQt, ldO, ldOt;
+  DLoader<T> ldQ, ldO, ldT;  // ldT: both token-contiguous copies (row stride Np)
+  // per-lane LDS byte offsets of the 16-bit operand fragments (buffer 0):
+  // Q / dO row sigma(l32) at k-step ks; Q^T / dO^T row l32 at query chunk c4
+  int rofs[kHalf ? NSD : 1];
+  int tofs[kHalf ? 2 * KPS : 1];
   frag kf[NSD], vf[NSD];
   f32x16 dk[2], dv[2];
   float acc_lo, acc_hi;
 
-  __device__ __forceinline__ void issue(int t, int buf) {
+  template <int BUF>
+  __device__ __forceinline__ void issue(int t) {
     const int q0 = t * kTile;
-    ldQ.load(sQ + buf * TB, Qb + (int64_t)q0 * sq, N - q0, lane);
-    ldO.load(sO + buf * TB, Ob + (int64_t)q0 * so, N - q0, lane);
+    ldQ.load(sQ[BUF], Qb + (int64_t)q0 * sq, N - q0, lane);
+    ldO.load(sO[BUF], Ob + (int64_t)q0 * so, N - q0, lane);
     if constexpr (kHalf) {
-      ldQt.load(sQt + buf * TB, Qtb + q0, 64, lane);
-      ldOt.load(sOt + buf * TB, Otb + q0, 64, lane);
+      ldT.load(sQt[BUF], Qtb + q0, 64, lane);
+      ldT.load(sOt[BUF], Otb + q0, 64, lane);
     }
-    if (w == 0) {
-      dword_direct((char*)(sL + buf * kTile), L2b + q0 + lane, true, lane);
-    } else if (w == 1) {
-      dword_direct((char*)(sD + buf * kTile), Db + q0 + lane, true, lane);
-    } else if (has_zq) {
-      const float* p = qside_sat_ptr(g, zq_bh, q0 + lane, w - 2);
-      dword_direct((char*)(sZQ + buf * 2 * kTile + (w - 2) * kTile), p, p != nullptr, lane);
+    // wave w brings seed vector w of the tile's 64 queries
+    dword_direct((char*)(sR[BUF] + w * kTile), seeds + w * seed_stride + q0 + lane, true, lane);
+  }
+
+  // Row fragment (tile row 32 st + sigma(l32), k-step ks) of Q or dO.
+  __device__ __forceinline__ frag rfrag(const char* tile, int st, int ks) const {
+    if constexpr (kHalf) {
+      return *reinterpret_cast<const frag*>(tile + rofs[ks] + st * 32 * ROWB);
+    } else {
+      return dfrag<T>(tile, 32 * st + sig, KS * ks + E * hl);
+    }
+  }
+  // Transposed fragment (d row 32 dt + l32, query chunk column c4) of Q^T or dO^T.
+  __device__ __forceinline__ frag tfrag(const char* tile, const char* rowtile, int dt,
+                                        int c4) const {
+    if constexpr (kHalf) {
+      return *reinterpret_cast<const frag*>(tile + tofs[c4] + dt * 32 * ROWB);
+    } else {
+      return dfrag_t32(rowtile, 32 * dt + l32, KS * c4 + E * hl);
     }
   }
 
-  template <int SEG>
-  __device__ __forceinline__ void tile(int t, int buf) {
+  // Relation response of this lane's key against the 16 band queries
+  // ib + kap0(e) (all in the query group of the tile).  Every load is issued
+  // without a branch at an address clamped into its row (rows clamped to
+  // N - 1), so the loads of a subtile are in flight together.  Entries that
+  // are not live are replaced by -inf afterwards or belong to a discarded
+  // key; for a live entry the clamps are the identity.
+  __device__ __forceinline__ void band_rel(int ib, int wq, float (&v)[16]) const {
+    const int Wm = g.W - 1;
+    if (has_zq) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = imin(ib + kap0<T>(e), N - 1);
+        v[e] += zq_bh[(int64_t)i * g.W + imin(imax(jk - i - g.lo - wq, 0), Wm)];
+      }
+    }
+    if (has_zk) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        v[e] += zk_row[imin(imax(jk - ib - kap0<T>(e) - g.lo - wsk, 0), Wm)];
+    }
+    if (has_b) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        v[e] += bun[imin(imax(jk - ib - kap0<T>(e) - g.lo, 0), g.R - 1)];
+    }
+  }
+
+  // One 64-query tile from LDS buffer BUF.  BAND: the block's tile crosses
+  // the band or holds masked entries (each wave refines the kind for its
+  // own keys); otherwise the whole tile is saturated on side `sat`.
+  //
+  // Per 32-query half: S' = seed + Q K^T, where the seed (per query, from
+  // the row-term pass) already holds -LSE/(tau log2 e) and, on saturated
+  // tiles, the query-side saturated relation scalar; P = exp2(S' * tau
+  // log2 e + key-side constant).  dP' = -D + dO V^T, so dS = P * dP'.
+  template <bool BAND, int BUF>
+  __device__ __forceinline__ void tile(int t, int sat) {
     const int qt0 = t * kTile;
-    if (jw0 >= imin(N, kv_end) || (g.causal && qt0 + kTile - 1 < jw0)) return;
-    const int kind = SEG == KIND_BAND ? tile_kind_k(g, qt0, jw0) : SEG;
-    const bool needmask = (qt0 + kTile > N) || (jw0 + 32 > kv_end) || (g.causal && jw0 + 31 > qt0);
-    const char* tQ = sQ + buf * TB;
-    const char* tO = sO + buf * TB;
-    const char* tQt = kHalf ? sQt + buf * TB : tQ;
-    const char* tOt = kHalf ? sOt + buf * TB : tO;
-    const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
-    const float off = cst * sc2;
-    // the two 32-query halves of the tile, one after the other
+    if (BAND && (jw0 >= imin(N, kv_end) || (g.causal && qt0 + kTile - 1 < jw0))) return;
+    const int kind = BAND ? tile_kind_k(g, qt0, jw0) : sat;
+    // masks are only applied in the band body (a saturated body is only
+    // used for tiles that need no mask anywhere in the block)
+    const bool needmask =
+        BAND && ((qt0 + kTile > N) || (jw0 + 32 > kv_end) || (g.causal && jw0 + 31 > qt0));
+    const char* tQ = sQ[BUF];
+    const char* tO = sO[BUF];
+    const char* tQt = kHalf ? sQt[BUF] : tQ;
+    const char* tOt = kHalf ? sOt[BUF] : tO;
+    const float* sr = sR[BUF];
+    const float off = kind == KIND_LO ? off_lo : (kind == KIND_HI ? off_hi : 0.f);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       f32x16 s;
-      int ks0 = 0;
-      if (kind != KIND_BAND && !has_zq) {
-        s = M::mma(dfrag<T>(tQ, 32 * st + sig, E * hl), kf[0], zero16());
-        ks0 = 1;
-      } else if (kind != KIND_BAND) {
+      {
         float v[16];
-        lds_rows16<T>(sZQ + buf * 2 * kTile + (kind == KIND_LO ? 0 : kTile) + 32 * st, hl, v);
+        if (!BAND || kind != KIND_BAND) {
+          lds_rows16<T>(sr + (kind == KIND_LO ? 0 : kTile) + 32 * st, hl, v);
+        } else {
+          lds_rows16<T>(sr + 2 * kTile + 32 * st, hl, v);
+          band_rel(qt0 + 32 * st + E * hl, win_q(g, qt0 / kGroup), v);
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = v[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int i = qt0 + 32 * st + kappa<T>(hl, e);
-          const bool live = i < N && jk < kv_end && !(g.causal && jk > i);
-          float v = 0.f;
-          if (live) {
-            const int r = rrow(g, jk - i);
-            if (has_zq) v += zq_bh[(int64_t)i * g.W + r - win_q(g, i / kGroup)];
-            if (has_zk) v += zk_row[r - wsk];
-            if (has_b) v += bun[r];
-          }
-          s[e] = v;
-        }
       }
 #pragma unroll
-      for (int ks = 0; ks < NSD; ++ks) {
-        if (ks < ks0) continue;
-        s = M::mma(dfrag<T>(tQ, 32 * st + sig, KS * ks + E * hl), kf[ks], s);
-      }
+      for (int ks = 0; ks < NSD; ++ks) s = M::mma(rfrag(tQ, st, ks), kf[ks], s);
       if (needmask) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -134,40 +173,40 @@ struct BwdK {
           if (i >= N || jk >= kv_end || (g.causal && jk > i)) s[e] = -INFINITY;
         }
       }
-      f32x16 dp = M::mma(dfrag<T>(tO, 32 * st + sig, E * hl), vf[0], zero16());
+      f32x16 dp;
+      {
+        float v[16];
+        lds_rows16<T>(sr + 3 * kTile + 32 * st, hl, v);
 #pragma unroll
-      for (int ks = 1; ks < NSD; ++ks)
-        dp = M::mma(dfrag<T>(tO, 32 * st + sig, KS * ks + E * hl), vf[ks], dp);
+        for (int e = 0; e < 16; ++e) dp[e] = v[e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < NSD; ++ks) dp = M::mma(rfrag(tO, st, ks), vf[ks], dp);
 
       float p[16], ds[16];
-      {
-        float L[16], Dv[16];
-        lds_rows16<T>(sL + buf * kTile + 32 * st, hl, L);
-        lds_rows16<T>(sD + buf * kTile + 32 * st, hl, Dv);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[e] = exp2_fast(fmaf(s[e], sc2, off - L[e]));
-          ds[e] = p[e] * (dp[e] - Dv[e]);
-        }
+      for (int e = 0; e < 16; ++e) {
+        p[e] = exp2_fast(fmaf(s[e], sc2, off));
+        ds[e] = p[e] * dp[e];
       }
       if (has_zk) {
-        if (SEG != KIND_BAND || kind != KIND_BAND) {
+        if (!BAND || kind != KIND_BAND) {
           float tsum = 0.f;
 #pragma unroll
           for (int e = 0; e < 16; ++e) tsum += ds[e];
           if (kind == KIND_LO) acc_lo += tsum; else acc_hi += tsum;
         } else {
+          // saturated entries of a band tile go to the two accumulators
+          // (masked entries have ds = 0); interior live entries are stored
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int i = qt0 + 32 * st + kappa<T>(hl, e);
             const int o = jk - i;
-            if (o <= g.lo) {
-              acc_lo += ds[e];
-            } else if (o >= g.hi) {
-              acc_hi += ds[e];
-            } else if (i < N && jk < N && !(g.causal && jk > i)) {
+            // (lo == hi: an offset equal to both counts once, on the low side)
+            acc_lo += o <= g.lo ? ds[e] : 0.f;
+            acc_hi += (o > g.lo && o >= g.hi) ? ds[e] : 0.f;
+            if (o > g.lo && o < g.hi && i < N && jk < N && !(g.causal && jk > i))
               dz_row[o - g.lo - wsk] = tau * ds[e];
-            }
           }
         }
       }
@@ -181,54 +220,63 @@ struct BwdK {
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int kk = 0; kk < KPS; ++kk) {
-          const int col = KS * (KPS * st + kk) + E * hl;
-          frag of, qf;
-          if constexpr (kHalf) {
-            of = dfrag<T>(tOt, 32 * dt + l32, col);
-            qf = dfrag<T>(tQt, 32 * dt + l32, col);
-          } else {
-            of = dfrag_t32(tO, 32 * dt + l32, col);
-            qf = dfrag_t32(tQ, 32 * dt + l32, col);
-          }
-          dv[dt] = M::mma(of, pf[kk], dv[dt]);
-          dk[dt] = M::mma(qf, sf[kk], dk[dt]);
+          dv[dt] = M::mma(tfrag(tOt, tO, dt, KPS * st + kk), pf[kk], dv[dt]);
+          dk[dt] = M::mma(tfrag(tQt, tQ, dt, KPS * st + kk), sf[kk], dk[dt]);
         }
     }
   }
 
-  template <int SEG>
-  __device__ __forceinline__ void segment(int tb, int te) {
-    for (int t = tb; t < te; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntq) issue(t + 1, buf ^ 1);
-      tile<SEG>(t, buf);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
+  // Query tile t from buffer BUF with the loads of tile t + 1 in flight;
+  // tiles before tA have all offsets >= hi, tiles from tB on all <= lo.
+  template <int BUF>
+  __device__ __forceinline__ void step(int t, int tA, int tB) {
+    if (t + 1 < ntq) issue<BUF ^ 1>(t + 1);
+    // tiles with masked entries also take the band body
+    const int qt0 = t * kTile;
+    const bool masked = (qt0 + kTile > N) || (j0b + kBlockRows > kv_end) ||
+                        (g.causal && j0b + kBlockRows - 1 > qt0);
+    if ((t >= tA && t < tB) || masked)
+      tile<true, BUF>(t, KIND_BAND);
+    else
+      tile<false, BUF>(t, t < tA ? KIND_HI : KIND_LO);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+
+  // the tile t_begin goes to buffer 0; tile t to buffer (t - t_begin) & 1
+  __device__ __forceinline__ void run(int t_begin, int tA, int tB) {
+    if (t_begin < ntq) issue<0>(t_begin);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    for (int t = t_begin; t < ntq; t += 2) {
+      step<0>(t, tA, tB);
+      if (t + 1 < ntq) step<1>(t + 1, tA, tB);
     }
   }
 };
 
-template <typename T>
+// ZQ: whether the query-side relation term is present (compile-time switch).
+template <typename T, bool ZQ>
 __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   using M = MT<T>;
   using K = BwdK<T>;
   constexpr int TB = DTile<T>::BYTES;
-  __shared__ __align__(16) char sQ[2 * TB];
-  __shared__ __align__(16) char sQt[K::kHalf ? 2 * TB : 16];
-  __shared__ __align__(16) char sO[2 * TB];
-  __shared__ __align__(16) char sOt[K::kHalf ? 2 * TB : 16];
-  __shared__ __align__(16) float sL[2 * kTile];
-  __shared__ __align__(16) float sD[2 * kTile];
-  __shared__ __align__(16) float sZQ[2 * 2 * kTile];
+  constexpr int TBH = K::kHalf ? TB : 16;
+  __shared__ __align__(16) char sQ0[TB], sQ1[TB], sO0[TB], sO1[TB];
+  __shared__ __align__(16) char sQt0[TBH], sQt1[TBH], sOt0[TBH], sOt1[TBH];
+  __shared__ __align__(16) float sR0[4 * kTile], sR1[4 * kTile];
 
   K k;
-  k.sQ = sQ;
-  k.sQt = sQt;
-  k.sO = sO;
-  k.sOt = sOt;
-  k.sL = sL;
-  k.sD = sD;
-  k.sZQ = sZQ;
+  k.sQ[0] = sQ0;
+  k.sQ[1] = sQ1;
+  k.sQt[0] = sQt0;
+  k.sQt[1] = sQt1;
+  k.sO[0] = sO0;
+  k.sO[1] = sO1;
+  k.sOt[0] = sOt0;
+  k.sOt[1] = sOt1;
+  k.sR[0] = sR0;
+  k.sR[1] = sR1;
   k.g = a.geo;
   const Geo& g = k.g;
   const int N = g.N;
@@ -244,10 +292,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   const int kb = lid - bh * a.nblk;  // causal: early key blocks have the most queries
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int j0b = kb * kBlockRows, jw0 = j0b + 32 * w, jk = jw0 + l32;
+  k.j0b = j0b;
   k.jw0 = jw0;
   k.jk = jk;
   k.sig = sigma<T>(l32);
-  k.has_zq = a.flags & F_ZQ;
+  k.has_zq = ZQ;
   k.has_zk = a.flags & F_ZK;
   k.has_b = a.flags & F_B;
 
@@ -270,33 +319,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   if constexpr (K::kHalf) {
     k.Qtb = (const T*)a.qt + (int64_t)bh * kHeadDim * a.Np;
     k.Otb = (const T*)a.dot + (int64_t)bh * kHeadDim * a.Np;
-    k.ldQt.init(a.Np, w, lane);
-    k.ldOt.init(a.Np, w, lane);
+    k.ldT.init(a.Np, w, lane);
+    const int sg = sigma<T>(l32);
+#pragma unroll
+    for (int ks = 0; ks < K::NSD; ++ks) k.rofs[ks] = dt_off<T>(sg, K::KS * ks + K::E * hl);
+#pragma unroll
+    for (int c4 = 0; c4 < 2 * K::KPS; ++c4) k.tofs[c4] = dt_off<T>(l32, K::KS * c4 + K::E * hl);
   }
-  k.L2b = a.L2 + (int64_t)bh * a.Np;
-  k.Db = a.D + (int64_t)bh * a.Np;
+  k.seed_stride = (int64_t)a.B * a.H * a.Np;
+  k.seeds = a.kseed + (int64_t)bh * a.Np;
   k.zq_bh = k.has_zq ? a.zq + (int64_t)bh * N * g.W : nullptr;
   k.bun = k.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   k.wsk = win_k(g, kb);
-  k.zk_row = k.has_zk ? a.zk + ((int64_t)bh * N + jk) * g.W : nullptr;
+  k.zk_row = k.has_zk ? a.zk + ((int64_t)bh * N + imin(jk, N - 1)) * g.W : nullptr;
   k.dz_row = k.has_zk ? a.dzk + ((int64_t)bh * N + jk) * g.W : nullptr;
   k.sc2 = a.scale2;
   k.tau = a.tau;
 
-  // Key-side constants of saturated tiles: Z^K[j, first/last row] + b.
-  k.cst_lo = 0.f;
-  k.cst_hi = 0.f;
+  // Key-side constants of saturated tiles, Z^K[j, first/last row] + b, in
+  // the exp2 domain.
+  float cst_lo = 0.f, cst_hi = 0.f;
   if (k.has_zk && jk < N) {
     int cb, ce;
     cols_k(g, kb, cb, ce);
     const int c0 = 0 - k.wsk, c1 = g.R - 1 - k.wsk;
-    if (c0 >= cb && c0 < ce) k.cst_lo += k.zk_row[c0];
-    if (c1 >= cb && c1 < ce) k.cst_hi += k.zk_row[c1];
+    if (c0 >= cb && c0 < ce) cst_lo += k.zk_row[c0];
+    if (c1 >= cb && c1 < ce) cst_hi += k.zk_row[c1];
   }
   if (k.has_b) {
-    k.cst_lo += k.bun[0];
-    k.cst_hi += k.bun[g.R - 1];
+    cst_lo += k.bun[0];
+    cst_hi += k.bun[g.R - 1];
   }
+  k.off_lo = cst_lo * a.scale2;
+  k.off_hi = cst_hi * a.scale2;
   {
     const T* krow = (const T*)a.k + bb * a.sk.b + hh * a.sk.h + (int64_t)jk * a.sk.n;
     const T* vrow = (const T*)a.v + bb * a.sv.b + hh * a.sv.h + (int64_t)jk * a.sv.n;
@@ -318,12 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   const int tA = imin(ntq, imax(t_begin, floor_div_k(j0b - (kTile - 1) - g.hi, kTile) + 1));
   const int tB = imin(ntq, imax(tA, ceil_div_k(j0b + kBlockRows - 1 - g.lo, kTile)));
 
-  if (t_begin < ntq) k.issue(t_begin, t_begin & 1);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  k.template segment<KIND_HI>(t_begin, tA);
-  k.template segment<KIND_BAND>(tA, tB);
-  k.template segment<KIND_LO>(tB, ntq);
+  k.run(t_begin, tA, tB);
 
   if (jk < N) {
     T* vrow = (T*)a.dv + bb * a.sdv.b + hh * a.sdv.h + (int64_t)jk * a.sdv.n;
@@ -359,8 +409,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   }
 
   if (k.has_zk) {
-    const float acc_lo = k.acc_lo + __shfl_xor(k.acc_lo, 32);
-    const float acc_hi = k.acc_hi + __shfl_xor(k.acc_hi, 32);
+    const float acc_lo = sum_xor32(k.acc_lo);
+    const float acc_hi = sum_xor32(k.acc_hi);
     float* dz_row = k.dz_row;
     const int wsk = k.wsk;
     if (jk < N) {
@@ -395,7 +445,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
 template <typename T>
 static hipError_t launch_bwd_k_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
-  hipLaunchKernelGGL(bwd_k_kernel<T>, dim3(total), dim3(kThreads), 0, st, a);
+  if (a.flags & F_ZQ)
+    hipLaunchKernelGGL((bwd_k_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_k_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -122,6 +122,7 @@ struct AttnArgs {
   const void* dO;
   const float* L2; // [B*H][Np] padded log2-domain LSE (backward)
   const float* D;  // [B*H][Np] padded row terms (backward)
+  const float* kseed;  // [4][B*H][Np] per-query seeds of the key pass (RowTermArgs)
   const void* vt;  // [B*H][64][Np] token-contiguous copies (16-bit types)
   const void* kt;
   const void* qt;
@@ -160,6 +161,15 @@ struct RowTermArgs {     // padded backward row terms
   const float* lse;      // [B*H][N]
   float* L2;             // [B*H][Np]  LSE * log2(e), +inf for dead and padded rows
   float* D;              // [B*H][Np]  sum_d dO O, 0 for padded rows
+  // Seeds of the key pass's MFMA accumulators, [4][B*H][Np], in units of the
+  // score before the tau * log2(e) scale:
+  //  0 / 1: Z^Q[i, first / last row] - L2 / (tau log2 e)  (saturated tiles)
+  //  2:     -L2 / (tau log2 e)                              (band tiles)
+  //  3:     -D
+  float* kseed;
+  const float* zq;       // [B*H][N][W] or null
+  Geo geo;
+  float scale2;          // tau * log2(e)
   int B, H, N, Np;
 };
 

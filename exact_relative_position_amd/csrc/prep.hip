@@ -9,9 +9,13 @@
 //    L2[i] = LSE_i * log2(e) (+inf for a row whose keys are all masked, and
 //    for padding, so that P = exp2(s - L2) = 0 there) and
 //    D[i] = sum_d dO_id O_id (0 for padding), the row term of
-//    dS = P (dP - D) in the FlashAttention backward.
+//    dS = P (dP - D) in the FlashAttention backward; and the per-query seeds
+//    of the key pass, which start its score accumulator at the row's
+//    -LSE (plus, on saturated tiles, the query-side saturated relation
+//    scalar) and its dP accumulator at -D.
 #include "device.hpp"
 #include "tiles.hpp"
+#include "qside.hpp"
 
 namespace relpos {
 
@@ -81,6 +85,19 @@ __global__ __launch_bounds__(kThreads) void rowterm_kernel(RowTermArgs a) {
       l2 = L == -INFINITY ? INFINITY : L * kLog2e;
     }
     a.L2[row] = l2;
+    const float base = -(l2 / a.scale2);
+    float zlo = 0.f, zhi = 0.f;
+    if (a.zq) {
+      const float* zqb = a.zq + bh * (int64_t)a.N * a.geo.W;
+      const float* p0 = qside_sat_ptr(a.geo, zqb, i, 0);
+      const float* p1 = qside_sat_ptr(a.geo, zqb, i, 1);
+      if (p0) zlo = *p0;
+      if (p1) zhi = *p1;
+    }
+    a.kseed[row] = zlo + base;
+    a.kseed[rows + row] = zhi + base;
+    a.kseed[2 * rows + row] = base;
+    a.kseed[3 * rows + row] = -acc;
   }
 }
 
