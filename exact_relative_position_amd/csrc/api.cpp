@@ -6,7 +6,7 @@
 //   map tables (T5 unfold) -> relation projection of the reachable window ->
 //   fused tiled forward.
 // Backward (backward section of the same page):
-//   token-contiguous operand copies and the padded row terms (LSE, D) ->
+//   the padded row terms (LSE, D, the key pass's seeds) ->
 //   query-parallel pass -> key-parallel pass ->
 //   dZ . table into dQ / dK -> dZ^T . Q / K into the table gradients ->
 //   fold of copied bucket columns.
@@ -22,7 +22,6 @@
 
 namespace relpos {
 hipError_t launch_fwd(int dtype, const AttnArgs& a, hipStream_t st);
-hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st);
 hipError_t launch_rowterm(int dtype, const RowTermArgs& a, hipStream_t st);
 hipError_t launch_bwd_q(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_bwd_k(int dtype, const AttnArgs& a, hipStream_t st);
@@ -251,7 +250,6 @@ struct WsFwd {
   float* bunf = nullptr;
   float* zq = nullptr;
   float* zk = nullptr;
-  void* vt = nullptr;  // V^T copy [B*H][64][Np] (16-bit types)
 };
 
 struct WsBwd {
@@ -264,9 +262,6 @@ struct WsBwd {
   float* L2 = nullptr;  // [B*H][Np]
   float* D = nullptr;   // [B*H][Np]
   float* kseed = nullptr;  // [4][B*H][Np]
-  void* kt = nullptr;   // K^T, Q^T, dO^T copies [B*H][64][Np] (16-bit types)
-  void* qt = nullptr;
-  void* dot = nullptr;
   float* dq_part = nullptr;
   float* dk_part = nullptr;
   float* dzq = nullptr;
@@ -286,7 +281,6 @@ size_t carve_fwd(const Plan& pl, bool zsave_given, void* base, WsFwd& w) {
     if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
     if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
   }
-  if (pl.esz == 2) w.vt = c.take<char>(2 * (size_t)pl.B * pl.H * kHeadDim * pl.Np);
   return c.off;
 }
 
@@ -307,11 +301,6 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
   w.L2 = c.take<float>(sizeof(float) * bhnp);
   w.D = c.take<float>(sizeof(float) * bhnp);
   w.kseed = c.take<float>(sizeof(float) * 4 * bhnp);
-  if (pl.esz == 2) {
-    w.kt = c.take<char>(2 * bhnp * kHeadDim);
-    w.qt = c.take<char>(2 * bhnp * kHeadDim);
-    w.dot = c.take<char>(2 * bhnp * kHeadDim);
-  }
   if (pl.has_aq) w.dq_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_ak) w.dk_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_aq || pl.has_b) w.dzq = c.take<float>(sizeof(float) * pl.z_elems);
@@ -564,11 +553,6 @@ relpos_status relpos_attn_fwd_stages(const relpos_problem* prob, const relpos_ph
   a.zq = w.zq;
   a.zk = w.zk;
   a.bunf = w.bunf;
-  if (pl.esz == 2) {
-    TransposeArgs t{V, str_of(prob, RELPOS_T_V), w.vt, pl.B, pl.H, pl.N, pl.Np};
-    if ((s = hip_check(launch_transpose(pl.dtype, t, st), "forward (V^T)")) != RELPOS_OK) return s;
-    a.vt = w.vt;
-  }
   return hip_check(launch_fwd(pl.dtype, a, st), "forward");
 }
 
@@ -654,9 +638,6 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   a.L2 = w.L2;
   a.D = w.D;
   a.kseed = w.kseed;
-  a.kt = w.kt;
-  a.qt = w.qt;
-  a.dot = w.dot;
   a.zq = w.zq;
   a.zk = w.zk;
   a.bunf = w.bunf;
@@ -671,16 +652,6 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
                   pl.B,   pl.H,  pl.N,    pl.Np};
     if ((s = hip_check(launch_rowterm(pl.dtype, r, st), "backward (row terms)")) != RELPOS_OK)
       return s;
-    if (pl.esz == 2) {
-      const struct { const void* x; int role; void* xt; } cp[3] = {
-          {K, RELPOS_T_K, w.kt}, {Q, RELPOS_T_Q, w.qt}, {dO, RELPOS_T_DO, w.dot}};
-      for (const auto& c : cp) {
-        TransposeArgs t{c.x, str_of(prob, c.role), c.xt, pl.B, pl.H, pl.N, pl.Np};
-        if ((s = hip_check(launch_transpose(pl.dtype, t, st), "backward (operand copies)")) !=
-            RELPOS_OK)
-          return s;
-      }
-    }
   }
   if (stages & RELPOS_BWD_QUERY_PASS) {
     if ((s = hip_check(launch_bwd_q(pl.dtype, a, st), "backward (query pass)")) != RELPOS_OK)

@@ -10,10 +10,10 @@
 //
 // One workgroup = one (batch, head, 128-key block); 4 waves x 32 keys; inner
 // loop over 64-query tiles.  Orientation S = Q K^T: lane l owns key l % 32.
-// Q and dO tiles go into LDS both row-major (operands of S = Q K^T and
-// dP = dO V^T, contracted over d) and transposed from query-contiguous
-// copies (operands of dV^T = dO^T P and dK^T = Q^T dS, contracted over the
-// queries), all by direct loads; the query loop runs in three segments.
+// Q and dO tiles go into LDS row-major by direct loads: they are the
+// operands of S = Q K^T and dP = dO V^T (contracted over d) as they are, and
+// of dV^T = dO^T P and dK^T = Q^T dS (contracted over the queries) through
+// ds_read_b64_tr_b16 transpose reads; the query loop runs in three segments.
 #include "qside.hpp"
 
 namespace relpos {
@@ -40,9 +40,7 @@ struct BwdK {
   // LDS buffers, two of each (separate arrays, so that the compiler can tell
   // the asynchronous loads into one buffer from the reads of the other)
   char* sQ[2];     // Q rows
-  char* sQt[2];    // Q^T (16-bit)
   char* sO[2];     // dO rows
-  char* sOt[2];    // dO^T (16-bit)
   float* sR[2];    // [4][kTile] per-query seeds of the tile (see RowTermArgs)
 
   Geo g;
@@ -50,9 +48,7 @@ struct BwdK {
   bool has_zq, has_zk, has_b;
   float off_lo, off_hi, sc2, tau;
   const T* Qb;
-  const T* Qtb;
   const T* Ob;
-  const T* Otb;
   const float* seeds;   // [4][B*H][Np]: LO seed, HI seed, band seed, -D
   int64_t seed_stride;  // B*H*Np
   const float* zq_bh;
@@ -60,11 +56,12 @@ struct BwdK {
   const float* bun;
   float* dz_row;
   int64_t sq, so, Np;
-  DLoader<T> ldQ, ldO, ldT;  // ldT: both token-contiguous copies (row stride Np)
-  // per-lane LDS byte offsets of the 16-bit operand fragments (buffer 0):
-  // Q / dO row sigma(l32) at k-step ks; Q^T / dO^T row l32 at query chunk c4
+  DLoader<T> ldQ, ldO;
+  // per-lane LDS byte offsets of the 16-bit row fragments (Q / dO row
+  // sigma(l32) at k-step ks); transposed fragments (Q^T, dO^T, contracted
+  // over the queries) come from the same row tiles through transpose reads
   int rofs[kHalf ? NSD : 1];
-  int tofs[kHalf ? 2 * KPS : 1];
+  TrReader<std::conditional_t<kHalf, T, _Float16>> tr;
   frag kf[NSD], vf[NSD];
   f32x16 dk[2], dv[2];
   float acc_lo, acc_hi;
@@ -74,10 +71,6 @@ struct BwdK {
     const int q0 = t * kTile;
     ldQ.load(sQ[BUF], Qb + (int64_t)q0 * sq, N - q0, lane);
     ldO.load(sO[BUF], Ob + (int64_t)q0 * so, N - q0, lane);
-    if constexpr (kHalf) {
-      ldT.load(sQt[BUF], Qtb + q0, 64, lane);
-      ldT.load(sOt[BUF], Otb + q0, 64, lane);
-    }
     // wave w brings seed vector w of the tile's 64 queries
     dword_direct((char*)(sR[BUF] + w * kTile), seeds + w * seed_stride + q0 + lane, true, lane);
   }
@@ -90,11 +83,11 @@ struct BwdK {
       return dfrag<T>(tile, 32 * st + sig, KS * ks + E * hl);
     }
   }
-  // Transposed fragment (d row 32 dt + l32, query chunk column c4) of Q^T or dO^T.
-  __device__ __forceinline__ frag tfrag(const char* tile, const char* rowtile, int dt,
-                                        int c4) const {
+  // Transposed fragment (d row 32 dt + l32, query chunk column c4) of Q^T or
+  // dO^T, read from the row tile.
+  __device__ __forceinline__ frag tfrag(const char* rowtile, int dt, int c4) const {
     if constexpr (kHalf) {
-      return *reinterpret_cast<const frag*>(tile + tofs[c4] + dt * 32 * ROWB);
+      return tr.read(rowtile, dt, c4);
     } else {
       return dfrag_t32(rowtile, 32 * dt + l32, KS * c4 + E * hl);
     }
@@ -146,8 +139,6 @@ struct BwdK {
         BAND && ((qt0 + kTile > N) || (jw0 + 32 > kv_end) || (g.causal && jw0 + 31 > qt0));
     const char* tQ = sQ[BUF];
     const char* tO = sO[BUF];
-    const char* tQt = kHalf ? sQt[BUF] : tQ;
-    const char* tOt = kHalf ? sOt[BUF] : tO;
     const float* sr = sR[BUF];
     const float off = kind == KIND_LO ? off_lo : (kind == KIND_HI ? off_hi : 0.f);
 #pragma unroll
@@ -220,8 +211,8 @@ struct BwdK {
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int kk = 0; kk < KPS; ++kk) {
-          dv[dt] = M::mma(tfrag(tOt, tO, dt, KPS * st + kk), pf[kk], dv[dt]);
-          dk[dt] = M::mma(tfrag(tQt, tQ, dt, KPS * st + kk), sf[kk], dk[dt]);
+          dv[dt] = M::mma(tfrag(tO, dt, KPS * st + kk), pf[kk], dv[dt]);
+          dk[dt] = M::mma(tfrag(tQ, dt, KPS * st + kk), sf[kk], dk[dt]);
         }
     }
   }
@@ -261,20 +252,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   using M = MT<T>;
   using K = BwdK<T>;
   constexpr int TB = DTile<T>::BYTES;
-  constexpr int TBH = K::kHalf ? TB : 16;
   __shared__ __align__(16) char sQ0[TB], sQ1[TB], sO0[TB], sO1[TB];
-  __shared__ __align__(16) char sQt0[TBH], sQt1[TBH], sOt0[TBH], sOt1[TBH];
   __shared__ __align__(16) float sR0[4 * kTile], sR1[4 * kTile];
 
   K k;
   k.sQ[0] = sQ0;
   k.sQ[1] = sQ1;
-  k.sQt[0] = sQt0;
-  k.sQt[1] = sQt1;
   k.sO[0] = sO0;
   k.sO[1] = sO1;
-  k.sOt[0] = sOt0;
-  k.sOt[1] = sOt1;
   k.sR[0] = sR0;
   k.sR[1] = sR1;
   k.g = a.geo;
@@ -317,14 +302,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   k.ldQ.init(a.sq.n, w, lane);
   k.ldO.init(a.sdo.n, w, lane);
   if constexpr (K::kHalf) {
-    k.Qtb = (const T*)a.qt + (int64_t)bh * kHeadDim * a.Np;
-    k.Otb = (const T*)a.dot + (int64_t)bh * kHeadDim * a.Np;
-    k.ldT.init(a.Np, w, lane);
+    k.tr.init(lane);
     const int sg = sigma<T>(l32);
 #pragma unroll
     for (int ks = 0; ks < K::NSD; ++ks) k.rofs[ks] = dt_off<T>(sg, K::KS * ks + K::E * hl);
-#pragma unroll
-    for (int c4 = 0; c4 < 2 * K::KPS; ++c4) k.tofs[c4] = dt_off<T>(l32, K::KS * c4 + K::E * hl);
   }
   k.seed_stride = (int64_t)a.B * a.H * a.Np;
   k.seeds = a.kseed + (int64_t)bh * a.Np;

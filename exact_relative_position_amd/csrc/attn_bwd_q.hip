@@ -10,8 +10,9 @@
 // saturated rows collect into two on-chip sums per query.
 //
 // One workgroup = one (batch, head, 128-query block); 4 waves x 32 queries;
-// per 64-key tile K, K^T (from a key-contiguous copy) and V are loaded
-// straight into LDS; the key loop runs in three segments like the forward.
+// per 64-key tile the K and V rows are loaded straight into LDS (K^T, the
+// operand of dQ = dS K, through transpose reads); the key loop runs in three
+// segments like the forward.
 #include "qside.hpp"
 
 namespace relpos {
@@ -31,7 +32,6 @@ struct BwdQ {
   // LDS buffers, two of each (separate arrays, so that the compiler can tell
   // the asynchronous loads into one buffer from the reads of the other)
   char* sK[2];     // K rows
-  char* sKt[2];    // K^T (16-bit) -- unused for fp32 (K read transposed)
   char* sV[2];     // V rows
   float* sZK[2];   // saturated Z^K scalars [2][kTile]
 
@@ -41,14 +41,15 @@ struct BwdQ {
   float cst_lo, cst_hi, sc2, tau, lse2, Dl;
   bool need_dz;
   const T* Kb;
-  const T* Ktb;
   const T* Vb;
   int64_t sk, sv, Np;
-  DLoader<T> ldK, ldKt, ldV;
+  DLoader<T> ldK, ldV;
   // per-lane LDS byte offsets of the 16-bit operand fragments (buffer 0):
-  // K / V row sigma(l32) at k-step ks; K^T row l32 at key chunk column c4
+  // K / V row sigma(l32) at k-step ks
   int kofs[kHalf ? NSD : 1];
-  int tofs[kHalf ? 2 * KPS : 1];
+  // K^T (contracted over the keys in dQ = dS K) comes from the K row tile
+  // through transpose reads
+  TrReader<std::conditional_t<kHalf, T, _Float16>> tr;
   frag qf[NSD], df[NSD];
   f32x16 dq[2];
   float acc_lo, acc_hi;
@@ -58,7 +59,6 @@ struct BwdQ {
   __device__ __forceinline__ void issue(int t) {
     const int j0 = t * kTile;
     ldK.load(sK[BUF], Kb + (int64_t)j0 * sk, N - j0, lane);
-    if constexpr (kHalf) ldKt.load(sKt[BUF], Ktb + j0, 64, lane);
     ldV.load(sV[BUF], Vb + (int64_t)j0 * sv, N - j0, lane);
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
@@ -77,7 +77,6 @@ struct BwdQ {
     // used for tiles that need no mask anywhere in the block)
     const bool needmask = BAND && ((j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0));
     const char* tK = sK[BUF];
-    const char* tKt = kHalf ? sKt[BUF] : tK;
     const char* tV = sV[BUF];
     const float* zk = sZK[BUF];
     const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
@@ -133,8 +132,7 @@ struct BwdQ {
         for (int kk = 0; kk < KPS; ++kk) {
           frag kf;
           if constexpr (kHalf) {
-            kf = *reinterpret_cast<const frag*>(tKt + tofs[KPS * st + kk] +
-                                                dt * 32 * DTile<T>::ROWB);
+            kf = tr.read(tK, dt, KPS * st + kk);
           } else {
             kf = dfrag_t32(tK, 32 * dt + l32, KS * (KPS * st + kk) + E * hl);
           }
@@ -177,14 +175,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   using B = BwdQ<T>;
   constexpr int TB = DTile<T>::BYTES;
   __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
-  __shared__ __align__(16) char sKt0[B::kHalf ? TB : 16], sKt1[B::kHalf ? TB : 16];
   __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
 
   B q;
   q.sK[0] = sK0;
   q.sK[1] = sK1;
-  q.sKt[0] = sKt0;
-  q.sKt[1] = sKt1;
   q.sV[0] = sV0;
   q.sV[1] = sV1;
   q.sZK[0] = sZK0;
@@ -224,13 +219,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   q.ldK.init(a.sk.n, w, lane);
   q.ldV.init(a.sv.n, w, lane);
   if constexpr (B::kHalf) {
-    q.Ktb = (const T*)a.kt + (int64_t)bh * kHeadDim * a.Np;
-    q.ldKt.init(a.Np, w, lane);
+    q.tr.init(lane);
     const int sig = sigma<T>(l32);
 #pragma unroll
     for (int ks = 0; ks < B::NSD; ++ks) q.kofs[ks] = dt_off<T>(sig, B::KS * ks + B::E * hl);
-#pragma unroll
-    for (int c4 = 0; c4 < 2 * B::KPS; ++c4) q.tofs[c4] = dt_off<T>(l32, B::KS * c4 + B::E * hl);
   }
 
   QCtx& c = q.c;

@@ -7,11 +7,11 @@
 // the three-segment key loop.
 //
 // One workgroup = one (batch, head, 128-query block); 4 waves x 32 queries.
-// Per 64-key tile: K and V^T (read from a key-contiguous copy of V) go from
-// HBM straight into LDS with global_load_lds_dwordx4 (no staging registers),
-// double buffered; S^T = K Q^T and O^T += V^T P^T run on
-// v_mfma_f32_32x32x16_{f16,bf16} (32x32x2_f32 for fp32 inputs, whose V tile
-// is read transposed from its row-major copy).
+// Per 64-key tile: the K and V rows go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no staging registers), double buffered;
+// S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_{f16,bf16}
+// (32x32x2_f32 for fp32 inputs).  The V^T operand is read from the V row
+// tile with ds_read_b64_tr_b16 transpose reads (fp32: element reads).
 //
 // Three-segment key loop: two comparisons per tile against the thresholds
 // split the block's key tiles into a left-saturated run, a band run and a
@@ -43,7 +43,7 @@ struct Fwd {
   // LDS buffers, two of each (separate arrays, so that the compiler can tell
   // the asynchronous loads into one buffer from the reads of the other)
   char* sK[2];    // K tile
-  char* sV[2];    // V^T (16-bit) or V (fp32) tile
+  char* sV[2];    // V tile
   float* sZK[2];  // saturated Z^K scalars of the tile's keys [2][kTile]
 
   Geo g;
@@ -51,13 +51,15 @@ struct Fwd {
   int tid, w, lane, hl, l32, i0, iw0, nkt, N;
   float cst_lo, cst_hi, sc2;
   const T* Kb;   // K of this (b, h)
-  const T* Vb;   // V^T copy (16-bit, row stride Np) or V (fp32)
-  int64_t sk, Np;
+  const T* Vb;   // V of this (b, h)
+  int64_t sk, sv;
   DLoader<T> ldK, ldV;
   // per-lane LDS byte offsets of the 16-bit operand fragments (buffer 0):
-  // K row sigma(l32) at k-step ks; V^T row l32 at key chunk column c4
+  // K row sigma(l32) at k-step ks
   int kofs[kHalf ? NSD : 1];
-  int vofs[kHalf ? 2 * KPS : 1];
+  // V^T (contracted over the keys in P V) comes from the V row tile through
+  // transpose reads
+  TrReader<std::conditional_t<kHalf, T, _Float16>> tr;
   frag qf[NSD];
   f32x16 oacc[2];
   float m_used, lsum;
@@ -67,11 +69,7 @@ struct Fwd {
   __device__ __forceinline__ void issue(int t) {
     const int j0 = t * kTile;
     ldK.load(sK[BUF], Kb + (int64_t)j0 * sk, N - j0, lane);
-    if constexpr (kHalf) {
-      ldV.load(sV[BUF], Vb + j0, 64, lane);
-    } else {
-      ldV.load(sV[BUF], Vb + (int64_t)j0 * Np, N - j0, lane);
-    }
+    ldV.load(sV[BUF], Vb + (int64_t)j0 * sv, N - j0, lane);
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
       dword_direct((char*)(sZK[BUF] + w * kTile), p, p != nullptr, lane);
@@ -81,7 +79,7 @@ struct Fwd {
   // V^T fragment (rows d = 32 dt + l32, keys of chunk column c4) of P V.
   __device__ __forceinline__ frag vfrag(const char* tV, int dt, int c4) const {
     if constexpr (kHalf) {
-      return *reinterpret_cast<const frag*>(tV + vofs[c4] + dt * 32 * DTile<T>::ROWB);
+      return tr.read(tV, dt, c4);
     } else {
       return dfrag_t32(tV, 32 * dt + l32, KS * c4 + E * hl);
     }
@@ -250,24 +248,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnArgs a) {
   const T* Qp = (const T*)a.q + bb * a.sq.b + hh * a.sq.h;
   f.Kb = (const T*)a.k + bb * a.sk.b + hh * a.sk.h;
   f.sk = a.sk.n;
-  f.Np = a.Np;
-  if constexpr (Fwd<T>::kHalf) {
-    f.Vb = (const T*)a.vt + (int64_t)bh * kHeadDim * a.Np;
-    f.ldV.init(a.Np, w, lane);
-  } else {
-    f.Vb = (const T*)a.v + bb * a.sv.b + hh * a.sv.h;
-    f.Np = a.sv.n;
-    f.ldV.init(a.sv.n, w, lane);
-  }
+  f.Vb = (const T*)a.v + bb * a.sv.b + hh * a.sv.h;
+  f.sv = a.sv.n;
+  f.ldV.init(a.sv.n, w, lane);
   f.ldK.init(a.sk.n, w, lane);
   if constexpr (Fwd<T>::kHalf) {
     const int sig = sigma<T>(l32);
 #pragma unroll
     for (int ks = 0; ks < Fwd<T>::NSD; ++ks)
       f.kofs[ks] = dt_off<T>(sig, Fwd<T>::KS * ks + Fwd<T>::E * hl);
-#pragma unroll
-    for (int c4 = 0; c4 < 2 * Fwd<T>::KPS; ++c4)
-      f.vofs[c4] = dt_off<T>(l32, Fwd<T>::KS * c4 + Fwd<T>::E * hl);
+    f.tr.init(lane);
   }
 
   QCtx& c = f.c;

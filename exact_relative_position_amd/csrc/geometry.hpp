@@ -123,10 +123,6 @@ struct AttnArgs {
   const float* L2; // [B*H][Np] padded log2-domain LSE (backward)
   const float* D;  // [B*H][Np] padded row terms (backward)
   const float* kseed;  // [4][B*H][Np] per-query seeds of the key pass (RowTermArgs)
-  const void* vt;  // [B*H][64][Np] token-contiguous copies (16-bit types)
-  const void* kt;
-  const void* qt;
-  const void* dot;
   int Np;          // N rounded up to 64
   const float* zq; // [B*H][N][W] or null
   const float* zk;
@@ -145,13 +141,6 @@ struct AttnArgs {
   float scale2;    // tau * log2(e)
   int flags;
   int nblk;        // blocks per (b, h) along the parallel dimension
-};
-
-struct TransposeArgs {   // X [B, H, N, 64] -> Xt [B*H][64][Np], zero beyond N
-  const void* x;
-  Str sx;
-  void* xt;
-  int B, H, N, Np;
 };
 
 struct RowTermArgs {     // padded backward row terms

@@ -1,10 +1,5 @@
-// prep.hip -- operand layouts and row terms prepared once per pass.
+// prep.hip -- per-query row terms prepared once per backward.
 //
-//  * transpose_kernel: X [B, H, N, 64] -> Xt [B*H][64][Np], Np = N rounded up
-//    to 64, zero beyond N.  The attention kernels contract over the token
-//    index in P V (forward), dS K (query pass), dO^T P and Q^T dS (key pass);
-//    an MFMA operand needs its contraction index contiguous in a lane, so
-//    those operands are read from a token-contiguous copy (16-bit types).
 //  * rowterm_kernel: the backward's per-query terms, padded to Np:
 //    L2[i] = LSE_i * log2(e) (+inf for a row whose keys are all masked, and
 //    for padding, so that P = exp2(s - L2) = 0 there) and
@@ -18,40 +13,6 @@
 #include "qside.hpp"
 
 namespace relpos {
-
-// One block: 64 tokens x 64 dims of one (b, h), through LDS.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeArgs a) {
-  __shared__ T tile[64][64 + 2];
-  const int nt = a.Np / 64;
-  const int bh = blockIdx.x / nt, jt = blockIdx.x - bh * nt;
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int j0 = jt * 64;
-  const T* x = (const T*)a.x + b * a.sx.b + h * a.sx.h;
-  const int tid = threadIdx.x;
-  // 64 rows x 8 chunks of 8 elements
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + kThreads * u;
-    const int r = c >> 3, col = (c & 7) * 8;
-    const int j = j0 + r;
-    typename MT<T>::frag v = MT<T>::zero();
-    if (j < a.N) v = *reinterpret_cast<const typename MT<T>::frag*>(x + (int64_t)j * a.sx.n + col);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[r][col + e] = v[e];
-  }
-  __syncthreads();
-  T* xt = (T*)a.xt + (int64_t)bh * 64 * a.Np + j0;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + kThreads * u;
-    const int d = c >> 3, k0 = (c & 7) * 8;
-    typename MT<T>::frag v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[k0 + e][d];
-    *reinterpret_cast<typename MT<T>::frag*>(xt + (int64_t)d * a.Np + k0) = v;
-  }
-}
 
 // 8 lanes per row; rows over B*H*Np.
 template <typename T>
@@ -99,17 +60,6 @@ __global__ __launch_bounds__(kThreads) void rowterm_kernel(RowTermArgs a) {
     a.kseed[2 * rows + row] = base;
     a.kseed[3 * rows + row] = -acc;
   }
-}
-
-hipError_t launch_transpose(int dtype, const TransposeArgs& a, hipStream_t st) {
-  const int blocks = a.B * a.H * (a.Np / 64);
-  if (blocks <= 0) return hipSuccess;
-  switch (dtype) {
-    case 1: hipLaunchKernelGGL(transpose_kernel<_Float16>, dim3(blocks), dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(transpose_kernel<__bf16>, dim3(blocks), dim3(kThreads), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_rowterm(int dtype, const RowTermArgs& a, hipStream_t st) {

@@ -13,6 +13,8 @@
 //  * col map: 64 consecutive lanes cover 64 rows at one column chunk, which
 //    makes the 2-byte transposed LDS writes hit 32 distinct banks.
 #pragma once
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace relpos {
@@ -213,6 +215,42 @@ __device__ __forceinline__ typename MT<T>::frag dfrag(const char* lds, int row, 
 __device__ __forceinline__ float dfrag_t32(const char* lds, int row, int col) {
   return *reinterpret_cast<const float*>(lds + dt_off<float>(col, row));
 }
+
+// Transposed MFMA operand read straight from a row-major 16-bit direct tile
+// with ds_read_b64_tr_b16 (gfx950).  That instruction works on groups of 16
+// lanes: input lane i of a group supplies 4 consecutive elements x_i[0..3]
+// from its address, and output lane m receives x_{m/4 + 4j}[m % 4] for
+// j = 0..3.  If input lane i reads tile row R + i/4 at columns C + 4 (i % 4)
+// .. + 3, output lane m therefore holds column C + m of rows R .. R + 3.
+// Two such reads (rows +0..3 and +4..7) give the 8 k-values of a 32x32x16
+// operand fragment: lane l holds tile column 32 dt + (l % 32) (the MFMA free
+// index) and tile rows 16 c + 8 (l / 32) + 0..7 (its k-values of k-step c).
+template <typename T>
+struct TrReader {
+  static_assert(sizeof(T) == 2, "transpose reads are for 16-bit tiles");
+  using frag = typename MT<T>::frag;
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  int o[2][2];  // byte offset of read r for column block dt, k-step 0
+  __device__ __forceinline__ void init(int lane) {
+    const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+        o[r][dt] = dt_off<T>(8 * h + 4 * r + (i >> 2), 32 * dt + 16 * (grp & 1) + 4 * (i & 3));
+  }
+  // operand for column block dt and k-step c (tile rows 16 c .. 16 c + 15)
+  __device__ __forceinline__ frag read(const char* lds, int dt, int c) const {
+    const s4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4*)(lds + o[0][dt] + c * 16 * DTile<T>::ROWB));
+    const s4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4*)(lds + o[1][dt] + c * 16 * DTile<T>::ROWB));
+    typedef short s8 __attribute__((ext_vector_type(8)));
+    const s8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(frag, v);
+  }
+};
 
 // One 4-byte value per lane, written to lds + 4 * lane (when valid, else 0).
 __device__ __forceinline__ void dword_direct(char* lds, const float* src, bool valid, int lane) {
