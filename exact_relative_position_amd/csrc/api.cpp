@@ -31,7 +31,9 @@ hipError_t launch_phi_fold(const PhiArgs& p, int32_t* fold, int32_t* ub, int32_t
 hipError_t launch_bias_unfold(int dtype, const BiasArgs& a, hipStream_t st);
 hipError_t launch_proj(int dtype, const ProjArgs& a, hipStream_t st);
 hipError_t launch_rows(int dtype, const RowsArgs& a, hipStream_t st);
+hipError_t launch_tab_unfold(int dtype, const TabUnfoldArgs& a, hipStream_t st);
 hipError_t launch_cols(int dtype, const ColsArgs& a, int Ho, hipStream_t st);
+hipError_t launch_cols1(int dtype, const ColsArgs& a, int Ho, hipStream_t st);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t st);
 }  // namespace relpos
 
@@ -163,6 +165,7 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   pl.geo.W = (int)std::min<int64_t>(pl.Runf, (int64_t)pl.N + kGroup - 1);
   pl.geo.causal = (mask->flags & RELPOS_MASK_CAUSAL) ? 1 : 0;
   if (pl.geo.W < 1) pl.geo.W = 1;
+  pl.geo.Wp = (pl.geo.W + 31) / 32 * 32;
   pl.phi.kind = phi->kind;
   pl.phi.N = pl.N;
   pl.phi.lo_unf = (int)lo;
@@ -180,13 +183,13 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
     return fail(RELPOS_ERR_INVALID_ARG, "negative table head stride");
   if ((pl.has_aq && (pl.aq_hs * pl.esz) % 16) || (pl.has_ak && (pl.ak_hs * pl.esz) % 16))
     return fail(RELPOS_ERR_INVALID_ARG, "table head stride must be a multiple of 16 bytes");
-  if ((size_t)pl.B * pl.H * pl.N * (size_t)pl.geo.W > (size_t)1 << 40)
+  if ((size_t)pl.B * pl.H * pl.N * (size_t)pl.geo.Wp > (size_t)1 << 40)
     return fail(RELPOS_ERR_UNSUPPORTED, "projection window too large");
   pl.ho_aq = pl.aq_hs == 0 ? 1 : pl.H;
   pl.ho_ak = pl.ak_hs == 0 ? 1 : pl.H;
   pl.ho_b = pl.b_hs == 0 ? 1 : pl.H;
   pl.nblk = (pl.N + kBlockRows - 1) / kBlockRows;
-  pl.z_elems = (size_t)pl.B * pl.H * pl.N * pl.geo.W;
+  pl.z_elems = (size_t)pl.B * pl.H * pl.N * pl.geo.Wp;
   // column tiles of the projection (max over groups)
   for (int grp = 0; grp < pl.nblk; ++grp) {
     int cb, ce;
@@ -196,11 +199,12 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
     pl.ncol_k = std::max(pl.ncol_k, (ce - cb + 63) / 64);
     if (!grouped(pl.geo)) break;
   }
-  pl.rtiles = (pl.Runf + 31) / 32;
-  pl.Rpad = pl.rtiles * 32;
+  pl.Rpad = (pl.Runf + 63) / 64 * 64;  // 64-row tiles of the column contraction
+  pl.rtiles = pl.Rpad / 32;
   auto splits = [&](int ho, bool shared) {
     const int64_t rows = (int64_t)(shared ? pl.B * pl.H : pl.B) * pl.N;
-    int64_t want = (1024 + (int64_t)pl.rtiles * ho - 1) / std::max<int64_t>(1, (int64_t)pl.rtiles * ho);
+    const int64_t tiles = (int64_t)(pl.Rpad / 64) * ho;
+    int64_t want = (1024 + tiles - 1) / std::max<int64_t>(1, tiles);
     int64_t cap = std::max<int64_t>(1, rows / 512);
     return (int)std::max<int64_t>(1, std::min(want, cap));
   };
@@ -262,6 +266,8 @@ struct WsBwd {
   float* L2 = nullptr;  // [B*H][Np]
   float* D = nullptr;   // [B*H][Np]
   float* kseed = nullptr;  // [4][B*H][Np]
+  float* tunf_q = nullptr;  // [ho][Runf + 32][64] fp32 unfolded tables
+  float* tunf_k = nullptr;
   float* dq_part = nullptr;
   float* dk_part = nullptr;
   float* dzq = nullptr;
@@ -301,6 +307,9 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
   w.L2 = c.take<float>(sizeof(float) * bhnp);
   w.D = c.take<float>(sizeof(float) * bhnp);
   w.kseed = c.take<float>(sizeof(float) * 4 * bhnp);
+  const size_t tu = (size_t)(pl.Runf + 32) * kHeadDim;
+  if (pl.has_aq) w.tunf_q = c.take<float>(sizeof(float) * pl.ho_aq * tu);
+  if (pl.has_ak) w.tunf_k = c.take<float>(sizeof(float) * pl.ho_ak * tu);
   if (pl.has_aq) w.dq_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_ak) w.dk_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_aq || pl.has_b) w.dzq = c.take<float>(sizeof(float) * pl.z_elems);
@@ -330,6 +339,14 @@ int terms_of(const void* aQ, const void* aK, const void* b) {
 }
 
 // Map tables needed by both passes: T5 fold table (+ ranges), unfolded bias.
+// Column contraction: a single-group window of a 16-bit problem streams its
+// dZ rows through the 64-row tiled kernel; grouped windows (a different
+// window per 128-row group) use the general kernel.
+hipError_t cols(const Plan& pl, const ColsArgs& c, int Ho, hipStream_t st) {
+  if (pl.esz == 2 && !grouped(pl.geo)) return launch_cols1(pl.dtype, c, Ho, st);
+  return launch_cols(pl.dtype, c, Ho, st);
+}
+
 relpos_status prepare_tables(const Plan& pl, const void* b, int32_t* fold, int32_t* ub,
                              int32_t* ue, float* bunf, hipStream_t st) {
   if (pl.t5) {
@@ -664,13 +681,20 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   if (!(stages & RELPOS_BWD_CONTRACT)) return RELPOS_OK;
 
   // dQ += dZ^Q aQ, dK += dZ^K aK
+  const int64_t tu_hs = (int64_t)(pl.Runf + 32) * kHeadDim;
   if (pl.has_aq) {
-    RowsArgs r{w.dq_part, w.dzq, aQ, pl.aq_hs, pl.t5 ? w.fold : nullptr, dQ,
+    TabUnfoldArgs t{aQ, pl.aq_hs, pl.t5 ? w.fold : nullptr, w.tunf_q, pl.ho_aq, pl.Runf};
+    if ((s = hip_check(launch_tab_unfold(pl.dtype, t, st), "table unfold aQ")) != RELPOS_OK)
+      return s;
+    RowsArgs r{w.dq_part, w.dzq, w.tunf_q, pl.aq_hs == 0 ? 0 : tu_hs, dQ,
                str_of(prob, RELPOS_T_DQ), pl.B, pl.H, pl.geo, 0, pl.nblk};
     if ((s = hip_check(launch_rows(pl.dtype, r, st), "contraction dQ")) != RELPOS_OK) return s;
   }
   if (pl.has_ak) {
-    RowsArgs r{w.dk_part, w.dzk, aK, pl.ak_hs, pl.t5 ? w.fold : nullptr, dK,
+    TabUnfoldArgs t{aK, pl.ak_hs, pl.t5 ? w.fold : nullptr, w.tunf_k, pl.ho_ak, pl.Runf};
+    if ((s = hip_check(launch_tab_unfold(pl.dtype, t, st), "table unfold aK")) != RELPOS_OK)
+      return s;
+    RowsArgs r{w.dk_part, w.dzk, w.tunf_k, pl.ak_hs == 0 ? 0 : tu_hs, dK,
                str_of(prob, RELPOS_T_DK), pl.B, pl.H, pl.geo, 1, pl.nblk};
     if ((s = hip_check(launch_rows(pl.dtype, r, st), "contraction dK")) != RELPOS_OK) return s;
   }
@@ -694,7 +718,7 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     c.rtiles = pl.rtiles;
     c.Rpad = pl.Rpad;
     c.want_x = 1;
-    if ((s = hip_check(launch_cols(pl.dtype, c, pl.ho_aq, st), "contraction daQ")) != RELPOS_OK)
+    if ((s = hip_check(cols(pl, c, pl.ho_aq, st), "contraction daQ")) != RELPOS_OK)
       return s;
     FoldArgs f{w.part_q, joint_b ? w.part_qb : nullptr, ub, ue, daQ, joint_b ? db : nullptr,
                pl.ho_aq, pl.R, pl.Rpad, pl.split_q};
@@ -716,7 +740,7 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     c.rtiles = pl.rtiles;
     c.Rpad = pl.Rpad;
     c.want_x = 0;
-    if ((s = hip_check(launch_cols(pl.dtype, c, pl.ho_b, st), "contraction db")) != RELPOS_OK)
+    if ((s = hip_check(cols(pl, c, pl.ho_b, st), "contraction db")) != RELPOS_OK)
       return s;
     FoldArgs f{nullptr, w.part_qb, ub, ue, nullptr, db, pl.ho_b, pl.R, pl.Rpad, pl.split_b};
     if ((s = hip_check(launch_fold(f, st), "fold db")) != RELPOS_OK) return s;
@@ -737,7 +761,7 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     c.rtiles = pl.rtiles;
     c.Rpad = pl.Rpad;
     c.want_x = 1;
-    if ((s = hip_check(launch_cols(pl.dtype, c, pl.ho_ak, st), "contraction daK")) != RELPOS_OK)
+    if ((s = hip_check(cols(pl, c, pl.ho_ak, st), "contraction daK")) != RELPOS_OK)
       return s;
     FoldArgs f{w.part_k, nullptr, ub, ue, daK, nullptr, pl.ho_ak, pl.R, pl.Rpad, pl.split_k};
     if ((s = hip_check(launch_fold(f, st), "fold daK")) != RELPOS_OK) return s;

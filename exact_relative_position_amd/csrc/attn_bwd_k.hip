@@ -105,7 +105,7 @@ struct BwdK {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int i = imin(ib + kap0<T>(e), N - 1);
-        v[e] += zq_bh[(int64_t)i * g.W + imin(imax(jk - i - g.lo - wq, 0), Wm)];
+        v[e] += zq_bh[(int64_t)i * g.Wp + imin(imax(jk - i - g.lo - wq, 0), Wm)];
       }
     }
     if (has_zk) {
@@ -309,11 +309,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   }
   k.seed_stride = (int64_t)a.B * a.H * a.Np;
   k.seeds = a.kseed + (int64_t)bh * a.Np;
-  k.zq_bh = k.has_zq ? a.zq + (int64_t)bh * N * g.W : nullptr;
+  k.zq_bh = k.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr;
   k.bun = k.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   k.wsk = win_k(g, kb);
-  k.zk_row = k.has_zk ? a.zk + ((int64_t)bh * N + imin(jk, N - 1)) * g.W : nullptr;
-  k.dz_row = k.has_zk ? a.dzk + ((int64_t)bh * N + jk) * g.W : nullptr;
+  k.zk_row = k.has_zk ? a.zk + ((int64_t)bh * N + imin(jk, N - 1)) * g.Wp : nullptr;
+  k.dz_row = k.has_zk ? a.dzk + ((int64_t)bh * N + jk) * g.Wp : nullptr;
   k.sc2 = a.scale2;
   k.tau = a.tau;
 

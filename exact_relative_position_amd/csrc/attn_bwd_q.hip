@@ -234,8 +234,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   c.has_zk = ZK;
   c.has_b = a.flags & F_B;
   c.wsq = win_q(g, qb);
-  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.W : nullptr;
-  c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.W : nullptr;
+  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.Wp : nullptr;
+  c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   q.need_dz = a.flags & F_ZQ_NEEDED;
   qside_consts(g, c, qb, q.cst_lo, q.cst_hi);
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
     q.lse2 = a.L2[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
     q.Dl = a.D[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
   }
-  q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.W : nullptr;
+  q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
   q.dq[0] = zero16();
   q.dq[1] = zero16();
   q.acc_lo = 0.f;

@@ -269,8 +269,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnArgs a) {
   c.has_zk = ZK;
   c.has_b = a.flags & F_B;
   c.wsq = win_q(g, qb);
-  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.W : nullptr;
-  c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.W : nullptr;
+  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.Wp : nullptr;
+  c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
   f.sc2 = a.scale2;

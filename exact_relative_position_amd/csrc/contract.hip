@@ -10,7 +10,8 @@
 //
 // All three kernels use v_mfma_f32_32x32x2_f32 on fp32 data and fixed
 // summation orders (no atomics):
-//  * rows_kernel:  dX[i] = dX_part[i] + sum_c dZ[i][c] tab[fold(ws + c)]
+//  * rows_kernel:  dX[i] = dX_part[i] + sum_c dZ[i][c] tab[fold(ws + c)], with
+//                  the table unfolded to fp32 first (tab_unfold_kernel)
 //  * cols_kernel:  part[s][h][u] = sum over the rows i of split s of dZ[i][u - ws(i)] x_i
 //                  (and the column sums for db), window-aware;
 //  * fold_kernel:  out[h][k] = sum over splits and over the unfolded rows u of k.
@@ -23,84 +24,134 @@ __device__ inline f32x16 mma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// One block: 128 rows of one (b, h) (one group); 4 waves x 32 rows x 64 d.
+// Row contraction, one block = 128 rows of one (b, h) (one group), 4 waves x
+// 32 rows x 64 d, over the group's live window columns [cb, ce) in chunks of
+// 32 columns aligned to 128 bytes.  Each chunk of dZ (128 rows x 32 floats)
+// and the matching 32 rows of the fp32 unfolded table go straight from HBM
+// into LDS with global_load_lds_dwordx4, double buffered, so the next chunk
+// streams in while the MFMAs run.  Inside an LDS row of dZ the 16-byte
+// chunks are XOR-permuted with (row / 2) % 8, which keeps the operand reads
+// of 32 rows at one column at most two-way on a bank.  Columns of an edge
+// chunk outside [cb, ce) are never written by the backward passes; they are
+// read but replaced by zero before the MFMA.
+constexpr int kRC = 32;  // columns per chunk
+
+template <typename T>
+struct RowsK {
+  const float* dzb;   // dZ of this (b, h), row stride Wp
+  const float* tub;   // unfolded fp32 table of this head, [Runf + 32][64]
+  int N, Wp, i0, ws, cb, ce, w, lane, hl, l32;
+
+  __device__ static int zswz(int r) { return (r >> 1) & 7; }
+
+  // dZ rows [i0, i0 + 128) x columns [c0, c0 + 32) and the table rows
+  // ws + c0 .. + 31 into (zb, tb), asynchronously
+  __device__ __forceinline__ void issue(float* zb, float* tb, int c0) const {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 4 * w + u;  // 8 rows per instruction
+      const int r = 8 * j + (lane >> 3);
+      const int lc = (lane & 7) ^ zswz(r);
+      float* dst = zb + 256 * j;
+      if (i0 + r < N) {
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + c0 + 4 * lc),
+                                         (lds_void_t*)dst, 16, 0, 0);
+      } else {
+        *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * w + u;  // 4 table rows per instruction
+      const int r = 4 * j + (lane >> 4);
+      __builtin_amdgcn_global_load_lds(
+          (glb_void_t*)(tub + (int64_t)(ws + c0 + r) * kHeadDim + 4 * (lane & 15)),
+          (lds_void_t*)(tb + 256 * j), 16, 0, 0);
+    }
+  }
+  // acc += dZ chunk (this wave's 32 rows) x table chunk
+  template <bool EDGE>
+  __device__ __forceinline__ void mma_chunk(const float* zb, const float* tb, int c0,
+                                            f32x16 (&acc)[2]) const {
+    const int r = 32 * w + l32;
+    const float* zr = zb + 32 * r;
+    const int sw = zswz(r);
+#pragma unroll
+    for (int ks = 0; ks < kRC / 2; ++ks) {
+      const int c = 2 * ks + hl;
+      float av = zr[4 * ((c >> 2) ^ sw) + (c & 3)];
+      if (EDGE) av = (c0 + c >= cb && c0 + c < ce) ? av : 0.f;
+      const float* trow = tb + c * kHeadDim + l32;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[nt] = mma32(av, trow[32 * nt], acc[nt]);
+    }
+  }
+  __device__ __forceinline__ void chunk(const float* zb, const float* tb, int c0,
+                                        f32x16 (&acc)[2]) const {
+    if (c0 < cb || c0 + kRC > ce)
+      mma_chunk<true>(zb, tb, c0, acc);
+    else
+      mma_chunk<false>(zb, tb, c0, acc);
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
-  constexpr int P = 65;
-  __shared__ float sZ[kBlockRows * P];
-  __shared__ float sT[64 * P];
+  __shared__ __align__(16) float sZ0[128 * kRC], sZ1[128 * kRC];
+  __shared__ __align__(16) float sT0[kRC * kHeadDim], sT1[kRC * kHeadDim];
   const Geo g = a.geo;
   const int N = g.N;
   const int total = a.B * a.H * a.nblk;
   const int lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / a.nblk, rb = lid - bh * a.nblk;
   const int bb = bh / a.H, hh = bh - bb * a.H;
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int i0 = rb * kBlockRows;
-  int cb, ce, ws;
+  const int tid = threadIdx.x;
+  RowsK<T> k;
+  k.w = wave_id();
+  k.lane = tid & 63;
+  k.hl = k.lane >> 5;
+  k.l32 = k.lane & 31;
+  k.N = N;
+  k.Wp = g.Wp;
+  k.i0 = rb * kBlockRows;
   if (a.key_side) {
-    cols_k(g, rb, cb, ce);
-    ws = win_k(g, rb);
+    cols_k(g, rb, k.cb, k.ce);
+    k.ws = win_k(g, rb);
   } else {
-    cols_q(g, rb, cb, ce);
-    ws = win_q(g, rb);
+    cols_q(g, rb, k.cb, k.ce);
+    k.ws = win_q(g, rb);
   }
-  const float* dzb = a.dz + (int64_t)bh * N * g.W;
-  const T* tab = (const T*)a.tab + hh * a.tab_hs;
+  k.dzb = a.dz + (int64_t)bh * N * g.Wp;
+  k.tub = a.tunf + hh * a.tunf_hs;
+  const int w = k.w, hl = k.hl, l32 = k.l32;
 
   f32x16 acc[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int i = i0 + 32 * w + res_row(hl, e);
+      const int i = k.i0 + 32 * w + res_row(hl, e);
       acc[nt][e] = i < N ? a.part[((int64_t)bh * N + i) * kHeadDim + 32 * nt + l32] : 0.f;
     }
 
-  for (int c0 = cb; c0 < ce; c0 += 64) {
-    // stage dZ[i0 .. i0+127][c0 .. c0+63] and the 64 table rows (as fp32);
-    // all loads of a thread are issued before its LDS stores
-    {
-      float zv[32];
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int idx = tid + kThreads * u;
-        const int r = idx >> 6, cc = idx & 63;
-        const int i = i0 + r, col = c0 + cc;
-        zv[u] = (i < N && col < ce) ? dzb[(int64_t)i * g.W + col] : 0.f;
-      }
-      float tv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int idx = tid + kThreads * u;
-        const int cc = idx >> 6, d = idx & 63;
-        const int col = c0 + cc;
-        float v = 0.f;
-        if (col < ce) {
-          const int uu = ws + col;
-          const int r = a.fold ? a.fold[uu] : uu;
-          v = MT<T>::to_f(tab[(int64_t)r * kHeadDim + d]);
-        }
-        tv[u] = v;
-      }
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int idx = tid + kThreads * u;
-        sZ[(idx >> 6) * P + (idx & 63)] = zv[u];
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int idx = tid + kThreads * u;
-        sT[(idx >> 6) * P + (idx & 63)] = tv[u];
-      }
-    }
+  // chunks c0 = cb0, cb0 + 32, ... (cb0 = cb rounded down to 32); chunk n
+  // sits in buffer n & 1
+  const int cb0 = k.cb & ~(kRC - 1);
+  const int nch = k.ce > k.cb ? (k.ce - cb0 + kRC - 1) / kRC : 0;
+  if (nch > 0) k.issue(sZ0, sT0, cb0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  for (int n = 0; n < nch; n += 2) {
+    const int c0 = cb0 + n * kRC;
+    const bool more1 = n + 1 < nch;
+    if (more1) k.issue(sZ1, sT1, c0 + kRC);
+    k.chunk(sZ0, sT0, c0, acc);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-#pragma unroll 4
-    for (int ks = 0; ks < 32; ++ks) {
-      const float av = sZ[(32 * w + l32) * P + 2 * ks + hl];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[nt] = mma32(av, sT[(2 * ks + hl) * P + 32 * nt + l32], acc[nt]);
-    }
+    if (!more1) break;
+    if (n + 2 < nch) k.issue(sZ0, sT0, c0 + 2 * kRC);
+    k.chunk(sZ1, sT1, c0 + kRC, acc);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
@@ -109,9 +160,187 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int i = i0 + 32 * w + res_row(hl, e);
+      const int i = k.i0 + 32 * w + res_row(hl, e);
       if (i < N) ob[(int64_t)i * a.sout.n + 32 * nt + l32] = MT<T>::from_f(acc[nt][e]);
     }
+}
+
+// Column contraction for a single-group window (every row's window starts
+// at unfolded row 0, so column u of every dZ row is unfolded row u).
+// Block (ut, s, ho): unfolded rows u in [64 ut, 64 ut + 64), all 64 d, over
+// the rows of split s, in chunks of 64 rows.  Each chunk of dZ (64 rows x 64
+// floats) and of X (64 rows x 64 elements) goes straight into LDS with
+// global_load_lds_dwordx4, double buffered.  Wave w owns the output tile
+// u in 64 ut + 32 (w & 1) + [0, 32), d in 32 (w >> 1) + [0, 32); waves with
+// w >> 1 == 0 also sum the columns (db).  Columns outside the live window
+// [cb, ce) hold no gradient and are read as zero.
+constexpr int kCU = 64;  // unfolded rows per block
+
+template <typename T>
+struct ColsK {
+  const float* dz;
+  const T* x;
+  Str sx;
+  int N, Wp, H, ho, cb, ce, ut, w, lane, hl, l32;
+  bool shared;
+  int64_t f1;  // end of this split's flattened row range
+
+  // rows [f, f + nrow) of the flattened row range (one segment: b, or b*H + h
+  // for a table shared by all heads) into (zb, xb), asynchronously
+  __device__ __forceinline__ void issue(float* zb, T* xb, int64_t f, int nrow) const {
+    const int seg = (int)(f / N);
+    const int i = (int)(f - (int64_t)seg * N);
+    const int b_ = shared ? seg / H : seg;
+    const int h_ = shared ? seg % H : ho;
+    const float* dzs = dz + (int64_t)(b_ * H + h_) * N * Wp;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 4 * w + u;  // 4 rows of 64 floats per instruction
+      const int r = 4 * j + (lane >> 4);
+      const int col = kCU * ut + 4 * (lane & 15);
+      float* dst = zb + 256 * j;
+      if (r < nrow && col < Wp) {
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + col),
+                                         (lds_void_t*)dst, 16, 0, 0);
+      } else {
+        *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
+      }
+    }
+    const T* xs = x + b_ * sx.b + h_ * sx.h;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * w + u;  // 8 rows of 64 elements per instruction
+      const int r = 8 * j + (lane >> 3);
+      char* dst = reinterpret_cast<char*>(xb) + 1024 * j;
+      if (r < nrow) {
+        __builtin_amdgcn_global_load_lds(
+            (glb_void_t*)(xs + (int64_t)(i + r) * sx.n + 8 * (lane & 7)), (lds_void_t*)dst, 16,
+            0, 0);
+      } else {
+        *reinterpret_cast<Chunk*>(dst + 16 * lane) = Chunk{{0u, 0u, 0u, 0u}};
+      }
+    }
+  }
+  // rows of the chunk starting at f: up to 64, not past its segment or f1
+  __device__ __forceinline__ int chunk_rows(int64_t f) const {
+    const int64_t send = (f / N + 1) * N;
+    const int64_t e = send < f1 ? send : f1;
+    return (int)(e - f < 64 ? e - f : 64);
+  }
+};
+
+template <typename T, bool WANT_X>
+struct ColsMma {
+  // acc (this wave's 32 u x 32 d tile) and csum over the 64 rows of (zb, xb)
+  __device__ static __forceinline__ void run(const float* zb, const T* xb, int uo, int d, int hl,
+                                             bool uvalid, bool sums, f32x16& acc, float& csum) {
+#pragma unroll 8
+    for (int ks = 0; ks < 32; ++ks) {
+      const int r = 2 * ks + hl;
+      float av = zb[r * kCU + uo];
+      av = uvalid ? av : 0.f;
+      if (sums) csum += av;
+      if (WANT_X) acc = mma32(av, MT<T>::to_f(xb[r * kHeadDim + d]), acc);
+    }
+  }
+};
+
+template <typename T, bool WANT_X>
+__global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit inputs");
+  __shared__ __align__(16) float sZ0[64 * kCU], sZ1[64 * kCU];
+  __shared__ __align__(16) T sX0[64 * kHeadDim], sX1[64 * kHeadDim];
+  const Geo g = a.geo;
+  const int N = g.N;
+  const int nblk = gridDim.x * gridDim.y * gridDim.z;
+  const int lid = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), nblk);
+  const int ut = lid % gridDim.x, sp = (lid / gridDim.x) % gridDim.y;
+  const int ho = lid / (gridDim.x * gridDim.y);
+  ColsK<T> k;
+  k.w = wave_id();
+  k.lane = threadIdx.x & 63;
+  k.hl = k.lane >> 5;
+  k.l32 = k.lane & 31;
+  k.N = N;
+  k.Wp = g.Wp;
+  k.H = a.H;
+  k.ho = ho;
+  k.ut = ut;
+  k.shared = a.shared;
+  k.sx = a.sx;
+  k.dz = a.dz;
+  k.x = (const T*)a.x;
+  if (a.key_side) cols_k(g, 0, k.cb, k.ce); else cols_q(g, 0, k.cb, k.ce);
+  const int w = k.w, hl = k.hl, l32 = k.l32;
+  const int uo = 32 * (w & 1) + l32;  // this lane's unfolded row inside the block
+  const int u = kCU * ut + uo;
+  const bool uvalid = u >= k.cb && u < k.ce;
+  const bool sums = w < 2;
+  const int d = 32 * (w >> 1) + l32;
+
+  // this split's range of the flattened rows (segment-major)
+  const int nseg = a.shared ? a.B * a.H : a.B;
+  const int64_t nrows = (int64_t)nseg * N;
+  const int64_t per = (nrows + a.splits - 1) / a.splits;
+  const int64_t f0 = (int64_t)sp * per;
+  k.f1 = f0 + per < nrows ? f0 + per : nrows;
+
+  f32x16 acc = zero16();
+  float csum = 0.f;
+  // chunk n (rows [f, f + rows)) sits in buffer n & 1
+  int64_t f = f0;
+  int nrow = f < k.f1 ? k.chunk_rows(f) : 0;
+  if (nrow > 0) k.issue(sZ0, sX0, f, nrow);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  while (f < k.f1) {
+    int64_t fn = f + nrow;
+    int nrow1 = fn < k.f1 ? k.chunk_rows(fn) : 0;
+    if (nrow1 > 0) k.issue(sZ1, sX1, fn, nrow1);
+    ColsMma<T, WANT_X>::run(sZ0, sX0, uo, d, hl, uvalid, sums, acc, csum);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    f = fn;
+    nrow = nrow1;
+    if (f >= k.f1) break;
+    fn = f + nrow;
+    nrow1 = fn < k.f1 ? k.chunk_rows(fn) : 0;
+    if (nrow1 > 0) k.issue(sZ0, sX0, fn, nrow1);
+    ColsMma<T, WANT_X>::run(sZ1, sX1, uo, d, hl, uvalid, sums, acc, csum);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    f = fn;
+    nrow = nrow1;
+  }
+
+  if (WANT_X) {
+    float* outp = a.part + (((int64_t)sp * gridDim.z + ho) * a.Rpad + kCU * ut) * 64;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) outp[(32 * (w & 1) + res_row(hl, e)) * 64 + d] = acc[e];
+  }
+  if (a.partb && sums) {
+    csum = sum_xor32(csum);
+    if (hl == 0) a.partb[((int64_t)sp * gridDim.z + ho) * a.Rpad + u] = csum;
+  }
+}
+
+// Unfolded fp32 copy of a vector table: out[ho][u][:] = tab[ho][fold(u)][:]
+// for u < Runf, zero for the 32 padding rows after it.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void tab_unfold_kernel(TabUnfoldArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int rows = a.Runf + 32;
+  const int64_t n = (int64_t)a.Ho * rows * kHeadDim;
+  if (idx >= n) return;
+  const int d = (int)(idx % kHeadDim);
+  const int64_t hu = idx / kHeadDim;
+  const int u = (int)(hu % rows), ho = (int)(hu / rows);
+  float v = 0.f;
+  if (u < a.Runf) {
+    const int r = a.fold ? a.fold[u] : u;
+    v = MT<T>::to_f(((const T*)a.tab)[ho * a.tab_hs + (int64_t)r * kHeadDim + d]);
+  }
+  a.out[idx] = v;
 }
 
 // Block (rt, s, ho): unfolded rows u in [32 rt, 32 rt + 32), all 64 d, over
@@ -123,7 +352,12 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
   __shared__ float sSum[4][32];
   const Geo g = a.geo;
   const int N = g.N;
-  const int rt = blockIdx.x, sp = blockIdx.y, ho = blockIdx.z;
+  // the row tiles of one (split, head) are consecutive logical blocks, which
+  // xcd_remap keeps on one XCD: they read the same dZ rows and X rows, so
+  // those lines are fetched into that XCD's L2 once
+  const int nblk = gridDim.x * gridDim.y * gridDim.z;
+  const int lid = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), nblk);
+  const int rt = lid % gridDim.x, sp = (lid / gridDim.x) % gridDim.y, ho = lid / (gridDim.x * gridDim.y);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int u = 32 * rt + l32;  // unfolded row of this lane (operand A row)
   const int nseg = a.shared ? a.B * a.H : a.B;
@@ -158,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
       const int b_ = a.shared ? seg / a.H : seg;
       const int h_ = a.shared ? seg % a.H : ho;
       const int bh = b_ * a.H + h_;
-      const float* dzb = a.dz + (int64_t)bh * N * g.W;
+      const float* dzb = a.dz + (int64_t)bh * N * g.Wp;
       const T* xb = (const T*)a.x + b_ * a.sx.b + h_ * a.sx.h;
       const int col = u - ws;
       const bool colv = col >= cb && col < ce;
@@ -170,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
         for (int s2 = 0; s2 < 8; ++s2) {
           const int i = ib + 2 * s2 + hl;
           const bool rv = i < i_end;
-          av[s2] = (rv && colv) ? dzb[(int64_t)i * g.W + col] : 0.f;
+          av[s2] = (rv && colv) ? dzb[(int64_t)i * g.Wp + col] : 0.f;
           const T* xr = xb + (int64_t)i * a.sx.n;
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
@@ -240,6 +474,30 @@ hipError_t launch_rows(int dtype, const RowsArgs& a, hipStream_t st) {
     case 0: hipLaunchKernelGGL(rows_kernel<float>, dim3(total), dim3(kThreads), 0, st, a); break;
     case 1: hipLaunchKernelGGL(rows_kernel<_Float16>, dim3(total), dim3(kThreads), 0, st, a); break;
     default: hipLaunchKernelGGL(rows_kernel<__bf16>, dim3(total), dim3(kThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tab_unfold(int dtype, const TabUnfoldArgs& a, hipStream_t st) {
+  const int64_t n = (int64_t)a.Ho * (a.Runf + 32) * kHeadDim;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(tab_unfold_kernel<float>, grid, dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(tab_unfold_kernel<_Float16>, grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL(tab_unfold_kernel<__bf16>, grid, dim3(kThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cols1(int dtype, const ColsArgs& a, int Ho, hipStream_t st) {
+  dim3 grid((a.Rpad + kCU - 1) / kCU, a.splits, Ho);
+  if (dtype == 1) {
+    if (a.want_x) hipLaunchKernelGGL((cols1_kernel<_Float16, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((cols1_kernel<_Float16, false>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (a.want_x) hipLaunchKernelGGL((cols1_kernel<__bf16, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((cols1_kernel<__bf16, false>), grid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -32,6 +32,7 @@ struct Geo {
   int lo, hi;  // unfolded truncated map
   int R;       // rows of the unfolded map = hi - lo + 1
   int W;       // projection window width (= R for a single group, else N + G - 1)
+  int Wp;      // row stride of the Z / dZ buffers: W rounded up to 32 floats (128 B)
   int causal;  // 1 if j > i is masked
 };
 
@@ -164,16 +165,23 @@ struct RowTermArgs {     // padded backward row terms
 
 struct RowsArgs {       // dX = part + dZ . table   (per row)
   const float* part;    // [B*H][N][64] fp32
-  const float* dz;      // [B*H][N][W]
-  const void* tab;
-  int64_t tab_hs;
-  const int32_t* fold;
+  const float* dz;      // [B*H][N][Wp]
+  const float* tunf;    // [Ho][Runf + 32][64] fp32 unfolded table
+  int64_t tunf_hs;      // 0 (shared) or (Runf + 32) * 64
   void* out;            // dtype
   Str sout;
   int B, H;
   Geo geo;
   int key_side;
   int nblk;             // 128-row blocks per (b, h)
+};
+
+struct TabUnfoldArgs {  // out[ho][u][:] = tab[ho][fold(u)][:], 32 zero rows after Runf
+  const void* tab;
+  int64_t tab_hs;
+  const int32_t* fold;
+  float* out;
+  int Ho, Runf;
 };
 
 struct ColsArgs {       // partial[s][ho][u][:] = sum_i dZ[i][u - ws] x_i[:]

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void rowterm_kernel(RowTermArgs a) {
     const float base = -(l2 / a.scale2);
     float zlo = 0.f, zhi = 0.f;
     if (a.zq) {
-      const float* zqb = a.zq + bh * (int64_t)a.N * a.geo.W;
+      const float* zqb = a.zq + bh * (int64_t)a.N * a.geo.Wp;
       const float* p0 = qside_sat_ptr(a.geo, zqb, i, 0);
       const float* p1 = qside_sat_ptr(a.geo, zqb, i, 1);
       if (p0) zlo = *p0;

@@ -122,11 +122,11 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
     float badd = 0.f;
     if (a.bias && cv) badd = MT<T>::to_f(((const T*)a.bias)[hh * a.bias_hs + r]);
     if (cv) {
-      float* zc = a.z + (int64_t)bh * N * g.W + col;
+      float* zc = a.z + (int64_t)bh * N * g.Wp + col;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = grp * kBlockRows + 32 * w + res_row(hl, e);
-        if (row < N) zc[(int64_t)row * g.W] = acc[e] + badd;
+        if (row < N) zc[(int64_t)row * g.Wp] = acc[e] + badd;
       }
     }
   }

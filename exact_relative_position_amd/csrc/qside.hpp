@@ -76,7 +76,7 @@ __device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, i
     for (int e = 0; e < 16; ++e) {
       const int j = imin(jb + kap0<T>(e), g.N - 1);
       const int col = imin(imax(j - c.iq - g.lo - wk, 0), Wm);
-      v[e] += c.zkb[(int64_t)j * g.W + col];
+      v[e] += c.zkb[(int64_t)j * g.Wp + col];
     }
   }
   if (c.has_b) {
@@ -176,7 +176,7 @@ __device__ __forceinline__ const float* kside_sat_ptr(const Geo& g, const float*
   cols_k(g, grp, cb, ce);
   const int col = (side == 0 ? 0 : g.R - 1) - wk;
   if (col < cb || col >= ce) return nullptr;
-  return zkb + (int64_t)j * g.W + col;
+  return zkb + (int64_t)j * g.Wp + col;
 }
 // Same for the query side: Z^Q[i, first / last row] of query i.
 __device__ __forceinline__ const float* qside_sat_ptr(const Geo& g, const float* zqb, int i,
@@ -188,7 +188,7 @@ __device__ __forceinline__ const float* qside_sat_ptr(const Geo& g, const float*
   cols_q(g, grp, cb, ce);
   const int col = (side == 0 ? 0 : g.R - 1) - wq;
   if (col < cb || col >= ce) return nullptr;
-  return zqb + (int64_t)i * g.W + col;
+  return zqb + (int64_t)i * g.Wp + col;
 }
 
 }  // namespace relpos

@@ -127,8 +127,9 @@ relpos_status relpos_attn_workspace_size(const relpos_problem* prob, const relpo
 
 /* Bytes of the optional buffer in which the forward keeps the relation
  * projections Z^Q, Z^K (fp32, reachable window only) for the backward
- * (keeping them trades memory for recomputation, section on ablations).
- * 0 when no vector table is present.  Host-only. */
+ * (keeping them trades memory for recomputation, section on ablations):
+ * B*H*N rows per present vector term, each of the window width rounded up
+ * to 32 floats (128 bytes).  0 when no vector table is present.  Host-only. */
 relpos_status relpos_attn_zsave_size(const relpos_problem* prob, const relpos_phi* phi,
                                      int32_t terms, size_t* bytes);
 

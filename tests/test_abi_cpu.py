@@ -76,17 +76,19 @@ def test_phi_info_closed_forms():
 
 
 def test_zsave_size_closed_form(L):
-    # Shaw 8K: B*H*N*R*4 bytes (single group since R <= N + 127)
+    # Shaw 8K: B*H*N*Wp*4 bytes, window W = R = 257 (single group since
+    # R <= N + 127), rows padded to Wp = 288 floats (a multiple of 128 bytes)
     p = _prob(B=1, H=12, N=8192)
     phi = b.phi_struct({"kind": "truncated", "lo": -128, "hi": 128})
     n = ctypes.c_size_t()
     assert L.relpos_attn_zsave_size(ctypes.byref(p), ctypes.byref(phi), 1, ctypes.byref(n)) == 0
-    assert n.value == 12 * 8192 * 257 * 4
-    # identity map: the window is N + G - 1 = N + 127 columns per row
+    assert n.value == 12 * 8192 * 288 * 4
+    # identity map: the window is N + G - 1 = N + 127 = 4223 columns per row,
+    # padded to 4224
     p = _prob(B=2, H=8, N=4096, dtype=2)
     phi = b.phi_struct({"kind": "identity"})
     assert L.relpos_attn_zsave_size(ctypes.byref(p), ctypes.byref(phi), 1, ctypes.byref(n)) == 0
-    assert n.value == 2 * 8 * 4096 * (4096 + 127) * 4
+    assert n.value == 2 * 8 * 4096 * 4224 * 4
     # no vector table: nothing to keep
     assert L.relpos_attn_zsave_size(ctypes.byref(p), ctypes.byref(phi), 4, ctypes.byref(n)) == 0
     assert n.value == 0
