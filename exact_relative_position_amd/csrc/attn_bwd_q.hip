@@ -20,7 +20,11 @@ namespace relpos {
 __device__ inline int floor_div_q(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 __device__ inline int ceil_div_q(int a, int b) { return -floor_div_q(-a, b); }
 
-template <typename T>
+constexpr int kStagePitch = 36;  // floats per staged row (16-byte aligned, bank-spread)
+constexpr int kStageMinW = 1024; // band width from which band stores are staged
+
+// STAGE: band stores go through an LDS staging area (chosen for wide bands)
+template <typename T, bool STAGE>
 struct BwdQ {
   using M = MT<T>;
   using frag = typename M::frag;
@@ -54,6 +58,8 @@ struct BwdQ {
   f32x16 dq[2];
   float acc_lo, acc_hi;
   float* dz_row;
+  float* dz_w;     // dZ^Q row of this wave's first query (iw0)
+  float* stage;    // this wave's [32][kStagePitch] LDS staging area for band stores
 
   template <int BUF>
   __device__ __forceinline__ void issue(int t) {
@@ -63,6 +69,36 @@ struct BwdQ {
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
       dword_direct((char*)(sZK[BUF] + w * kTile), p, p != nullptr, lane);
+    }
+  }
+
+  // Store tau * ds of the 32 x 32 subtile (keys jb .. jb + 31) into dZ^Q:
+  // entry (query iw0 + q, key jb + k) goes to offset o = jb + k - iw0 - q of
+  // row iw0 + q when it is live and strictly inside the band.
+  __device__ __forceinline__ void band_store(const float (&ds)[16], int jb) {
+    // registers -> LDS [query][key]: lane (l32, hl) holds keys kappa(hl, e)
+    // (16-bit types: runs of 4 consecutive keys)
+    if constexpr (kHalf) {
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int k0 = kappa<T>(hl, 4 * e4);
+        *reinterpret_cast<f32x4*>(stage + l32 * kStagePitch + k0) = f32x4{
+            tau * ds[4 * e4], tau * ds[4 * e4 + 1], tau * ds[4 * e4 + 2], tau * ds[4 * e4 + 3]};
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) stage[l32 * kStagePitch + kappa<T>(hl, e)] = tau * ds[e];
+    }
+    // LDS -> HBM: rows q = 2 r + hl, key l32 of each
+    const int j = jb + l32;
+#pragma unroll 1
+    for (int r = 0; r < 16; ++r) {
+      const int q = 2 * r + hl;
+      const float v = stage[q * kStagePitch + l32];
+      const int i = iw0 + q;
+      const int o = j - i;
+      if (o > g.lo && o < g.hi && i < N && j < N && !(g.causal && j > i))
+        dz_w[(int64_t)q * g.Wp + o - g.lo - c.wsq] = v;
     }
   }
 
@@ -109,6 +145,12 @@ struct BwdQ {
           for (int e = 0; e < 16; ++e) tsum += ds[e];
           if (kind == KIND_LO) acc_lo += tsum; else acc_hi += tsum;
         } else {
+          // saturated entries go to the two per-query accumulators (masked
+          // entries have ds = 0).  With a wide band (most tiles inside it)
+          // the subtile goes through LDS so that each store instruction
+          // writes two 128-byte runs of dZ^Q rows (a query row holds its 32
+          // keys at consecutive offsets) instead of 64 scattered words; a
+          // narrow band has few fully interior subtiles and stores directly.
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int j = j0 + 32 * st + kappa<T>(hl, e);
@@ -117,10 +159,11 @@ struct BwdQ {
               acc_lo += ds[e];
             } else if (o >= g.hi) {
               acc_hi += ds[e];
-            } else if (c.iq < N && j < N && !(g.causal && j > c.iq)) {
+            } else if (!STAGE && c.iq < N && j < N && !(g.causal && j > c.iq)) {
               dz_row[o - g.lo - c.wsq] = tau * ds[e];
             }
           }
+          if constexpr (STAGE) band_store(ds, j0 + 32 * st);
         }
       }
       frag sf[KPS];
@@ -168,14 +211,16 @@ struct BwdQ {
   }
 };
 
-// ZK: whether the key-side relation term is present (compile-time switch).
-template <typename T, bool ZK>
+// ZK: whether the key-side relation term is present (compile-time switch);
+// STAGE: band stores staged through LDS.
+template <typename T, bool ZK, bool STAGE>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
   using M = MT<T>;
-  using B = BwdQ<T>;
+  using B = BwdQ<T, STAGE>;
   constexpr int TB = DTile<T>::BYTES;
   __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
   __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
+  __shared__ __align__(16) float sStage[STAGE ? 4 * 32 * kStagePitch : 4];
 
   B q;
   q.sK[0] = sK0;
@@ -255,6 +300,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
     q.Dl = a.D[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
   }
   q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
+  q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;
+  q.stage = STAGE ? sStage + w * 32 * kStagePitch : sStage;
   q.dq[0] = zero16();
   q.dq[1] = zero16();
   q.acc_lo = 0.f;
@@ -321,10 +368,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
 template <typename T>
 static hipError_t launch_bwd_q_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
-  if (a.flags & F_ZK)
-    hipLaunchKernelGGL((bwd_q_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+  const bool zk = a.flags & F_ZK, stage = a.geo.W >= kStageMinW;
+  if (zk && stage)
+    hipLaunchKernelGGL((bwd_q_kernel<T, true, true>), dim3(total), dim3(kThreads), 0, st, a);
+  else if (zk)
+    hipLaunchKernelGGL((bwd_q_kernel<T, true, false>), dim3(total), dim3(kThreads), 0, st, a);
+  else if (stage)
+    hipLaunchKernelGGL((bwd_q_kernel<T, false, true>), dim3(total), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((bwd_q_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<T, false, false>), dim3(total), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
