@@ -339,11 +339,11 @@ int terms_of(const void* aQ, const void* aK, const void* b) {
 }
 
 // Map tables needed by both passes: T5 fold table (+ ranges), unfolded bias.
-// Column contraction: a single-group window of a 16-bit problem streams its
-// dZ rows through the 64-row tiled kernel; grouped windows (a different
-// window per 128-row group) use the general kernel.
+// Column contraction: 16-bit problems stream their dZ rows through the
+// 64-row tiled kernel (grouped windows shift the loaded columns per group);
+// fp32 inputs use the general kernel.
 hipError_t cols(const Plan& pl, const ColsArgs& c, int Ho, hipStream_t st) {
-  if (pl.esz == 2 && !grouped(pl.geo)) return launch_cols1(pl.dtype, c, Ho, st);
+  if (pl.esz == 2) return launch_cols1(pl.dtype, c, Ho, st);
   return launch_cols(pl.dtype, c, Ho, st);
 }
 

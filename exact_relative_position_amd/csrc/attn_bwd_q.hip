@@ -214,7 +214,7 @@ struct BwdQ {
 // ZK: whether the key-side relation term is present (compile-time switch);
 // STAGE: band stores staged through LDS.
 template <typename T, bool ZK, bool STAGE>
-__global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel(AttnArgs a) {
   using M = MT<T>;
   using B = BwdQ<T, STAGE>;
   constexpr int TB = DTile<T>::BYTES;

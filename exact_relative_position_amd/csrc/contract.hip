@@ -176,34 +176,109 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
 // [cb, ce) hold no gradient and are read as zero.
 constexpr int kCU = 64;  // unfolded rows per block
 
+// Position in the flattened row range: row i of segment seg (b, or b*H + h
+// for a table shared by all heads).
+struct RowPos {
+  int seg, i;
+};
+__device__ __forceinline__ bool before(RowPos a, RowPos b) {
+  return a.seg < b.seg || (a.seg == b.seg && a.i < b.i);
+}
+
 template <typename T>
 struct ColsK {
   const float* dz;
   const T* x;
   Str sx;
-  int N, Wp, H, ho, cb, ce, ut, w, lane, hl, l32;
-  bool shared;
-  int64_t f1;  // end of this split's flattened row range
+  Geo g;
+  int N, Wp, H, ho, u0, w, lane, hl, l32, key_side;
+  bool shared, grp_on;
+  RowPos end;  // end of this split's row range
+  int cb0, ce0, ws0;  // the single window (ungrouped)
 
-  // rows [f, f + nrow) of the flattened row range (one segment: b, or b*H + h
-  // for a table shared by all heads) into (zb, xb), asynchronously
-  __device__ __forceinline__ void issue(float* zb, T* xb, int64_t f, int nrow) const {
-    const int seg = (int)(f / N);
-    const int i = (int)(f - (int64_t)seg * N);
+  // live window of group grp: columns [cb, ce) hold entries, column c is
+  // unfolded row ws + c
+  __device__ __forceinline__ void window(int grp, int& cb, int& ce, int& ws) const {
+    if (!grp_on) {
+      cb = cb0;
+      ce = ce0;
+      ws = ws0;
+    } else if (key_side) {
+      cols_k(g, grp, cb, ce);
+      ws = win_k(g, grp);
+    } else {
+      cols_q(g, grp, cb, ce);
+      ws = win_q(g, grp);
+    }
+  }
+  __device__ __forceinline__ int group_of(RowPos p) const { return grp_on ? p.i / kGroup : 0; }
+  // end of the run of rows that shares p's segment and window
+  __device__ __forceinline__ RowPos run_end(RowPos p) const {
+    RowPos e = grp_on ? RowPos{p.seg, imin(N, (p.i / kGroup + 1) * kGroup)} : RowPos{p.seg, N};
+    if (e.i >= N) e = RowPos{p.seg + 1, 0};
+    return before(end, e) ? end : e;
+  }
+  // first row at or after p (end if none) whose window's live columns meet
+  // this block's unfolded rows [u0, u0 + kCU); whole runs are skipped
+  __device__ __forceinline__ RowPos next_live(RowPos p) const {
+    while (before(p, end)) {
+      int cb, ce, ws;
+      window(group_of(p), cb, ce, ws);
+      if (ws + ce > u0 && ws + cb < u0 + kCU) return p;
+      p = run_end(p);
+    }
+    return end;
+  }
+  // rows of the chunk starting at p: up to 64, inside one run
+  __device__ __forceinline__ int chunk_rows(RowPos p) const {
+    const RowPos e = run_end(p);
+    const int n = e.seg == p.seg ? e.i - p.i : N - p.i;
+    return n < 64 ? n : 64;
+  }
+  __device__ __forceinline__ RowPos advance(RowPos p, int n) const {
+    p.i += n;
+    if (p.i >= N) p = RowPos{p.seg + 1, 0};
+    return p;
+  }
+
+  // rows [p.i, p.i + nrow) of segment p.seg into (zb, xb), asynchronously:
+  // zb[r][uo] holds dZ[i + r][u0 + uo - ws] (zero outside the stored row)
+  __device__ __forceinline__ void issue(float* zb, T* xb, RowPos p, int nrow) const {
+    const int seg = p.seg, i = p.i;
     const int b_ = shared ? seg / H : seg;
     const int h_ = shared ? seg % H : ho;
     const float* dzs = dz + (int64_t)(b_ * H + h_) * N * Wp;
+    int cb, ce, ws;
+    window(group_of(p), cb, ce, ws);
+    const int colb = u0 - ws;  // stored column of the block's first unfolded row
+    if ((colb & 3) == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = 4 * w + u;  // 4 rows of 64 floats per instruction
-      const int r = 4 * j + (lane >> 4);
-      const int col = kCU * ut + 4 * (lane & 15);
-      float* dst = zb + 256 * j;
-      if (r < nrow && col < Wp) {
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + col),
-                                         (lds_void_t*)dst, 16, 0, 0);
-      } else {
-        *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
+      for (int u = 0; u < 4; ++u) {
+        const int j = 4 * w + u;  // 4 rows of 64 floats per instruction
+        const int r = 4 * j + (lane >> 4);
+        const int col = colb + 4 * (lane & 15);
+        float* dst = zb + 256 * j;
+        if (r < nrow && col >= 0 && col < Wp) {
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + col),
+                                           (lds_void_t*)dst, 16, 0, 0);
+        } else {
+          *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
+        }
+      }
+    } else {
+      // window not 16-byte aligned with the block: one row of 64 floats per
+      // instruction
+      const int col = colb + lane;
+#pragma unroll 4
+      for (int u = 0; u < 16; ++u) {
+        const int r = 16 * w + u;
+        float* dst = zb + kCU * r;
+        if (r < nrow && col >= 0 && col < Wp) {
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + col),
+                                           (lds_void_t*)dst, 4, 0, 0);
+        } else {
+          dst[lane] = 0.f;
+        }
       }
     }
     const T* xs = x + b_ * sx.b + h_ * sx.h;
@@ -221,11 +296,12 @@ struct ColsK {
       }
     }
   }
-  // rows of the chunk starting at f: up to 64, not past its segment or f1
-  __device__ __forceinline__ int chunk_rows(int64_t f) const {
-    const int64_t send = (f / N + 1) * N;
-    const int64_t e = send < f1 ? send : f1;
-    return (int)(e - f < 64 ? e - f : 64);
+  // whether unfolded row u0 + uo is a live column of the chunk at p
+  __device__ __forceinline__ bool live(RowPos p, int uo) const {
+    int cb, ce, ws;
+    window(group_of(p), cb, ce, ws);
+    const int c = u0 + uo - ws;
+    return c >= cb && c < ce;
   }
 };
 
@@ -261,20 +337,20 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   k.lane = threadIdx.x & 63;
   k.hl = k.lane >> 5;
   k.l32 = k.lane & 31;
+  k.g = g;
   k.N = N;
   k.Wp = g.Wp;
   k.H = a.H;
   k.ho = ho;
-  k.ut = ut;
+  k.u0 = kCU * ut;
+  k.key_side = a.key_side;
   k.shared = a.shared;
   k.sx = a.sx;
   k.dz = a.dz;
   k.x = (const T*)a.x;
-  if (a.key_side) cols_k(g, 0, k.cb, k.ce); else cols_q(g, 0, k.cb, k.ce);
   const int w = k.w, hl = k.hl, l32 = k.l32;
   const int uo = 32 * (w & 1) + l32;  // this lane's unfolded row inside the block
-  const int u = kCU * ut + uo;
-  const bool uvalid = u >= k.cb && u < k.ce;
+  const int u = k.u0 + uo;
   const bool sums = w < 2;
   const int d = 32 * (w >> 1) + l32;
 
@@ -283,38 +359,42 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   const int64_t nrows = (int64_t)nseg * N;
   const int64_t per = (nrows + a.splits - 1) / a.splits;
   const int64_t f0 = (int64_t)sp * per;
-  k.f1 = f0 + per < nrows ? f0 + per : nrows;
+  const int64_t f1 = f0 + per < nrows ? f0 + per : nrows;
+  k.end = RowPos{(int)(f1 / N), (int)(f1 % N)};
+  k.grp_on = grouped(g);
+  if (a.key_side) cols_k(g, 0, k.cb0, k.ce0); else cols_q(g, 0, k.cb0, k.ce0);
+  k.ws0 = 0;
 
   f32x16 acc = zero16();
   float csum = 0.f;
-  // chunk n (rows [f, f + rows)) sits in buffer n & 1
-  int64_t f = f0;
-  int nrow = f < k.f1 ? k.chunk_rows(f) : 0;
-  if (nrow > 0) k.issue(sZ0, sX0, f, nrow);
+  // live chunk n (rows [p.i, p.i + nrow) of segment p.seg) sits in buffer n & 1
+  RowPos p = k.next_live(RowPos{(int)(f0 / N), (int)(f0 % N)});
+  int nrow = before(p, k.end) ? k.chunk_rows(p) : 0;
+  if (nrow > 0) k.issue(sZ0, sX0, p, nrow);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  while (f < k.f1) {
-    int64_t fn = f + nrow;
-    int nrow1 = fn < k.f1 ? k.chunk_rows(fn) : 0;
-    if (nrow1 > 0) k.issue(sZ1, sX1, fn, nrow1);
-    ColsMma<T, WANT_X>::run(sZ0, sX0, uo, d, hl, uvalid, sums, acc, csum);
+  while (before(p, k.end)) {
+    RowPos pn = k.next_live(k.advance(p, nrow));
+    int nrow1 = before(pn, k.end) ? k.chunk_rows(pn) : 0;
+    if (nrow1 > 0) k.issue(sZ1, sX1, pn, nrow1);
+    ColsMma<T, WANT_X>::run(sZ0, sX0, uo, d, hl, k.live(p, uo), sums, acc, csum);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    f = fn;
+    p = pn;
     nrow = nrow1;
-    if (f >= k.f1) break;
-    fn = f + nrow;
-    nrow1 = fn < k.f1 ? k.chunk_rows(fn) : 0;
-    if (nrow1 > 0) k.issue(sZ0, sX0, fn, nrow1);
-    ColsMma<T, WANT_X>::run(sZ1, sX1, uo, d, hl, uvalid, sums, acc, csum);
+    if (!before(p, k.end)) break;
+    pn = k.next_live(k.advance(p, nrow));
+    nrow1 = before(pn, k.end) ? k.chunk_rows(pn) : 0;
+    if (nrow1 > 0) k.issue(sZ0, sX0, pn, nrow1);
+    ColsMma<T, WANT_X>::run(sZ1, sX1, uo, d, hl, k.live(p, uo), sums, acc, csum);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    f = fn;
+    p = pn;
     nrow = nrow1;
   }
 
   if (WANT_X) {
-    float* outp = a.part + (((int64_t)sp * gridDim.z + ho) * a.Rpad + kCU * ut) * 64;
+    float* outp = a.part + (((int64_t)sp * gridDim.z + ho) * a.Rpad + k.u0) * 64;
 #pragma unroll
     for (int e = 0; e < 16; ++e) outp[(32 * (w & 1) + res_row(hl, e)) * 64 + d] = acc[e];
   }
