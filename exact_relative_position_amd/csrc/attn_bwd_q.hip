@@ -21,7 +21,6 @@ __device__ inline int floor_div_q(int a, int b) { return a >= 0 ? a / b : -((-a 
 __device__ inline int ceil_div_q(int a, int b) { return -floor_div_q(-a, b); }
 
 constexpr int kStagePitch = 36;  // floats per staged row (16-byte aligned, bank-spread)
-constexpr int kStageMinW = 1024; // band width from which band stores are staged
 
 // STAGE: band stores go through an LDS staging area (chosen for wide bands)
 template <typename T, bool STAGE>

@@ -31,7 +31,8 @@ namespace relpos {
 __device__ inline int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 __device__ inline int ceil_div(int a, int b) { return -floor_div(-a, b); }
 
-template <typename T>
+// ZQS: Z^Q band rows staged in LDS (wide bands) instead of gathered per score.
+template <typename T, bool ZQS>
 struct Fwd {
   using M = MT<T>;
   using frag = typename M::frag;
@@ -63,6 +64,7 @@ struct Fwd {
   frag qf[NSD];
   f32x16 oacc[2];
   float m_used, lsum;
+  ZqStage zs;  // Z^Q band rows of this wave, staged per subtile
 
   // Issue the loads of tile t into LDS buffer BUF (asynchronous).
   template <int BUF>
@@ -74,6 +76,19 @@ struct Fwd {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
       dword_direct((char*)(sZK[BUF] + w * kTile), p, p != nullptr, lane);
     }
+  }
+
+  // Whether this wave takes the band path with a Z^Q lookup on tile t (the
+  // tile's Z^Q rows are then staged in LDS).
+  __device__ __forceinline__ bool band_here(int t) const {
+    if constexpr (!ZQS) return false;
+    const int j0 = t * kTile;
+    return c.has_zq && t < nkt && iw0 < N && !(g.causal && j0 > iw0 + 31) &&
+           tile_kind_q(g, j0, iw0) == KIND_BAND;
+  }
+  template <int ST>
+  __device__ __forceinline__ void stage(int t) {
+    zs.template issue<ST>(g, c, iw0, t * kTile + 32 * ST, lane);
   }
 
   // V^T fragment (rows d = 32 dt + l32, keys of chunk column c4) of P V.
@@ -88,8 +103,10 @@ struct Fwd {
   // One 64-key tile for this wave, read from LDS buffer BUF.  BAND: the
   // block's tile crosses the band (each wave refines the kind for its own
   // queries); otherwise the whole tile is saturated on side `sat`.
+  // stage_next: this wave stages the Z^Q rows of tile t + 1 from its band
+  // path here, each subtile's rows once its own have been read.
   template <bool BAND, int BUF>
-  __device__ __forceinline__ void tile(int t, int sat) {
+  __device__ __forceinline__ void tile(int t, int sat, bool stage_next) {
     const int j0 = t * kTile;
     // (a saturated body also runs for a wave whose queries are all beyond N:
     // its results are discarded, and skipping would cost a branch and
@@ -127,9 +144,13 @@ struct Fwd {
         for (int ks = 0; ks < NSD; ++ks) kf[st][ks] = kfrag<T>(tK, kofs, c, st, ks);
       }
       f32x16 s;
-      if (BAND && kind == KIND_BAND)
-        s = qside_scores<T>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask);
-      else
+      if (BAND && kind == KIND_BAND) {
+        s = qside_scores<T>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask,
+                            ZQS ? zs.template row<T>(st, l32, hl) : nullptr);
+        if (stage_next) {
+          if (st == 0) stage<0>(t + 1); else stage<1>(t + 1);
+        }
+      } else
         s = qside_scores<T>(g, c, kf[st], zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
                             needmask);
       float mx = -INFINITY;
@@ -176,18 +197,29 @@ struct Fwd {
   template <int BUF>
   __device__ __forceinline__ void step(int t, int t1, int t2) {
     if (t + 1 < nkt) issue<BUF ^ 1>(t + 1);
+    // Z^Q rows of tile t + 1: staged now when tile t leaves the buffers
+    // free, else from tile t's band path
+    const bool bn = band_here(t + 1), bc = band_here(t);
+    if (bn && !bc) {
+      stage<0>(t + 1);
+      stage<1>(t + 1);
+    }
     const int j0 = t * kTile;
     const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
     if ((t >= t1 && t < t2) || masked)
-      tile<true, BUF>(t, KIND_BAND);
+      tile<true, BUF>(t, KIND_BAND, bn && bc);
     else
-      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI);
+      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI, false);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of tile t+1 landed
     __syncthreads();
   }
 
   __device__ __forceinline__ void run(int t1, int t2) {
     if (nkt > 0) issue<0>(0);
+    if (band_here(0)) {
+      stage<0>(0);
+      stage<1>(0);
+    }
     // every load issued so far (Q fragments, tile 0) has landed: inside the
     // loop a wave only waits for its own next-tile loads, before the barrier
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -201,17 +233,20 @@ struct Fwd {
 
 // ZK: whether the key-side relation term is present (a compile-time switch, so
 // that saturated tiles without it seed their MFMA accumulators with zero and
-// carry no branch).
-template <typename T, bool ZK>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnArgs a) {
+// carry no branch); ZQS: Z^Q band rows staged in LDS.
+template <typename T, bool ZK, bool ZQS>
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(AttnArgs a) {
   using M = MT<T>;
   constexpr float kLn2 = 0.693147180559945309f;
   constexpr int TB = DTile<T>::BYTES;
 
   __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
   __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
+  constexpr int kZQ = ZQS ? 4 * ZqStage::kFloats : 4;
+  __shared__ __align__(16) float sZQ0[kZQ], sZQ1[kZQ];
 
-  Fwd<T> f;
+  using F = Fwd<T, ZQS>;
+  F f;
   f.sK[0] = sK0;
   f.sK[1] = sK1;
   f.sV[0] = sV0;
@@ -252,11 +287,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnArgs a) {
   f.sv = a.sv.n;
   f.ldV.init(a.sv.n, w, lane);
   f.ldK.init(a.sk.n, w, lane);
-  if constexpr (Fwd<T>::kHalf) {
+  if constexpr (F::kHalf) {
     const int sig = sigma<T>(l32);
 #pragma unroll
-    for (int ks = 0; ks < Fwd<T>::NSD; ++ks)
-      f.kofs[ks] = dt_off<T>(sig, Fwd<T>::KS * ks + Fwd<T>::E * hl);
+    for (int ks = 0; ks < F::NSD; ++ks)
+      f.kofs[ks] = dt_off<T>(sig, F::KS * ks + F::E * hl);
     f.tr.init(lane);
   }
 
@@ -273,13 +308,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnArgs a) {
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
+  f.zs.buf[0] = ZQS ? sZQ0 + w * ZqStage::kFloats : sZQ0;
+  f.zs.buf[1] = ZQS ? sZQ1 + w * ZqStage::kFloats : sZQ1;
+  f.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, lane);
   f.sc2 = a.scale2;
 
   {
     const T* qrow = Qp + (int64_t)iq * a.sq.n;
 #pragma unroll
-    for (int ks = 0; ks < Fwd<T>::NSD; ++ks)
-      f.qf[ks] = iq < N ? frag_g<T>(qrow, Fwd<T>::KS * ks + Fwd<T>::E * hl) : M::zero();
+    for (int ks = 0; ks < F::NSD; ++ks)
+      f.qf[ks] = iq < N ? frag_g<T>(qrow, F::KS * ks + F::E * hl) : M::zero();
   }
   f.oacc[0] = zero16();
   f.oacc[1] = zero16();
@@ -313,10 +351,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnArgs a) {
 template <typename T>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
-  if (a.flags & F_ZK)
-    hipLaunchKernelGGL((fwd_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+  const bool zk = a.flags & F_ZK, zqs = (a.flags & F_ZQ) && a.geo.W >= kStageMinW;
+  if (zk && zqs)
+    hipLaunchKernelGGL((fwd_kernel<T, true, true>), dim3(total), dim3(kThreads), 0, st, a);
+  else if (zk)
+    hipLaunchKernelGGL((fwd_kernel<T, true, false>), dim3(total), dim3(kThreads), 0, st, a);
+  else if (zqs)
+    hipLaunchKernelGGL((fwd_kernel<T, false, true>), dim3(total), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, false, false>), dim3(total), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

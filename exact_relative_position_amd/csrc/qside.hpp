@@ -25,6 +25,10 @@ namespace relpos {
 
 enum : int { KIND_LO = 0, KIND_BAND = 1, KIND_HI = 2 };
 
+// Window width from which the lane = query kernels stage band rows through
+// LDS (most key tiles are then band tiles); narrower bands gather per score.
+constexpr int kStageMinW = 1024;
+
 // Kind of the tile of keys [j0, j0 + 64) for the 32 queries [iw0, iw0 + 32).
 __device__ inline int tile_kind_q(const Geo& g, int j0, int iw0) {
   int omax = j0 + kTile - 1 - iw0;
@@ -59,17 +63,24 @@ __device__ constexpr int kap0(int e) {
 // afterwards or belong to a discarded row, so what such a clamped load
 // returns never reaches a result.  For a live entry the clamp is the
 // identity: its unfolded row lies inside the group's window.
+// zst: this lane's Z^Q row in the LDS stage of the subtile (ZqStage, offset
+// by E * hl), which then replaces the Z^Q gather from global memory.
 template <typename T>
 __device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, int wk,
-                                          f32x16& s) {
+                                          const float* zst, f32x16& s) {
   const int Wm = g.W - 1;
   float v[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) v[e] = 0.f;
   if (c.has_zq) {
     const int base = jb - c.iq - g.lo - c.wsq;
+    if (zst) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = c.zq_row[imin(imax(base + kap0<T>(e), 0), Wm)];
+      for (int e = 0; e < 16; ++e) v[e] = zst[kap0<T>(e)];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = c.zq_row[imin(imax(base + kap0<T>(e), 0), Wm)];
+    }
   }
   if (c.has_zk) {
 #pragma unroll
@@ -107,11 +118,13 @@ __device__ __forceinline__ typename MT<T>::frag kfrag(const char* sK, const int*
 // The per-query constant of a saturated tile (Z^Q of the saturated row plus
 // b) is NOT included.
 // kf: the NSD K fragments of this subtile (kfrag), already read from LDS.
+// zst: the lane's staged Z^Q row of a band subtile (see band_seed), or null.
 template <typename T>
 __device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c,
                                                const typename MT<T>::frag* kf, const float* sZK,
                                                const typename MT<T>::frag* qf, int kind,
-                                               int j0, int st, bool needmask) {
+                                               int j0, int st, bool needmask,
+                                               const float* zst = nullptr) {
   using M = MT<T>;
   constexpr int NSD = kHeadDim / M::KS;
   f32x16 s;
@@ -127,7 +140,7 @@ __device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c,
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = v[e];
   } else {
-    band_seed<T>(g, c, j0 + 32 * st + MT<T>::E * c.hl, win_k(g, j0 / kGroup), s);
+    band_seed<T>(g, c, j0 + 32 * st + MT<T>::E * c.hl, win_k(g, j0 / kGroup), zst, s);
   }
 #pragma unroll
   for (int ks = 0; ks < NSD; ++ks) {
@@ -143,6 +156,67 @@ __device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c,
   }
   return s;
 }
+
+// Z^Q band entries of a wave's 32 queries for one 32-key subtile, staged in
+// LDS by row DMA instead of gathered per score.  Query iw0 + q, key jb + k
+// needs Z^Q[i, jb + k - i - lo - wsq]: for each query a run of 32
+// consecutive floats of its row.  One global_load_lds_dword moves the runs of
+// two queries (lanes 0-31: query 2p, lanes 32-63: query 2p + 1); row pairs
+// sit at a pitch of 68 floats, so that the 16-byte reads of 16 consecutive
+// queries hit distinct banks.  Each subtile position has its own buffer (and
+// LDS array), filled while the other one is read.
+struct ZqStage {
+  static constexpr int kPitch = 68;             // floats per row pair
+  static constexpr int kFloats = 16 * kPitch;   // one wave, one subtile
+  float* buf[2];     // this wave's buffers of subtile 0 / 1
+  const float* zq;   // Z^Q of this (b, h)
+  int lane_off;      // (lane & 31) + (lane >> 5) * (Wp - 1)
+
+  __device__ __forceinline__ void init(const Geo& g, const float* zq_bh, int lane) {
+    zq = zq_bh;
+    lane_off = (lane & 31) + (lane >> 5) * (g.Wp - 1);
+  }
+  // the lane's staged row of subtile position st (query l32, offset E * hl)
+  template <typename T>
+  __device__ __forceinline__ const float* row(int st, int l32, int hl) const {
+    return buf[st] + (l32 >> 1) * kPitch + (l32 & 1) * 32 + MT<T>::E * hl;
+  }
+  // Issue the row DMAs of keys [jb, jb + 32) into buffer ST (asynchronous).
+  // Columns are clamped into [0, W - 1] exactly as the per-score lookup
+  // clamps them: for a saturated entry of a band tile the clamp is the
+  // truncation of the map (first / last row); rows beyond N read row N - 1
+  // (their results are discarded).  A subtile that needs no clamp takes the
+  // fast path.
+  template <int ST>
+  __device__ __forceinline__ void issue(const Geo& g, const QCtx& c, int iw0, int jb,
+                                        int lane) const {
+    float* dst = buf[ST];
+    const int c0 = jb - iw0 - g.lo - c.wsq;  // column of query iw0, key jb
+    if (iw0 + 31 < g.N && c0 - 31 >= 0 && c0 + 31 < g.W) {
+      // wave-uniform row-pair address plus a fixed 32-bit lane offset
+      const char* base = reinterpret_cast<const char*>(zq + (int64_t)iw0 * g.Wp + c0);
+      const int64_t step = (int64_t)8 * (g.Wp - 1);  // bytes between row pairs
+      const uint32_t lb = 4u * (uint32_t)lane_off;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(base + lb),
+                                         (lds_void_t*)(dst + p * kPitch), 4, 0, 0);
+        base += step;
+      }
+    } else {
+      // crossing a threshold or the end of the sequence: clamped per lane
+      const int h = lane >> 5, k = lane & 31;
+#pragma unroll 1
+      for (int p = 0; p < 16; ++p) {
+        const int i = iw0 + 2 * p + h;
+        const int r = imin(i, g.N - 1);
+        const int col = imin(imax(jb + k - i - g.lo - c.wsq, 0), g.W - 1);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(zq + (int64_t)r * g.Wp + col),
+                                         (lds_void_t*)(dst + p * kPitch), 4, 0, 0);
+      }
+    }
+  }
+};
 
 // Saturated-row constants of this lane's query: Z^Q[i, first/last row] + b.
 // Columns outside the group's live window are never used for a live entry;
