@@ -21,6 +21,10 @@ __device__ inline int floor_div_q(int a, int b) { return a >= 0 ? a / b : -((-a 
 __device__ inline int ceil_div_q(int a, int b) { return -floor_div_q(-a, b); }
 
 constexpr int kStagePitch = 36;  // floats per staged row (16-byte aligned, bank-spread)
+// per wave and subtile position: Z^Q rows of the subtile (ZqStage), later
+// reused for the subtile's band stores ([32][kStagePitch])
+constexpr int kStageFloats = 32 * kStagePitch;
+static_assert(kStageFloats >= ZqStage::kFloats, "stage area holds the Z^Q rows");
 
 // STAGE: band stores go through an LDS staging area (chosen for wide bands)
 template <typename T, bool STAGE>
@@ -58,7 +62,21 @@ struct BwdQ {
   float acc_lo, acc_hi;
   float* dz_row;
   float* dz_w;     // dZ^Q row of this wave's first query (iw0)
-  float* stage;    // this wave's [32][kStagePitch] LDS staging area for band stores
+  // STAGE: this wave's two LDS areas (subtile positions 0 / 1); each first
+  // holds the Z^Q rows of its subtile, then takes its band stores
+  ZqStage zs;
+
+  // Whether this wave reads staged Z^Q rows on tile t.
+  __device__ __forceinline__ bool band_here(int t) const {
+    if constexpr (!STAGE) return false;
+    const int j0 = t * kTile;
+    return c.has_zq && t < nkt && iw0 < N && !(g.causal && j0 > iw0 + 31) &&
+           tile_kind_q(g, j0, iw0) == KIND_BAND;
+  }
+  template <int ST>
+  __device__ __forceinline__ void stage_zq(int t) {
+    zs.template issue<ST>(g, c, iw0, t * kTile + 32 * ST, lane);
+  }
 
   template <int BUF>
   __device__ __forceinline__ void issue(int t) {
@@ -74,7 +92,7 @@ struct BwdQ {
   // Store tau * ds of the 32 x 32 subtile (keys jb .. jb + 31) into dZ^Q:
   // entry (query iw0 + q, key jb + k) goes to offset o = jb + k - iw0 - q of
   // row iw0 + q when it is live and strictly inside the band.
-  __device__ __forceinline__ void band_store(const float (&ds)[16], int jb) {
+  __device__ __forceinline__ void band_store(const float (&ds)[16], int jb, float* stage) {
     // registers -> LDS [query][key]: lane (l32, hl) holds keys kappa(hl, e)
     // (16-bit types: runs of 4 consecutive keys)
     if constexpr (kHalf) {
@@ -103,8 +121,10 @@ struct BwdQ {
 
   // One 64-key tile from LDS buffer BUF; BAND: the block's tile crosses the
   // band, otherwise it is saturated on side `sat`.
+  // stage_next: the Z^Q rows of tile t + 1 are staged from this tile's band
+  // path, each subtile's once its area is free again.
   template <bool BAND, int BUF>
-  __device__ __forceinline__ void tile(int t, int sat) {
+  __device__ __forceinline__ void tile(int t, int sat, bool stage_next) {
     const int j0 = t * kTile;
     if (iw0 >= N || (g.causal && j0 > iw0 + 31)) return;
     const int kind = BAND ? tile_kind_q(g, j0, iw0) : sat;
@@ -123,7 +143,8 @@ struct BwdQ {
       for (int ks = 0; ks < NSD; ++ks) kf[ks] = kfrag<T>(tK, kofs, c, st, ks);
       f32x16 s;
       if (BAND && kind == KIND_BAND)
-        s = qside_scores<T>(g, c, kf, zk, qf, KIND_BAND, j0, st, needmask);
+        s = qside_scores<T>(g, c, kf, zk, qf, KIND_BAND, j0, st, needmask,
+                            STAGE ? zs.template row<T>(st, l32, hl) : nullptr);
       else
         s = qside_scores<T>(g, c, kf, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
                             needmask);
@@ -162,8 +183,11 @@ struct BwdQ {
               dz_row[o - g.lo - c.wsq] = tau * ds[e];
             }
           }
-          if constexpr (STAGE) band_store(ds, j0 + 32 * st);
+          if constexpr (STAGE) band_store(ds, j0 + 32 * st, zs.buf[st]);
         }
+      }
+      if (BAND && STAGE && kind == KIND_BAND && stage_next) {
+        if (st == 0) stage_zq<0>(t + 1); else stage_zq<1>(t + 1);
       }
       frag sf[KPS];
 #pragma unroll
@@ -188,19 +212,30 @@ struct BwdQ {
   template <int BUF>
   __device__ __forceinline__ void step(int t, int t1, int t2) {
     if (t + 1 < nkt) issue<BUF ^ 1>(t + 1);
+    // Z^Q rows of tile t + 1: staged now when tile t leaves the areas free,
+    // else from tile t's band path
+    const bool bn = band_here(t + 1), bc = band_here(t);
+    if (bn && !bc) {
+      stage_zq<0>(t + 1);
+      stage_zq<1>(t + 1);
+    }
     // tiles with masked entries also take the band body
     const int j0 = t * kTile;
     const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
     if ((t >= t1 && t < t2) || masked)
-      tile<true, BUF>(t, KIND_BAND);
+      tile<true, BUF>(t, KIND_BAND, bn && bc);
     else
-      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI);
+      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI, false);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
   __device__ __forceinline__ void run(int t1, int t2) {
     if (nkt > 0) issue<0>(0);
+    if (band_here(0)) {
+      stage_zq<0>(0);
+      stage_zq<1>(0);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     for (int t = 0; t < nkt; t += 2) {
@@ -219,7 +254,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   constexpr int TB = DTile<T>::BYTES;
   __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
   __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
-  __shared__ __align__(16) float sStage[STAGE ? 4 * 32 * kStagePitch : 4];
+  constexpr int kSt = STAGE ? 4 * kStageFloats : 4;
+  __shared__ __align__(16) float sSt0[kSt], sSt1[kSt];
 
   B q;
   q.sK[0] = sK0;
@@ -300,7 +336,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   }
   q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
   q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;
-  q.stage = STAGE ? sStage + w * 32 * kStagePitch : sStage;
+  q.zs.buf[0] = STAGE ? sSt0 + w * kStageFloats : sSt0;
+  q.zs.buf[1] = STAGE ? sSt1 + w * kStageFloats : sSt1;
+  q.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, lane);
   q.dq[0] = zero16();
   q.dq[1] = zero16();
   q.acc_lo = 0.f;
