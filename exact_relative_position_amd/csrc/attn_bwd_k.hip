@@ -27,7 +27,13 @@ __device__ inline int tile_kind_k(const Geo& g, int qt0, int jw0) {
 __device__ inline int floor_div_k(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 __device__ inline int ceil_div_k(int a, int b) { return -floor_div_k(-a, b); }
 
-template <typename T>
+constexpr int kStagePitchK = 36;  // floats per staged key row (16-byte aligned, bank-spread)
+// Window width from which band dZ^K stores are staged: the band's tiles are
+// few but each holds many interior entries.
+constexpr int kStageMinWK = 512;
+
+// STAGE: band dZ^K stores go through an LDS staging area.
+template <typename T, bool STAGE>
 struct BwdK {
   using M = MT<T>;
   using frag = typename M::frag;
@@ -55,6 +61,8 @@ struct BwdK {
   const float* zk_row;
   const float* bun;
   float* dz_row;
+  float* dz_w;    // dZ^K row of this wave's first key (jw0)
+  float* stage;   // STAGE: this wave's [32][kStagePitchK] LDS area
   int64_t sq, so, Np;
   DLoader<T> ldQ, ldO;
   // per-lane LDS byte offsets of the 16-bit row fragments (Q / dO row
@@ -117,6 +125,38 @@ struct BwdK {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         v[e] += bun[imin(imax(jk - ib - kap0<T>(e) - g.lo, 0), g.R - 1)];
+    }
+  }
+
+  // Store tau * ds of the 32 x 32 subtile (queries ib .. ib + 31) into dZ^K
+  // through LDS: entry (key jw0 + q, query ib + k) goes to offset
+  // o = jw0 + q - ib - k of key row jw0 + q when it is live and strictly
+  // inside the band.  A store instruction then writes two 128-byte runs of
+  // key rows (a key's 32 queries sit at consecutive offsets) instead of 64
+  // scattered words.
+  __device__ __forceinline__ void band_store(const float (&ds)[16], int ib) {
+    // registers -> LDS [key][query]: lane (l32, hl) holds queries kappa(hl, e)
+    if constexpr (kHalf) {
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int k0 = kappa<T>(hl, 4 * e4);
+        *reinterpret_cast<f32x4*>(stage + l32 * kStagePitchK + k0) = f32x4{
+            tau * ds[4 * e4], tau * ds[4 * e4 + 1], tau * ds[4 * e4 + 2], tau * ds[4 * e4 + 3]};
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) stage[l32 * kStagePitchK + kappa<T>(hl, e)] = tau * ds[e];
+    }
+    // LDS -> HBM: key rows q = 2 r + hl, query l32 of each
+    const int i = ib + l32;
+#pragma unroll 1
+    for (int r = 0; r < 16; ++r) {
+      const int q = 2 * r + hl;
+      const float v = stage[q * kStagePitchK + l32];
+      const int j = jw0 + q;
+      const int o = j - i;
+      if (o > g.lo && o < g.hi && i < N && j < N && !(g.causal && j > i))
+        dz_w[(int64_t)q * g.Wp + o - g.lo - wsk] = v;
     }
   }
 
@@ -196,9 +236,10 @@ struct BwdK {
             // (lo == hi: an offset equal to both counts once, on the low side)
             acc_lo += o <= g.lo ? ds[e] : 0.f;
             acc_hi += (o > g.lo && o >= g.hi) ? ds[e] : 0.f;
-            if (o > g.lo && o < g.hi && i < N && jk < N && !(g.causal && jk > i))
+            if (!STAGE && o > g.lo && o < g.hi && i < N && jk < N && !(g.causal && jk > i))
               dz_row[o - g.lo - wsk] = tau * ds[e];
           }
+          if constexpr (STAGE) band_store(ds, qt0 + 32 * st);
         }
       }
       frag pf[KPS], sf[KPS];
@@ -246,14 +287,16 @@ struct BwdK {
   }
 };
 
-// ZQ: whether the query-side relation term is present (compile-time switch).
-template <typename T, bool ZQ>
-__global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
+// ZQ: whether the query-side relation term is present (compile-time switch);
+// STAGE: band dZ^K stores staged through LDS.
+template <typename T, bool ZQ, bool STAGE>
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_k_kernel(AttnArgs a) {
   using M = MT<T>;
-  using K = BwdK<T>;
+  using K = BwdK<T, STAGE>;
   constexpr int TB = DTile<T>::BYTES;
   __shared__ __align__(16) char sQ0[TB], sQ1[TB], sO0[TB], sO1[TB];
   __shared__ __align__(16) float sR0[4 * kTile], sR1[4 * kTile];
+  __shared__ __align__(16) float sSt[STAGE ? 4 * 32 * kStagePitchK : 4];
 
   K k;
   k.sQ[0] = sQ0;
@@ -314,6 +357,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
   k.wsk = win_k(g, kb);
   k.zk_row = k.has_zk ? a.zk + ((int64_t)bh * N + imin(jk, N - 1)) * g.Wp : nullptr;
   k.dz_row = k.has_zk ? a.dzk + ((int64_t)bh * N + jk) * g.Wp : nullptr;
+  k.dz_w = k.has_zk ? a.dzk + ((int64_t)bh * N + jw0) * g.Wp : nullptr;
+  k.stage = STAGE ? sSt + w * 32 * kStagePitchK : sSt;
   k.sc2 = a.scale2;
   k.tau = a.tau;
 
@@ -426,10 +471,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_k_kernel(AttnArgs a) {
 template <typename T>
 static hipError_t launch_bwd_k_t(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
-  if (a.flags & F_ZQ)
-    hipLaunchKernelGGL((bwd_k_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+  const bool zq = a.flags & F_ZQ, stage = (a.flags & F_ZK) && a.geo.W >= kStageMinWK;
+  if (zq && stage)
+    hipLaunchKernelGGL((bwd_k_kernel<T, true, true>), dim3(total), dim3(kThreads), 0, st, a);
+  else if (zq)
+    hipLaunchKernelGGL((bwd_k_kernel<T, true, false>), dim3(total), dim3(kThreads), 0, st, a);
+  else if (stage)
+    hipLaunchKernelGGL((bwd_k_kernel<T, false, true>), dim3(total), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((bwd_k_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_k_kernel<T, false, false>), dim3(total), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

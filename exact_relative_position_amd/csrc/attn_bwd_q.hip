@@ -21,10 +21,10 @@ __device__ inline int floor_div_q(int a, int b) { return a >= 0 ? a / b : -((-a 
 __device__ inline int ceil_div_q(int a, int b) { return -floor_div_q(-a, b); }
 
 constexpr int kStagePitch = 36;  // floats per staged row (16-byte aligned, bank-spread)
-// per wave and subtile position: Z^Q rows of the subtile (ZqStage), later
+// per wave and subtile position: Z^Q rows of the subtile (RowStage), later
 // reused for the subtile's band stores ([32][kStagePitch])
 constexpr int kStageFloats = 32 * kStagePitch;
-static_assert(kStageFloats >= ZqStage::kFloats, "stage area holds the Z^Q rows");
+static_assert(kStageFloats >= RowStage::kFloats, "stage area holds the Z^Q rows");
 
 // STAGE: band stores go through an LDS staging area (chosen for wide bands)
 template <typename T, bool STAGE>
@@ -64,7 +64,7 @@ struct BwdQ {
   float* dz_w;     // dZ^Q row of this wave's first query (iw0)
   // STAGE: this wave's two LDS areas (subtile positions 0 / 1); each first
   // holds the Z^Q rows of its subtile, then takes its band stores
-  ZqStage zs;
+  RowStage zs;
 
   // Whether this wave reads staged Z^Q rows on tile t.
   __device__ __forceinline__ bool band_here(int t) const {
@@ -75,7 +75,7 @@ struct BwdQ {
   }
   template <int ST>
   __device__ __forceinline__ void stage_zq(int t) {
-    zs.template issue<ST>(g, c, iw0, t * kTile + 32 * ST, lane);
+    zs.template issue_q<ST>(g, c, iw0, t * kTile + 32 * ST, lane);
   }
 
   template <int BUF>
@@ -144,7 +144,7 @@ struct BwdQ {
       f32x16 s;
       if (BAND && kind == KIND_BAND)
         s = qside_scores<T>(g, c, kf, zk, qf, KIND_BAND, j0, st, needmask,
-                            STAGE ? zs.template row<T>(st, l32, hl) : nullptr);
+                            STAGE ? zs.row(st, l32) + E * hl : nullptr);
       else
         s = qside_scores<T>(g, c, kf, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
                             needmask);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;
   q.zs.buf[0] = STAGE ? sSt0 + w * kStageFloats : sSt0;
   q.zs.buf[1] = STAGE ? sSt1 + w * kStageFloats : sSt1;
-  q.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, lane);
+  q.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, -1, lane);
   q.dq[0] = zero16();
   q.dq[1] = zero16();
   q.acc_lo = 0.f;

@@ -64,7 +64,7 @@ struct Fwd {
   frag qf[NSD];
   f32x16 oacc[2];
   float m_used, lsum;
-  ZqStage zs;  // Z^Q band rows of this wave, staged per subtile
+  RowStage zs;  // Z^Q band rows of this wave, staged per subtile
 
   // Issue the loads of tile t into LDS buffer BUF (asynchronous).
   template <int BUF>
@@ -88,7 +88,7 @@ struct Fwd {
   }
   template <int ST>
   __device__ __forceinline__ void stage(int t) {
-    zs.template issue<ST>(g, c, iw0, t * kTile + 32 * ST, lane);
+    zs.template issue_q<ST>(g, c, iw0, t * kTile + 32 * ST, lane);
   }
 
   // V^T fragment (rows d = 32 dt + l32, keys of chunk column c4) of P V.
@@ -146,7 +146,7 @@ struct Fwd {
       f32x16 s;
       if (BAND && kind == KIND_BAND) {
         s = qside_scores<T>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask,
-                            ZQS ? zs.template row<T>(st, l32, hl) : nullptr);
+                            ZQS ? zs.row(st, l32) + E * hl : nullptr);
         if (stage_next) {
           if (st == 0) stage<0>(t + 1); else stage<1>(t + 1);
         }
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(A
 
   __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
   __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
-  constexpr int kZQ = ZQS ? 4 * ZqStage::kFloats : 4;
+  constexpr int kZQ = ZQS ? 4 * RowStage::kFloats : 4;
   __shared__ __align__(16) float sZQ0[kZQ], sZQ1[kZQ];
 
   using F = Fwd<T, ZQS>;
@@ -308,9 +308,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(A
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
-  f.zs.buf[0] = ZQS ? sZQ0 + w * ZqStage::kFloats : sZQ0;
-  f.zs.buf[1] = ZQS ? sZQ1 + w * ZqStage::kFloats : sZQ1;
-  f.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, lane);
+  f.zs.buf[0] = ZQS ? sZQ0 + w * RowStage::kFloats : sZQ0;
+  f.zs.buf[1] = ZQS ? sZQ1 + w * RowStage::kFloats : sZQ1;
+  f.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, -1, lane);
   f.sc2 = a.scale2;
 
   {

@@ -63,7 +63,7 @@ __device__ constexpr int kap0(int e) {
 // afterwards or belong to a discarded row, so what such a clamped load
 // returns never reaches a result.  For a live entry the clamp is the
 // identity: its unfolded row lies inside the group's window.
-// zst: this lane's Z^Q row in the LDS stage of the subtile (ZqStage, offset
+// zst: this lane's Z^Q row in the LDS stage of the subtile (RowStage, offset
 // by E * hl), which then replaces the Z^Q gather from global memory.
 template <typename T>
 __device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, int wk,
@@ -157,45 +157,48 @@ __device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c,
   return s;
 }
 
-// Z^Q band entries of a wave's 32 queries for one 32-key subtile, staged in
-// LDS by row DMA instead of gathered per score.  Query iw0 + q, key jb + k
-// needs Z^Q[i, jb + k - i - lo - wsq]: for each query a run of 32
-// consecutive floats of its row.  One global_load_lds_dword moves the runs of
-// two queries (lanes 0-31: query 2p, lanes 32-63: query 2p + 1); row pairs
-// sit at a pitch of 68 floats, so that the 16-byte reads of 16 consecutive
-// queries hit distinct banks.  Each subtile position has its own buffer (and
-// LDS array), filled while the other one is read.
-struct ZqStage {
+// Band entries of a relation projection staged in LDS by row DMA instead of
+// gathered per score.  For a wave's 32 rows (queries for Z^Q, keys for Z^K)
+// and one 32-token subtile of the other side, each row needs a run of 32
+// consecutive floats of its own row of Z: row row0 + m from column
+// c0 + dc * m (dc = -1 when the subtile's tokens are keys and the rows
+// queries, +1 for key rows against queries in reverse order).  One
+// global_load_lds_dword moves the runs of two rows (lanes 0-31: row 2p,
+// lanes 32-63: row 2p + 1); row pairs sit at a pitch of 68 floats, so that
+// 16-byte reads of 16 consecutive rows hit distinct banks.  Each subtile
+// position has its own buffer (and LDS array), filled while the other one
+// is read.
+struct RowStage {
   static constexpr int kPitch = 68;             // floats per row pair
   static constexpr int kFloats = 16 * kPitch;   // one wave, one subtile
   float* buf[2];     // this wave's buffers of subtile 0 / 1
-  const float* zq;   // Z^Q of this (b, h)
-  int lane_off;      // (lane & 31) + (lane >> 5) * (Wp - 1)
+  const float* z;    // Z of this (b, h), row stride Wp
+  int dc;            // column step per row
+  int lane_off;      // (lane & 31) + (lane >> 5) * (Wp + dc)
 
-  __device__ __forceinline__ void init(const Geo& g, const float* zq_bh, int lane) {
-    zq = zq_bh;
-    lane_off = (lane & 31) + (lane >> 5) * (g.Wp - 1);
+  __device__ __forceinline__ void init(const Geo& g, const float* z_bh, int dc_, int lane) {
+    z = z_bh;
+    dc = dc_;
+    lane_off = (lane & 31) + (lane >> 5) * (g.Wp + dc);
   }
-  // the lane's staged row of subtile position st (query l32, offset E * hl)
-  template <typename T>
-  __device__ __forceinline__ const float* row(int st, int l32, int hl) const {
-    return buf[st] + (l32 >> 1) * kPitch + (l32 & 1) * 32 + MT<T>::E * hl;
+  // staged row m, position 0 (row pairs at kPitch, odd rows 32 floats in)
+  __device__ __forceinline__ const float* row(int st, int m) const {
+    return buf[st] + (m >> 1) * kPitch + (m & 1) * 32;
   }
-  // Issue the row DMAs of keys [jb, jb + 32) into buffer ST (asynchronous).
-  // Columns are clamped into [0, W - 1] exactly as the per-score lookup
-  // clamps them: for a saturated entry of a band tile the clamp is the
-  // truncation of the map (first / last row); rows beyond N read row N - 1
-  // (their results are discarded).  A subtile that needs no clamp takes the
-  // fast path.
+  // Issue the row DMAs of rows [row0, row0 + 32), run k of row row0 + m at
+  // column c0 + dc m + k, into buffer ST (asynchronous).  Columns are
+  // clamped into [0, W - 1] exactly as the per-score lookup clamps them: for
+  // a saturated entry of a band tile the clamp is the truncation of the map
+  // (first / last row); rows beyond N read row N - 1 (their results are
+  // discarded).  A subtile that needs no clamp takes the fast path.
   template <int ST>
-  __device__ __forceinline__ void issue(const Geo& g, const QCtx& c, int iw0, int jb,
-                                        int lane) const {
+  __device__ __forceinline__ void issue(const Geo& g, int row0, int c0, int lane) const {
     float* dst = buf[ST];
-    const int c0 = jb - iw0 - g.lo - c.wsq;  // column of query iw0, key jb
-    if (iw0 + 31 < g.N && c0 - 31 >= 0 && c0 + 31 < g.W) {
+    const int cmin = c0 + (dc < 0 ? 31 * dc : 0), cmax = c0 + 31 + (dc > 0 ? 31 * dc : 0);
+    if (row0 + 31 < g.N && cmin >= 0 && cmax < g.W) {
       // wave-uniform row-pair address plus a fixed 32-bit lane offset
-      const char* base = reinterpret_cast<const char*>(zq + (int64_t)iw0 * g.Wp + c0);
-      const int64_t step = (int64_t)8 * (g.Wp - 1);  // bytes between row pairs
+      const char* base = reinterpret_cast<const char*>(z + (int64_t)row0 * g.Wp + c0);
+      const int64_t step = (int64_t)8 * (g.Wp + dc);  // bytes between row pairs
       const uint32_t lb = 4u * (uint32_t)lane_off;
 #pragma unroll
       for (int p = 0; p < 16; ++p) {
@@ -208,13 +211,20 @@ struct ZqStage {
       const int h = lane >> 5, k = lane & 31;
 #pragma unroll 1
       for (int p = 0; p < 16; ++p) {
-        const int i = iw0 + 2 * p + h;
-        const int r = imin(i, g.N - 1);
-        const int col = imin(imax(jb + k - i - g.lo - c.wsq, 0), g.W - 1);
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(zq + (int64_t)r * g.Wp + col),
+        const int m = 2 * p + h;
+        const int r = imin(row0 + m, g.N - 1);
+        const int col = imin(imax(c0 + dc * m + k, 0), g.W - 1);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(z + (int64_t)r * g.Wp + col),
                                          (lds_void_t*)(dst + p * kPitch), 4, 0, 0);
       }
     }
+  }
+  // Z^Q rows of queries [iw0, iw0 + 32) against keys [jb, jb + 32) (lane =
+  // query kernels)
+  template <int ST>
+  __device__ __forceinline__ void issue_q(const Geo& g, const QCtx& c, int iw0, int jb,
+                                          int lane) const {
+    issue<ST>(g, iw0, jb - iw0 - g.lo - c.wsq, lane);
   }
 };
 
