@@ -31,12 +31,24 @@ namespace relpos {
 __device__ inline int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 __device__ inline int ceil_div(int a, int b) { return -floor_div(-a, b); }
 
+// Waves per SIMD the forward is compiled for: 16-bit inputs without a
+// key-side term or staged rows fit 3 (168 VGPRs), which hides more latency
+// than operand prefetch; the others keep 2.
+template <typename T, bool ZK, bool ZQS>
+constexpr int fwd_occupancy() {
+  return (sizeof(T) == 2 && !ZK && !ZQS) ? 3 : (sizeof(T) == 2 ? 2 : 1);
+}
+
 // ZQS: Z^Q band rows staged in LDS (wide bands) instead of gathered per score.
-template <typename T, bool ZQS>
+// OCC3: compiled for 3 waves per SIMD: each subtile reads its own operand
+// fragments (instead of the whole tile's up front), which keeps fewer
+// registers live.
+template <typename T, bool ZQS, bool OCC3>
 struct Fwd {
   using M = MT<T>;
   using frag = typename M::frag;
   static constexpr bool kHalf = sizeof(T) == 2;
+  static constexpr bool kOcc3 = OCC3;
   static constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
   static constexpr int KPS = 32 / KS;  // MFMA k-steps per 32-key half
   static constexpr int TB = DTile<T>::BYTES;
@@ -120,11 +132,12 @@ struct Fwd {
     const char* tV = sV[BUF];
     const float* zk = sZK[BUF];
     const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
-    // 16-bit types: every operand fragment of the tile is read from LDS up
-    // front (one batch of ds_read_b128), so the reads of the second half
-    // overlap the first half's MFMAs and softmax
+    // 16-bit types at occupancy 2: every operand fragment of the tile is read
+    // from LDS up front (one batch), so the reads of the second half overlap
+    // the first half's MFMAs and softmax; at occupancy 3 (and for fp32) each
+    // subtile reads its own
     frag kf[2][NSD], vf[2][2 * KPS];
-    if constexpr (kHalf) {
+    if constexpr (kHalf && !kOcc3) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -139,9 +152,15 @@ struct Fwd {
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      if constexpr (!kHalf) {
+      if constexpr (!kHalf || kOcc3) {
 #pragma unroll
         for (int ks = 0; ks < NSD; ++ks) kf[st][ks] = kfrag<T>(tK, kofs, c, st, ks);
+      }
+      if constexpr (kHalf && kOcc3) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int kk = 0; kk < KPS; ++kk) vf[st][dt * KPS + kk] = vfrag(tV, dt, KPS * st + kk);
       }
       f32x16 s;
       if (BAND && kind == KIND_BAND) {
@@ -235,7 +254,7 @@ struct Fwd {
 // that saturated tiles without it seed their MFMA accumulators with zero and
 // carry no branch); ZQS: Z^Q band rows staged in LDS.
 template <typename T, bool ZK, bool ZQS>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, (fwd_occupancy<T, ZK, ZQS>())) void fwd_kernel(AttnArgs a) {
   using M = MT<T>;
   constexpr float kLn2 = 0.693147180559945309f;
   constexpr int TB = DTile<T>::BYTES;
@@ -245,7 +264,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(A
   constexpr int kZQ = ZQS ? 4 * RowStage::kFloats : 4;
   __shared__ __align__(16) float sZQ0[kZQ], sZQ1[kZQ];
 
-  using F = Fwd<T, ZQS>;
+  using F = Fwd<T, ZQS, fwd_occupancy<T, ZK, ZQS>() == 3>;
   F f;
   f.sK[0] = sK0;
   f.sK[1] = sK1;
