@@ -34,6 +34,7 @@ hipError_t launch_rows(int dtype, const RowsArgs& a, hipStream_t st);
 hipError_t launch_tab_unfold(int dtype, const TabUnfoldArgs& a, hipStream_t st);
 hipError_t launch_cols(int dtype, const ColsArgs& a, int Ho, hipStream_t st);
 hipError_t launch_cols1(int dtype, const ColsArgs& a, int Ho, hipStream_t st);
+hipError_t launch_xsplit(const SplitArgs& a, hipStream_t st);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t st);
 }  // namespace relpos
 
@@ -266,8 +267,15 @@ struct WsBwd {
   float* L2 = nullptr;  // [B*H][Np]
   float* D = nullptr;   // [B*H][Np]
   float* kseed = nullptr;  // [4][B*H][Np]
-  float* tunf_q = nullptr;  // [ho][Runf + 32][64] fp32 unfolded tables
+  // [ho][Runf + 32][64] unfolded tables: fp32, or for 16-bit inputs a bf16
+  // high part followed by a bf16 low part (fp16) in the same bytes
+  float* tunf_q = nullptr;
   float* tunf_k = nullptr;
+  // fp16 Q / K split into two bf16 parts, [B*H][N][64] each (column contraction)
+  void* xq_h = nullptr;
+  void* xq_l = nullptr;
+  void* xk_h = nullptr;
+  void* xk_l = nullptr;
   float* dq_part = nullptr;
   float* dk_part = nullptr;
   float* dzq = nullptr;
@@ -310,6 +318,17 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
   const size_t tu = (size_t)(pl.Runf + 32) * kHeadDim;
   if (pl.has_aq) w.tunf_q = c.take<float>(sizeof(float) * pl.ho_aq * tu);
   if (pl.has_ak) w.tunf_k = c.take<float>(sizeof(float) * pl.ho_ak * tu);
+  if (pl.dtype == 1) {
+    const size_t xb = sizeof(uint16_t) * bhn * kHeadDim;
+    if (pl.has_aq) {
+      w.xq_h = c.take<uint16_t>(xb);
+      w.xq_l = c.take<uint16_t>(xb);
+    }
+    if (pl.has_ak) {
+      w.xk_h = c.take<uint16_t>(xb);
+      w.xk_l = c.take<uint16_t>(xb);
+    }
+  }
   if (pl.has_aq) w.dq_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_ak) w.dk_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_aq || pl.has_b) w.dzq = c.take<float>(sizeof(float) * pl.z_elems);
@@ -682,21 +701,36 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
 
   // dQ += dZ^Q aQ, dK += dZ^K aK
   const int64_t tu_hs = (int64_t)(pl.Runf + 32) * kHeadDim;
+  // low bf16 part of an fp16 table: after the high part, in the same bytes
+  auto tab_lo = [&](float* t, int ho) -> void* {
+    return pl.dtype == 1 ? (void*)((uint16_t*)t + (size_t)ho * tu_hs) : nullptr;
+  };
   if (pl.has_aq) {
-    TabUnfoldArgs t{aQ, pl.aq_hs, pl.t5 ? w.fold : nullptr, w.tunf_q, pl.ho_aq, pl.Runf};
+    TabUnfoldArgs t{aQ, pl.aq_hs, pl.t5 ? w.fold : nullptr, w.tunf_q, tab_lo(w.tunf_q, pl.ho_aq),
+                    pl.ho_aq, pl.Runf};
     if ((s = hip_check(launch_tab_unfold(pl.dtype, t, st), "table unfold aQ")) != RELPOS_OK)
       return s;
-    RowsArgs r{w.dq_part, w.dzq, w.tunf_q, pl.aq_hs == 0 ? 0 : tu_hs, dQ,
+    RowsArgs r{w.dq_part, w.dzq, w.tunf_q, t.out_lo, pl.aq_hs == 0 ? 0 : tu_hs, dQ,
                str_of(prob, RELPOS_T_DQ), pl.B, pl.H, pl.geo, 0, pl.nblk};
     if ((s = hip_check(launch_rows(pl.dtype, r, st), "contraction dQ")) != RELPOS_OK) return s;
   }
   if (pl.has_ak) {
-    TabUnfoldArgs t{aK, pl.ak_hs, pl.t5 ? w.fold : nullptr, w.tunf_k, pl.ho_ak, pl.Runf};
+    TabUnfoldArgs t{aK, pl.ak_hs, pl.t5 ? w.fold : nullptr, w.tunf_k, tab_lo(w.tunf_k, pl.ho_ak),
+                    pl.ho_ak, pl.Runf};
     if ((s = hip_check(launch_tab_unfold(pl.dtype, t, st), "table unfold aK")) != RELPOS_OK)
       return s;
-    RowsArgs r{w.dk_part, w.dzk, w.tunf_k, pl.ak_hs == 0 ? 0 : tu_hs, dK,
+    RowsArgs r{w.dk_part, w.dzk, w.tunf_k, t.out_lo, pl.ak_hs == 0 ? 0 : tu_hs, dK,
                str_of(prob, RELPOS_T_DK), pl.B, pl.H, pl.geo, 1, pl.nblk};
     if ((s = hip_check(launch_rows(pl.dtype, r, st), "contraction dK")) != RELPOS_OK) return s;
+  }
+  // fp16 Q / K as two exact bf16 parts for the column contraction
+  if (pl.dtype == 1 && pl.has_aq) {
+    SplitArgs x{Q, str_of(prob, RELPOS_T_Q), w.xq_h, w.xq_l, pl.B, pl.H, pl.N};
+    if ((s = hip_check(launch_xsplit(x, st), "split Q")) != RELPOS_OK) return s;
+  }
+  if (pl.dtype == 1 && pl.has_ak) {
+    SplitArgs x{K, str_of(prob, RELPOS_T_K), w.xk_h, w.xk_l, pl.B, pl.H, pl.N};
+    if ((s = hip_check(launch_xsplit(x, st), "split K")) != RELPOS_OK) return s;
   }
   // table gradients: dZ^T Q, dZ^T K, column sums of dZ^Q; then the fold
   const int32_t* ub = pl.t5 ? w.ub : nullptr;
@@ -706,6 +740,8 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     ColsArgs c{};
     c.dz = w.dzq;
     c.x = Q;
+    c.xh = w.xq_h;
+    c.xl = w.xq_l;
     c.sx = str_of(prob, RELPOS_T_Q);
     c.part = w.part_q;
     c.partb = joint_b ? w.part_qb : nullptr;
@@ -749,6 +785,8 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     ColsArgs c{};
     c.dz = w.dzk;
     c.x = K;
+    c.xh = w.xk_h;
+    c.xl = w.xk_l;
     c.sx = str_of(prob, RELPOS_T_K);
     c.part = w.part_k;
     c.partb = nullptr;

@@ -8,12 +8,15 @@
 // The scalar-bias gradient is read here as the column sums of dZ^Q
 // (db[r] = tau * sum over all pairs with phi = r of dS, from Eq. 1 and 4).
 //
-// All three kernels use v_mfma_f32_32x32x2_f32 on fp32 data and fixed
-// summation orders (no atomics):
-//  * rows_kernel:  dX[i] = dX_part[i] + sum_c dZ[i][c] tab[fold(ws + c)], with
-//                  the table unfolded to fp32 first (tab_unfold_kernel)
-//  * cols_kernel:  part[s][h][u] = sum over the rows i of split s of dZ[i][u - ws(i)] x_i
-//                  (and the column sums for db), window-aware;
+// fp32 inputs run on v_mfma_f32_32x32x2_f32.  16-bit inputs run on
+// v_mfma_f32_32x32x16_bf16 with every fp32 operand split into two bf16 parts
+// (z = hi + lo + r, |r| <= 2^-16 |z|) and fp16 operands split exactly into two
+// bf16 parts; the products hi*hi, hi*lo and lo*hi are kept (the dropped lo*lo
+// is below 2^-16 of the term).  Summation orders are fixed (no atomics):
+//  * rows_kernel / rows2_kernel: dX[i] = dX_part[i] + sum_c dZ[i][c] tab[fold(ws + c)],
+//                  with the table unfolded first (tab_unfold_kernel)
+//  * cols_kernel / cols1_kernel: part[s][h][u] = sum over the rows i of split s
+//                  of dZ[i][u - ws(i)] x_i (and the column sums for db), window-aware;
 //  * fold_kernel:  out[h][k] = sum over splits and over the unfolded rows u of k.
 #include "device.hpp"
 #include "tiles.hpp"
@@ -22,6 +25,16 @@ namespace relpos {
 
 __device__ inline f32x16 mma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// z = hi + lo + r with |r| <= 2^-16 |z|: hi = bf16(z), lo = bf16(z - hi)
+// (z - hi is exact in fp32).
+__device__ __forceinline__ void split_bf16(const float (&z)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    hi[j] = (__bf16)z[j];
+    lo[j] = (__bf16)(z[j] - (float)hi[j]);
+  }
 }
 
 // Row contraction, one block = 128 rows of one (b, h) (one group), 4 waves x
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
     k.ws = win_q(g, rb);
   }
   k.dzb = a.dz + (int64_t)bh * N * g.Wp;
-  k.tub = a.tunf + hh * a.tunf_hs;
+  k.tub = (const float*)a.tunf + hh * a.tunf_hs;
   const int w = k.w, hl = k.hl, l32 = k.l32;
 
   f32x16 acc[2];
@@ -165,6 +178,156 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
     }
 }
 
+// Row contraction for 16-bit inputs: the blocks, chunks and dZ loads of
+// rows_kernel; the table chunk (32 unfolded rows, bf16 high and, for fp16
+// tables, low part) goes into LDS in the swizzled 16-bit tile layout and is
+// read as the MFMA B operand with transpose reads; each lane splits its 8 dZ
+// values of a k-step into bf16 parts.
+template <typename T>
+struct Rows2K {
+  using BF = MT<__bf16>;
+  static constexpr bool kLo = std::is_same<T, _Float16>::value;  // table has a low part
+  const float* dzb;   // dZ of this (b, h), row stride Wp
+  const __bf16* thb;  // unfolded table of this head, high part, [Runf + 32][64]
+  const __bf16* tlb;  // low part (fp16 tables)
+  int N, Wp, i0, ws, cb, ce, w, lane, hl, l32;
+  TrReader<__bf16> tr;
+
+  __device__ __forceinline__ void issue(float* zb, char* th, char* tl, int c0) const {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 4 * w + u;  // 8 rows per instruction
+      const int r = 8 * j + (lane >> 3);
+      const int lc = (lane & 7) ^ RowsK<T>::zswz(r);
+      float* dst = zb + 256 * j;
+      if (i0 + r < N) {
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + c0 + 4 * lc),
+                                         (lds_void_t*)dst, 16, 0, 0);
+      } else {
+        *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
+      }
+    }
+    // table rows ws + c0 + r, r = 8 w + lane / 8: slot lane % 8 of the row
+    // holds its chunk (lane % 8) ^ swz(r)
+    const int r = 8 * w + (lane >> 3);
+    const int cg = (lane & 7) ^ swz<__bf16>(r);
+    const int64_t off = (int64_t)(ws + c0 + r) * kHeadDim + 8 * cg;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(thb + off), (lds_void_t*)(th + 1024 * w), 16,
+                                     0, 0);
+    if (kLo)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(tlb + off), (lds_void_t*)(tl + 1024 * w),
+                                       16, 0, 0);
+  }
+  // acc += dZ chunk (this wave's 32 rows) x table chunk
+  template <bool EDGE>
+  __device__ __forceinline__ void mma_chunk(const float* zb, const char* th, const char* tl,
+                                            int c0, f32x16 (&acc)[2]) const {
+    const int r = 32 * w + l32;
+    const float* zr = zb + 32 * r;
+    const int sw = RowsK<T>::zswz(r);
+#pragma unroll
+    for (int ks = 0; ks < kRC / 16; ++ks) {
+      const int c = 16 * ks + 8 * hl;  // first of the lane's 8 columns
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(zr + 4 * ((c >> 2) ^ sw));
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(zr + 4 * (((c >> 2) + 1) ^ sw));
+      float z[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      if (EDGE) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = (c0 + c + j >= cb && c0 + c + j < ce) ? z[j] : 0.f;
+      }
+      bf16x8 ah, al;
+      split_bf16(z, ah, al);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const bf16x8 bh = tr.read(th, nt, ks);
+        acc[nt] = BF::mma(ah, bh, acc[nt]);
+        acc[nt] = BF::mma(al, bh, acc[nt]);
+        if (kLo) acc[nt] = BF::mma(ah, tr.read(tl, nt, ks), acc[nt]);
+      }
+    }
+  }
+  __device__ __forceinline__ void chunk(const float* zb, const char* th, const char* tl, int c0,
+                                        f32x16 (&acc)[2]) const {
+    if (c0 < cb || c0 + kRC > ce)
+      mma_chunk<true>(zb, th, tl, c0, acc);
+    else
+      mma_chunk<false>(zb, th, tl, c0, acc);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rows2_kernel(RowsArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit inputs");
+  constexpr int TT = kRC * kHeadDim * 2;  // bytes of one table part chunk
+  constexpr int TL = Rows2K<T>::kLo ? TT : 16;
+  __shared__ __align__(16) float sZ0[128 * kRC], sZ1[128 * kRC];
+  __shared__ __align__(16) char sH0[TT], sH1[TT], sL0[TL], sL1[TL];
+  const Geo g = a.geo;
+  const int N = g.N;
+  const int total = a.B * a.H * a.nblk;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int bh = lid / a.nblk, rb = lid - bh * a.nblk;
+  const int bb = bh / a.H, hh = bh - bb * a.H;
+  const int tid = threadIdx.x;
+  Rows2K<T> k;
+  k.w = wave_id();
+  k.lane = tid & 63;
+  k.hl = k.lane >> 5;
+  k.l32 = k.lane & 31;
+  k.N = N;
+  k.Wp = g.Wp;
+  k.i0 = rb * kBlockRows;
+  if (a.key_side) {
+    cols_k(g, rb, k.cb, k.ce);
+    k.ws = win_k(g, rb);
+  } else {
+    cols_q(g, rb, k.cb, k.ce);
+    k.ws = win_q(g, rb);
+  }
+  k.dzb = a.dz + (int64_t)bh * N * g.Wp;
+  k.thb = (const __bf16*)a.tunf + hh * a.tunf_hs;
+  k.tlb = a.tunf_lo ? (const __bf16*)a.tunf_lo + hh * a.tunf_hs : nullptr;
+  k.tr.init(k.lane);
+  const int w = k.w, hl = k.hl, l32 = k.l32;
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = k.i0 + 32 * w + res_row(hl, e);
+      acc[nt][e] = i < N ? a.part[((int64_t)bh * N + i) * kHeadDim + 32 * nt + l32] : 0.f;
+    }
+
+  const int cb0 = k.cb & ~(kRC - 1);
+  const int nch = k.ce > k.cb ? (k.ce - cb0 + kRC - 1) / kRC : 0;
+  if (nch > 0) k.issue(sZ0, sH0, sL0, cb0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  for (int n = 0; n < nch; n += 2) {
+    const int c0 = cb0 + n * kRC;
+    const bool more1 = n + 1 < nch;
+    if (more1) k.issue(sZ1, sH1, sL1, c0 + kRC);
+    k.chunk(sZ0, sH0, sL0, c0, acc);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (!more1) break;
+    if (n + 2 < nch) k.issue(sZ0, sH0, sL0, c0 + 2 * kRC);
+    k.chunk(sZ1, sH1, sL1, c0 + kRC, acc);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+
+  T* ob = (T*)a.out + bb * a.sout.b + hh * a.sout.h;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = k.i0 + 32 * w + res_row(hl, e);
+      if (i < N) ob[(int64_t)i * a.sout.n + 32 * nt + l32] = MT<T>::from_f(acc[nt][e]);
+    }
+}
+
 // Column contraction for a single-group window (every row's window starts
 // at unfolded row 0, so column u of every dZ row is unfolded row u).
 // Block (ut, s, ho): unfolded rows u in [64 ut, 64 ut + 64), all 64 d, over
@@ -188,13 +351,15 @@ __device__ __forceinline__ bool before(RowPos a, RowPos b) {
 template <typename T>
 struct ColsK {
   const float* dz;
-  const T* x;
-  Str sx;
+  const __bf16* x;   // X operand (bf16 inputs: X itself; fp16: its high part)
+  const __bf16* xl;  // low part of a split fp16 X, or null
+  Str sx;            // strides of x (a split X is [B*H][N][64])
   Geo g;
   int N, Wp, H, ho, u0, w, lane, hl, l32, key_side;
   bool shared, grp_on;
   RowPos end;  // end of this split's row range
   int cb0, ce0, ws0;  // the single window (ungrouped)
+  DLoader<__bf16> ldx;
 
   // live window of group grp: columns [cb, ce) hold entries, column c is
   // unfolded row ws + c
@@ -241,9 +406,12 @@ struct ColsK {
     return p;
   }
 
-  // rows [p.i, p.i + nrow) of segment p.seg into (zb, xb), asynchronously:
-  // zb[r][uo] holds dZ[i + r][u0 + uo - ws] (zero outside the stored row)
-  __device__ __forceinline__ void issue(float* zb, T* xb, RowPos p, int nrow) const {
+  // rows [p.i, p.i + nrow) of segment p.seg into zb (and, when WANT_X, the
+  // X rows into the 16-bit tiles xh, xl), asynchronously: zb[r][uo] holds
+  // dZ[i + r][u0 + uo - ws] (zero outside the stored row)
+  template <bool WANT_X>
+  __device__ __forceinline__ void issue(float* zb, char* xh, char* xlo, RowPos p,
+                                        int nrow) const {
     const int seg = p.seg, i = p.i;
     const int b_ = shared ? seg / H : seg;
     const int h_ = shared ? seg % H : ho;
@@ -281,18 +449,13 @@ struct ColsK {
         }
       }
     }
-    const T* xs = x + b_ * sx.b + h_ * sx.h;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = 2 * w + u;  // 8 rows of 64 elements per instruction
-      const int r = 8 * j + (lane >> 3);
-      char* dst = reinterpret_cast<char*>(xb) + 1024 * j;
-      if (r < nrow) {
-        __builtin_amdgcn_global_load_lds(
-            (glb_void_t*)(xs + (int64_t)(i + r) * sx.n + 8 * (lane & 7)), (lds_void_t*)dst, 16,
-            0, 0);
+    if constexpr (WANT_X) {
+      if (xl) {
+        const int64_t row0 = ((int64_t)(b_ * H + h_) * N + i) * kHeadDim;
+        ldx.load(xh, x + row0, nrow, lane);
+        ldx.load(xlo, xl + row0, nrow, lane);
       } else {
-        *reinterpret_cast<Chunk*>(dst + 16 * lane) = Chunk{{0u, 0u, 0u, 0u}};
+        ldx.load(xh, x + b_ * sx.b + h_ * sx.h + (int64_t)i * sx.n, nrow, lane);
       }
     }
   }
@@ -305,18 +468,44 @@ struct ColsK {
   }
 };
 
+// One 64-row chunk: acc (this wave's 32 u x 32 d tile) += dZ^T X on
+// v_mfma_f32_32x32x16_bf16, dZ split into two bf16 parts by each lane (its
+// 8 rows of a k-step at its column), X read from the 16-bit tile with
+// transpose reads; csum += the column's live values.  Without X only the
+// sums run.
 template <typename T, bool WANT_X>
 struct ColsMma {
-  // acc (this wave's 32 u x 32 d tile) and csum over the 64 rows of (zb, xb)
-  __device__ static __forceinline__ void run(const float* zb, const T* xb, int uo, int d, int hl,
+  using BF = MT<__bf16>;
+  static constexpr bool kLo = std::is_same<T, _Float16>::value;  // X split in two parts
+  __device__ static __forceinline__ void run(const float* zb, const char* xh, const char* xlo,
+                                             const TrReader<__bf16>& tr, int uo, int dh, int hl,
                                              bool uvalid, bool sums, f32x16& acc, float& csum) {
+    if constexpr (WANT_X) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        float z[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          z[j] = zb[(16 * ks + 8 * hl + j) * kCU + uo];
+          z[j] = uvalid ? z[j] : 0.f;
+        }
+        if (sums) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) csum += z[j];
+        }
+        bf16x8 ah, al;
+        split_bf16(z, ah, al);
+        const bf16x8 bh = tr.read(xh, dh, ks);
+        acc = BF::mma(ah, bh, acc);
+        acc = BF::mma(al, bh, acc);
+        if (kLo) acc = BF::mma(ah, tr.read(xlo, dh, ks), acc);
+      }
+    } else {
 #pragma unroll 8
-    for (int ks = 0; ks < 32; ++ks) {
-      const int r = 2 * ks + hl;
-      float av = zb[r * kCU + uo];
-      av = uvalid ? av : 0.f;
-      if (sums) csum += av;
-      if (WANT_X) acc = mma32(av, MT<T>::to_f(xb[r * kHeadDim + d]), acc);
+      for (int r = hl; r < 64; r += 2) {
+        const float av = zb[r * kCU + uo];
+        csum += uvalid ? av : 0.f;
+      }
     }
   }
 };
@@ -324,8 +513,10 @@ struct ColsMma {
 template <typename T, bool WANT_X>
 __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   static_assert(sizeof(T) == 2, "16-bit inputs");
+  constexpr int XB = WANT_X ? DTile<__bf16>::BYTES : 16;
+  constexpr int XL = (WANT_X && std::is_same<T, _Float16>::value) ? DTile<__bf16>::BYTES : 16;
   __shared__ __align__(16) float sZ0[64 * kCU], sZ1[64 * kCU];
-  __shared__ __align__(16) T sX0[64 * kHeadDim], sX1[64 * kHeadDim];
+  __shared__ __align__(16) char sX0[XB], sX1[XB], sL0[XL], sL1[XL];
   const Geo g = a.geo;
   const int N = g.N;
   const int nblk = gridDim.x * gridDim.y * gridDim.z;
@@ -345,14 +536,19 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   k.u0 = kCU * ut;
   k.key_side = a.key_side;
   k.shared = a.shared;
-  k.sx = a.sx;
   k.dz = a.dz;
-  k.x = (const T*)a.x;
+  k.xl = (const __bf16*)a.xl;
+  k.x = a.xl ? (const __bf16*)a.xh : (const __bf16*)a.x;
+  k.sx = a.sx;
+  if (WANT_X) k.ldx.init(a.xl ? kHeadDim : a.sx.n, k.w, k.lane);
+  TrReader<__bf16> tr;
+  tr.init(k.lane);
   const int w = k.w, hl = k.hl, l32 = k.l32;
   const int uo = 32 * (w & 1) + l32;  // this lane's unfolded row inside the block
   const int u = k.u0 + uo;
   const bool sums = w < 2;
-  const int d = 32 * (w >> 1) + l32;
+  const int dh = w >> 1;  // d half of this wave's tile
+  const int d = 32 * dh + l32;
 
   // this split's range of the flattened rows (segment-major)
   const int nseg = a.shared ? a.B * a.H : a.B;
@@ -370,14 +566,14 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   // live chunk n (rows [p.i, p.i + nrow) of segment p.seg) sits in buffer n & 1
   RowPos p = k.next_live(RowPos{(int)(f0 / N), (int)(f0 % N)});
   int nrow = before(p, k.end) ? k.chunk_rows(p) : 0;
-  if (nrow > 0) k.issue(sZ0, sX0, p, nrow);
+  if (nrow > 0) k.template issue<WANT_X>(sZ0, sX0, sL0, p, nrow);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   while (before(p, k.end)) {
     RowPos pn = k.next_live(k.advance(p, nrow));
     int nrow1 = before(pn, k.end) ? k.chunk_rows(pn) : 0;
-    if (nrow1 > 0) k.issue(sZ1, sX1, pn, nrow1);
-    ColsMma<T, WANT_X>::run(sZ0, sX0, uo, d, hl, k.live(p, uo), sums, acc, csum);
+    if (nrow1 > 0) k.template issue<WANT_X>(sZ1, sX1, sL1, pn, nrow1);
+    ColsMma<T, WANT_X>::run(sZ0, sX0, sL0, tr, uo, dh, hl, k.live(p, uo), sums, acc, csum);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     p = pn;
@@ -385,8 +581,8 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
     if (!before(p, k.end)) break;
     pn = k.next_live(k.advance(p, nrow));
     nrow1 = before(pn, k.end) ? k.chunk_rows(pn) : 0;
-    if (nrow1 > 0) k.issue(sZ0, sX0, pn, nrow1);
-    ColsMma<T, WANT_X>::run(sZ1, sX1, uo, d, hl, k.live(p, uo), sums, acc, csum);
+    if (nrow1 > 0) k.template issue<WANT_X>(sZ0, sX0, sL0, pn, nrow1);
+    ColsMma<T, WANT_X>::run(sZ1, sX1, sL1, tr, uo, dh, hl, k.live(p, uo), sums, acc, csum);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     p = pn;
@@ -404,8 +600,35 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   }
 }
 
-// Unfolded fp32 copy of a vector table: out[ho][u][:] = tab[ho][fold(u)][:]
-// for u < Runf, zero for the 32 padding rows after it.
+// fp16 X split exactly into two bf16 parts (hi + lo = x): an fp16 value has
+// 11 significant bits, bf16 keeps 8, and the remainder needs at most 3, all
+// inside bf16's exponent range.  xh, xl are [B*H][N][64].
+__global__ __launch_bounds__(kThreads) void xsplit_kernel(SplitArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 8 elements each
+  const int64_t n = (int64_t)a.B * a.H * a.N * (kHeadDim / 8);
+  if (idx >= n) return;
+  const int part = (int)(idx % (kHeadDim / 8));
+  const int64_t row = idx / (kHeadDim / 8);
+  const int i = (int)(row % a.N);
+  const int bh = (int)(row / a.N);
+  const int b = bh / a.H, h = bh - b * a.H;
+  const f16x8 v = *reinterpret_cast<const f16x8*>((const _Float16*)a.x + b * a.sx.b + h * a.sx.h +
+                                                  (int64_t)i * a.sx.n + 8 * part);
+  bf16x8 hi, lo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float f = (float)v[j];
+    hi[j] = (__bf16)f;
+    lo[j] = (__bf16)(f - (float)hi[j]);
+  }
+  *reinterpret_cast<bf16x8*>((__bf16*)a.xh + row * kHeadDim + 8 * part) = hi;
+  *reinterpret_cast<bf16x8*>((__bf16*)a.xl + row * kHeadDim + 8 * part) = lo;
+}
+
+// Unfolded copy of a vector table: out[ho][u][:] = tab[ho][fold(u)][:] for
+// u < Runf, zero for the 32 padding rows after it.  fp32 tables are copied as
+// they are; 16-bit tables become bf16 (fp16 ones split exactly into a high
+// and a low bf16 part, as in xsplit_kernel).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void tab_unfold_kernel(TabUnfoldArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -420,7 +643,13 @@ __global__ __launch_bounds__(kThreads) void tab_unfold_kernel(TabUnfoldArgs a) {
     const int r = a.fold ? a.fold[u] : u;
     v = MT<T>::to_f(((const T*)a.tab)[ho * a.tab_hs + (int64_t)r * kHeadDim + d]);
   }
-  a.out[idx] = v;
+  if constexpr (sizeof(T) == 4) {
+    ((float*)a.out)[idx] = v;
+  } else {
+    const __bf16 hi = (__bf16)v;
+    ((__bf16*)a.out)[idx] = hi;
+    if (a.out_lo) ((__bf16*)a.out_lo)[idx] = (__bf16)(v - (float)hi);
+  }
 }
 
 // Block (rt, s, ho): unfolded rows u in [32 rt, 32 rt + 32), all 64 d, over
@@ -552,9 +781,17 @@ hipError_t launch_rows(int dtype, const RowsArgs& a, hipStream_t st) {
   if (total <= 0) return hipSuccess;
   switch (dtype) {
     case 0: hipLaunchKernelGGL(rows_kernel<float>, dim3(total), dim3(kThreads), 0, st, a); break;
-    case 1: hipLaunchKernelGGL(rows_kernel<_Float16>, dim3(total), dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL(rows_kernel<__bf16>, dim3(total), dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(rows2_kernel<_Float16>, dim3(total), dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL(rows2_kernel<__bf16>, dim3(total), dim3(kThreads), 0, st, a); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_xsplit(const SplitArgs& a, hipStream_t st) {
+  const int64_t n = (int64_t)a.B * a.H * a.N * (kHeadDim / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(xsplit_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

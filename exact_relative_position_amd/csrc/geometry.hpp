@@ -166,7 +166,9 @@ struct RowTermArgs {     // padded backward row terms
 struct RowsArgs {       // dX = part + dZ . table   (per row)
   const float* part;    // [B*H][N][64] fp32
   const float* dz;      // [B*H][N][Wp]
-  const float* tunf;    // [Ho][Runf + 32][64] fp32 unfolded table
+  const void* tunf;     // [Ho][Runf + 32][64] unfolded table: fp32 for fp32 inputs,
+                        // else its bf16 high part
+  const void* tunf_lo;  // bf16 low part (fp16 tables), or null
   int64_t tunf_hs;      // 0 (shared) or (Runf + 32) * 64
   void* out;            // dtype
   Str sout;
@@ -180,13 +182,24 @@ struct TabUnfoldArgs {  // out[ho][u][:] = tab[ho][fold(u)][:], 32 zero rows aft
   const void* tab;
   int64_t tab_hs;
   const int32_t* fold;
-  float* out;
+  void* out;            // fp32 (fp32 tables) or the bf16 high part (16-bit tables)
+  void* out_lo;         // bf16 low part (fp16 tables), or null
   int Ho, Runf;
+};
+
+struct SplitArgs {      // xh + xl = x exactly (fp16 x split into two bf16 parts)
+  const void* x;        // [B, H, N, 64] with strides sx
+  Str sx;
+  void* xh;             // [B*H][N][64] bf16
+  void* xl;
+  int B, H, N;
 };
 
 struct ColsArgs {       // partial[s][ho][u][:] = sum_i dZ[i][u - ws] x_i[:]
   const float* dz;
-  const void* x;
+  const void* x;        // X in the input type (bf16: the MFMA operand as it is)
+  const void* xh;       // fp16 X split into bf16 parts, [B*H][N][64] (else null)
+  const void* xl;
   Str sx;
   float* part;          // [S][Ho][Rpad][64]
   float* partb;         // [S][Ho][Rpad] or null
