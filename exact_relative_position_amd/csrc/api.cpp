@@ -205,7 +205,7 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   auto splits = [&](int ho, bool shared) {
     const int64_t rows = (int64_t)(shared ? pl.B * pl.H : pl.B) * pl.N;
     const int64_t tiles = (int64_t)(pl.Rpad / 64) * ho;
-    int64_t want = (1024 + tiles - 1) / std::max<int64_t>(1, tiles);
+    int64_t want = (4096 + tiles - 1) / std::max<int64_t>(1, tiles);
     int64_t cap = std::max<int64_t>(1, rows / 512);
     return (int)std::max<int64_t>(1, std::min(want, cap));
   };
