@@ -8,8 +8,14 @@
 // queries and offsets correspond one to one); the saturated rows collect in
 // two on-chip sums per key.
 //
-// One workgroup = one (batch, head, 128-key block); 4 waves x 32 keys; inner
-// loop over 64-query tiles.  Orientation S = Q K^T: lane l owns key l % 32.
+// One workgroup = one (batch, head, 128-key block): 4 waves x 32 keys, or,
+// under a causal mask (16-bit inputs), 8 waves in two groups of 4 x 32 keys
+// that take alternate 64-query tiles (each group with its own LDS buffers) and
+// sum their accumulators through LDS at the end: the early key blocks of a
+// causal problem hold most of the work, and splitting their query range
+// halves the longest block.  (Without the mask two independent 4-wave blocks
+// per CU overlap MFMA and vector work better than one 8-wave block whose
+// groups share every barrier.)  Orientation S = Q K^T: lane l owns key l % 32.
 // Q and dO tiles go into LDS row-major by direct loads: they are the
 // operands of S = Q K^T and dP = dO V^T (contracted over d) as they are, and
 // of dV^T = dO^T P and dK^T = Q^T dS (contracted over the queries) through
@@ -32,9 +38,27 @@ constexpr int kStagePitchK = 36;  // floats per staged key row (16-byte aligned,
 // few but each holds many interior entries.
 constexpr int kStageMinWK = 512;
 
-// STAGE: band dZ^K stores go through an LDS staging area.
-template <typename T, bool STAGE>
+// Groups of 4 waves per workgroup (see the header comment).
+template <typename T, bool GRP>
+constexpr int key_groups() {
+  return (GRP && sizeof(T) == 2) ? 2 : 1;
+}
+
+template <typename T, bool GRP>
+constexpr int key_threads() {
+  return kThreads * key_groups<T, GRP>();
+}
+// blocks per CU for 2 waves per SIMD (fp32: 1 block)
+template <typename T, bool GRP>
+constexpr int key_blocks_per_cu() {
+  return (key_groups<T, GRP>() == 1 && sizeof(T) == 2) ? 2 : 1;
+}
+
+// STAGE: band dZ^K stores go through an LDS staging area; GRP: two groups
+// of waves split the query tiles.
+template <typename T, bool STAGE, bool GRP>
 struct BwdK {
+  static constexpr int kGroups = key_groups<T, GRP>();
   using M = MT<T>;
   using frag = typename M::frag;
   static constexpr bool kHalf = sizeof(T) == 2;
@@ -45,12 +69,14 @@ struct BwdK {
 
   // LDS buffers, two of each (separate arrays, so that the compiler can tell
   // the asynchronous loads into one buffer from the reads of the other)
-  char* sQ[2];     // Q rows
+  char* sQ[2];     // Q rows (group 0's buffers; this group's start goff bytes in)
   char* sO[2];     // dO rows
+  int goff;        // byte offset of this group's Q / dO buffers
   float* sR[2];    // [4][kTile] per-query seeds of the tile (see RowTermArgs)
 
   Geo g;
-  int w, lane, hl, l32, j0b, jw0, jk, sig, ntq, N, kv_end, wsk;
+  int w, lane, hl, l32, j0b, jw0, jk, sig, ntq, N, kv_end, wsk;  // w: wave within its group
+  int grp;                                                        // this wave's group
   bool has_zq, has_zk, has_b;
   float off_lo, off_hi, sc2, tau;
   const T* Qb;
@@ -77,8 +103,8 @@ struct BwdK {
   template <int BUF>
   __device__ __forceinline__ void issue(int t) {
     const int q0 = t * kTile;
-    ldQ.load(sQ[BUF], Qb + (int64_t)q0 * sq, N - q0, lane);
-    ldO.load(sO[BUF], Ob + (int64_t)q0 * so, N - q0, lane);
+    ldQ.load(sQ[BUF] + goff, Qb + (int64_t)q0 * sq, N - q0, lane);
+    ldO.load(sO[BUF] + goff, Ob + (int64_t)q0 * so, N - q0, lane);
     // wave w brings seed vector w of the tile's 64 queries
     dword_direct((char*)(sR[BUF] + w * kTile), seeds + w * seed_stride + q0 + lane, true, lane);
   }
@@ -88,7 +114,7 @@ struct BwdK {
     if constexpr (kHalf) {
       return *reinterpret_cast<const frag*>(tile + rofs[ks] + st * 32 * ROWB);
     } else {
-      return dfrag<T>(tile, 32 * st + sig, KS * ks + E * hl);
+      return dfrag<T>(tile + goff, 32 * st + sig, KS * ks + E * hl);
     }
   }
   // Transposed fragment (d row 32 dt + l32, query chunk column c4) of Q^T or
@@ -97,7 +123,7 @@ struct BwdK {
     if constexpr (kHalf) {
       return tr.read(rowtile, dt, c4);
     } else {
-      return dfrag_t32(rowtile, 32 * dt + l32, KS * c4 + E * hl);
+      return dfrag_t32(rowtile + goff, 32 * dt + l32, KS * c4 + E * hl);
     }
   }
 
@@ -259,57 +285,72 @@ struct BwdK {
   }
 
   // Query tile t from buffer BUF with the loads of tile t + 1 in flight;
-  // tiles before tA have all offsets >= hi, tiles from tB on all <= lo.
+  // Query tile t (none once t >= ntq) from buffer BUF with the loads of the
+  // group's next tile in flight; tiles before tA have all offsets >= hi,
+  // tiles from tB on all <= lo.
   template <int BUF>
   __device__ __forceinline__ void step(int t, int tA, int tB) {
-    if (t + 1 < ntq) issue<BUF ^ 1>(t + 1);
-    // tiles with masked entries also take the band body
-    const int qt0 = t * kTile;
-    const bool masked = (qt0 + kTile > N) || (j0b + kBlockRows > kv_end) ||
-                        (g.causal && j0b + kBlockRows - 1 > qt0);
-    if ((t >= tA && t < tB) || masked)
-      tile<true, BUF>(t, KIND_BAND);
-    else
-      tile<false, BUF>(t, t < tA ? KIND_HI : KIND_LO);
+    if (t + kGroups < ntq) issue<BUF ^ 1>(t + kGroups);
+    if (t < ntq) {
+      // tiles with masked entries also take the band body
+      const int qt0 = t * kTile;
+      const bool masked = (qt0 + kTile > N) || (j0b + kBlockRows > kv_end) ||
+                          (g.causal && j0b + kBlockRows - 1 > qt0);
+      if ((t >= tA && t < tB) || masked)
+        tile<true, BUF>(t, KIND_BAND);
+      else
+        tile<false, BUF>(t, t < tA ? KIND_HI : KIND_LO);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
-  // the tile t_begin goes to buffer 0; tile t to buffer (t - t_begin) & 1
+  // Group grp takes tiles t_begin + grp, t_begin + grp + kGroups, ...; every
+  // group runs the same number of steps (one workgroup barrier each), step m
+  // in buffer m & 1.
   __device__ __forceinline__ void run(int t_begin, int tA, int tB) {
-    if (t_begin < ntq) issue<0>(t_begin);
+    const int t0 = t_begin + grp;
+    if (t0 < ntq) issue<0>(t0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    for (int t = t_begin; t < ntq; t += 2) {
-      step<0>(t, tA, tB);
-      if (t + 1 < ntq) step<1>(t + 1, tA, tB);
+    const int nsteps = ntq > t_begin ? (ntq - t_begin + kGroups - 1) / kGroups : 0;
+    for (int m = 0; m < nsteps; m += 2) {
+      step<0>(t0 + kGroups * m, tA, tB);
+      if (m + 1 < nsteps) step<1>(t0 + kGroups * (m + 1), tA, tB);
     }
   }
 };
 
 // ZQ: whether the query-side relation term is present (compile-time switch);
-// STAGE: band dZ^K stores staged through LDS.
-template <typename T, bool ZQ, bool STAGE>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_k_kernel(AttnArgs a) {
+// STAGE: band dZ^K stores staged through LDS; GRP: grouped workgroup.
+template <typename T, bool ZQ, bool STAGE, bool GRP>
+__global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>()))
+    void bwd_k_kernel(AttnArgs a) {
   using M = MT<T>;
-  using K = BwdK<T, STAGE>;
+  using K = BwdK<T, STAGE, GRP>;
   constexpr int TB = DTile<T>::BYTES;
-  __shared__ __align__(16) char sQ0[TB], sQ1[TB], sO0[TB], sO1[TB];
-  __shared__ __align__(16) float sR0[4 * kTile], sR1[4 * kTile];
-  __shared__ __align__(16) float sSt[STAGE ? 4 * 32 * kStagePitchK : 4];
+  constexpr int G = K::kGroups;
+  __shared__ __align__(16) char sQ0[G * TB], sQ1[G * TB], sO0[G * TB], sO1[G * TB];
+  __shared__ __align__(16) float sR0[G * 4 * kTile], sR1[G * 4 * kTile];
+  __shared__ __align__(16) float sSt[STAGE ? 4 * G * 32 * kStagePitchK : 4];
 
+  const int tid = threadIdx.x, wall = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int grp = G == 2 ? wall >> 2 : 0, w = wall & 3;
   K k;
+  k.grp = grp;
+  // the group offset goes into the per-lane fragment offsets, so that the
+  // LDS reads keep compile-time buffer bases
+  k.goff = grp * TB;
   k.sQ[0] = sQ0;
   k.sQ[1] = sQ1;
   k.sO[0] = sO0;
   k.sO[1] = sO1;
-  k.sR[0] = sR0;
-  k.sR[1] = sR1;
+  k.sR[0] = sR0 + grp * 4 * kTile;
+  k.sR[1] = sR1 + grp * 4 * kTile;
   k.g = a.geo;
   const Geo& g = k.g;
   const int N = g.N;
   k.N = N;
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   k.w = w;
   k.lane = lane;
   k.hl = hl;
@@ -345,10 +386,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_k_kernel
   k.ldQ.init(a.sq.n, w, lane);
   k.ldO.init(a.sdo.n, w, lane);
   if constexpr (K::kHalf) {
-    k.tr.init(lane);
+    k.tr.init(lane, k.goff);
     const int sg = sigma<T>(l32);
 #pragma unroll
-    for (int ks = 0; ks < K::NSD; ++ks) k.rofs[ks] = dt_off<T>(sg, K::KS * ks + K::E * hl);
+    for (int ks = 0; ks < K::NSD; ++ks)
+      k.rofs[ks] = k.goff + dt_off<T>(sg, K::KS * ks + K::E * hl);
   }
   k.seed_stride = (int64_t)a.B * a.H * a.Np;
   k.seeds = a.kseed + (int64_t)bh * a.Np;
@@ -358,7 +400,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_k_kernel
   k.zk_row = k.has_zk ? a.zk + ((int64_t)bh * N + imin(jk, N - 1)) * g.Wp : nullptr;
   k.dz_row = k.has_zk ? a.dzk + ((int64_t)bh * N + jk) * g.Wp : nullptr;
   k.dz_w = k.has_zk ? a.dzk + ((int64_t)bh * N + jw0) * g.Wp : nullptr;
-  k.stage = STAGE ? sSt + w * 32 * kStagePitchK : sSt;
+  k.stage = STAGE ? sSt + wall * 32 * kStagePitchK : sSt;
   k.sc2 = a.scale2;
   k.tau = a.tau;
 
@@ -400,6 +442,40 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_k_kernel
   const int tB = imin(ntq, imax(tA, ceil_div_k(j0b + kBlockRows - 1 - g.lo, kTile)));
 
   k.run(t_begin, tA, tB);
+
+  if constexpr (G == 2) {
+    // group 1 hands dV, dK and the two sums to group 0 (lane-contiguous, in
+    // the Q / dO buffers, which every wave is done with after the last
+    // barrier); group 0 adds them and writes everything
+    const int t = tid & (4 * 64 - 1);
+    float* x0 = reinterpret_cast<float*>(sQ0);
+    float* x1 = reinterpret_cast<float*>(sQ1);
+    float* x2 = reinterpret_cast<float*>(sO0);
+    float* x3 = reinterpret_cast<float*>(sO1);
+    static_assert(G * TB >= 16 * 256 * 4, "combine buffers");
+    if (grp == 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x0[e * 256 + t] = k.dv[0][e];
+        x1[e * 256 + t] = k.dv[1][e];
+        x2[e * 256 + t] = k.dk[0][e];
+        x3[e * 256 + t] = k.dk[1][e];
+      }
+      sR0[t] = k.acc_lo;
+      sR0[256 + t] = k.acc_hi;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      k.dv[0][e] += x0[e * 256 + t];
+      k.dv[1][e] += x1[e * 256 + t];
+      k.dk[0][e] += x2[e * 256 + t];
+      k.dk[1][e] += x3[e * 256 + t];
+    }
+    k.acc_lo += sR0[t];
+    k.acc_hi += sR0[256 + t];
+  }
 
   if (jk < N) {
     T* vrow = (T*)a.dv + bb * a.sdv.b + hh * a.sdv.h + (int64_t)jk * a.sdv.n;
@@ -468,19 +544,26 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_k_kernel
   }
 }
 
-template <typename T>
-static hipError_t launch_bwd_k_t(const AttnArgs& a, hipStream_t st) {
+template <typename T, bool GRP>
+static hipError_t launch_bwd_k_g(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
   const bool zq = a.flags & F_ZQ, stage = (a.flags & F_ZK) && a.geo.W >= kStageMinWK;
+  const int nt = kThreads * key_groups<T, GRP>();
   if (zq && stage)
-    hipLaunchKernelGGL((bwd_k_kernel<T, true, true>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_k_kernel<T, true, true, GRP>), dim3(total), dim3(nt), 0, st, a);
   else if (zq)
-    hipLaunchKernelGGL((bwd_k_kernel<T, true, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_k_kernel<T, true, false, GRP>), dim3(total), dim3(nt), 0, st, a);
   else if (stage)
-    hipLaunchKernelGGL((bwd_k_kernel<T, false, true>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_k_kernel<T, false, true, GRP>), dim3(total), dim3(nt), 0, st, a);
   else
-    hipLaunchKernelGGL((bwd_k_kernel<T, false, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_k_kernel<T, false, false, GRP>), dim3(total), dim3(nt), 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_bwd_k_t(const AttnArgs& a, hipStream_t st) {
+  if (a.geo.causal && sizeof(T) == 2) return launch_bwd_k_g<T, true>(a, st);
+  return launch_bwd_k_g<T, false>(a, st);
 }
 
 hipError_t launch_bwd_k(int dtype, const AttnArgs& a, hipStream_t st) {

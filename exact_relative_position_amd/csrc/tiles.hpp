@@ -232,13 +232,15 @@ struct TrReader {
   typedef short s4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s4 lds_s4;
   int o[2][2];  // byte offset of read r for column block dt, k-step 0
-  __device__ __forceinline__ void init(int lane) {
+  // base: byte offset added to every read (a tile placed inside a larger buffer)
+  __device__ __forceinline__ void init(int lane, int base = 0) {
     const int i = lane & 15, grp = lane >> 4, h = lane >> 5;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
-        o[r][dt] = dt_off<T>(8 * h + 4 * r + (i >> 2), 32 * dt + 16 * (grp & 1) + 4 * (i & 3));
+        o[r][dt] =
+            base + dt_off<T>(8 * h + 4 * r + (i >> 2), 32 * dt + 16 * (grp & 1) + 4 * (i & 3));
   }
   // operand for column block dt and k-step c (tile rows 16 c .. 16 c + 15)
   __device__ __forceinline__ frag read(const char* lds, int dt, int c) const {
