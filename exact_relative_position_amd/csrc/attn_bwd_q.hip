@@ -26,9 +26,29 @@ constexpr int kStagePitch = 36;  // floats per staged row (16-byte aligned, bank
 constexpr int kStageFloats = 32 * kStagePitch;
 static_assert(kStageFloats >= RowStage::kFloats, "stage area holds the Z^Q rows");
 
-// STAGE: band stores go through an LDS staging area (chosen for wide bands)
-template <typename T, bool STAGE>
+// Groups of 4 waves per workgroup: under a causal mask (16-bit inputs) two
+// groups take alternate key tiles of the block and sum their dQ and
+// saturated-row sums through LDS at the end, which halves the longest
+// (last) query blocks; otherwise one.
+template <typename T, bool GRP>
+constexpr int query_groups() {
+  return (GRP && sizeof(T) == 2) ? 2 : 1;
+}
+template <typename T, bool GRP>
+constexpr int query_threads() {
+  return kThreads * query_groups<T, GRP>();
+}
+// blocks per CU for 2 waves per SIMD (fp32: 1 block)
+template <typename T, bool GRP>
+constexpr int query_blocks_per_cu() {
+  return (query_groups<T, GRP>() == 1 && sizeof(T) == 2) ? 2 : 1;
+}
+
+// STAGE: band stores go through an LDS staging area (chosen for wide bands);
+// GRP: two groups of waves split the key tiles.
+template <typename T, bool STAGE, bool GRP>
 struct BwdQ {
+  static constexpr int kGroups = query_groups<T, GRP>();
   using M = MT<T>;
   using frag = typename M::frag;
   static constexpr bool kHalf = sizeof(T) == 2;
@@ -38,9 +58,10 @@ struct BwdQ {
 
   // LDS buffers, two of each (separate arrays, so that the compiler can tell
   // the asynchronous loads into one buffer from the reads of the other)
-  char* sK[2];     // K rows
+  char* sK[2];     // K rows (group 0's buffers; this group's start goff bytes in)
   char* sV[2];     // V rows
-  float* sZK[2];   // saturated Z^K scalars [2][kTile]
+  float* sZK[2];   // saturated Z^K scalars [group][2][kTile]
+  int grp, goff;   // this wave's group, byte offset of its K / V buffers
 
   Geo g;
   QCtx c;
@@ -81,11 +102,11 @@ struct BwdQ {
   template <int BUF>
   __device__ __forceinline__ void issue(int t) {
     const int j0 = t * kTile;
-    ldK.load(sK[BUF], Kb + (int64_t)j0 * sk, N - j0, lane);
-    ldV.load(sV[BUF], Vb + (int64_t)j0 * sv, N - j0, lane);
+    ldK.load(sK[BUF] + goff, Kb + (int64_t)j0 * sk, N - j0, lane);
+    ldV.load(sV[BUF] + goff, Vb + (int64_t)j0 * sv, N - j0, lane);
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
-      dword_direct((char*)(sZK[BUF] + w * kTile), p, p != nullptr, lane);
+      dword_direct((char*)(sZK[BUF] + (2 * grp + w) * kTile), p, p != nullptr, lane);
     }
   }
 
@@ -133,7 +154,7 @@ struct BwdQ {
     const bool needmask = BAND && ((j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0));
     const char* tK = sK[BUF];
     const char* tV = sV[BUF];
-    const float* zk = sZK[BUF];
+    const float* zk = sZK[BUF] + 2 * grp * kTile;
     const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
     const float off = cst * sc2 - lse2;
 #pragma unroll
@@ -187,7 +208,7 @@ struct BwdQ {
         }
       }
       if (BAND && STAGE && kind == KIND_BAND && stage_next) {
-        if (st == 0) stage_zq<0>(t + 1); else stage_zq<1>(t + 1);
+        if (st == 0) stage_zq<0>(t + kGroups); else stage_zq<1>(t + kGroups);
       }
       frag sf[KPS];
 #pragma unroll
@@ -207,57 +228,74 @@ struct BwdQ {
     }
   }
 
-  // Tile t from buffer BUF with the loads of tile t + 1 in flight; tiles
-  // [0, t1) are left-saturated, [t2, nkt) right-saturated.
+  // Key tile t (none once t >= nkt) from buffer BUF with the loads of the
+  // group's next tile in flight; tiles [0, t1) are left-saturated, [t2, nkt)
+  // right-saturated.
   template <int BUF>
   __device__ __forceinline__ void step(int t, int t1, int t2) {
-    if (t + 1 < nkt) issue<BUF ^ 1>(t + 1);
-    // Z^Q rows of tile t + 1: staged now when tile t leaves the areas free,
-    // else from tile t's band path
-    const bool bn = band_here(t + 1), bc = band_here(t);
+    const int tn = t + kGroups;
+    if (tn < nkt) issue<BUF ^ 1>(tn);
+    // (one group: t < nkt always holds)
+    // Z^Q rows of the group's next tile: staged now when tile t leaves the
+    // areas free, else from tile t's band path
+    const bool bn = band_here(tn), bc = band_here(t);
     if (bn && !bc) {
-      stage_zq<0>(t + 1);
-      stage_zq<1>(t + 1);
+      stage_zq<0>(tn);
+      stage_zq<1>(tn);
     }
-    // tiles with masked entries also take the band body
-    const int j0 = t * kTile;
-    const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
-    if ((t >= t1 && t < t2) || masked)
-      tile<true, BUF>(t, KIND_BAND, bn && bc);
-    else
-      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI, false);
+    if (kGroups == 1 || t < nkt) {
+      // tiles with masked entries also take the band body
+      const int j0 = t * kTile;
+      const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
+      if ((t >= t1 && t < t2) || masked)
+        tile<true, BUF>(t, KIND_BAND, bn && bc);
+      else
+        tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI, false);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
+  // Group grp takes key tiles grp, grp + kGroups, ...; every group runs the
+  // same number of steps (one workgroup barrier each), step m in buffer m & 1.
   __device__ __forceinline__ void run(int t1, int t2) {
-    if (nkt > 0) issue<0>(0);
-    if (band_here(0)) {
-      stage_zq<0>(0);
-      stage_zq<1>(0);
+    const int t0 = grp;
+    if (t0 < nkt) issue<0>(t0);
+    if (band_here(t0)) {
+      stage_zq<0>(t0);
+      stage_zq<1>(t0);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    for (int t = 0; t < nkt; t += 2) {
-      step<0>(t, t1, t2);
-      if (t + 1 < nkt) step<1>(t + 1, t1, t2);
+    const int nsteps = (nkt + kGroups - 1) / kGroups;
+    for (int m = 0; m < nsteps; m += 2) {
+      step<0>(t0 + kGroups * m, t1, t2);
+      if (m + 1 < nsteps) step<1>(t0 + kGroups * (m + 1), t1, t2);
     }
   }
 };
 
 // ZK: whether the key-side relation term is present (compile-time switch);
-// STAGE: band stores staged through LDS.
-template <typename T, bool ZK, bool STAGE>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel(AttnArgs a) {
+// STAGE: band stores staged through LDS; GRP: grouped workgroup.
+template <typename T, bool ZK, bool STAGE, bool GRP>
+__global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, GRP>()))
+    void bwd_q_kernel(AttnArgs a) {
   using M = MT<T>;
-  using B = BwdQ<T, STAGE>;
+  using B = BwdQ<T, STAGE, GRP>;
   constexpr int TB = DTile<T>::BYTES;
-  __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
-  __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
-  constexpr int kSt = STAGE ? 4 * kStageFloats : 4;
+  constexpr int G = B::kGroups;
+  __shared__ __align__(16) char sK0[G * TB], sK1[G * TB], sV0[G * TB], sV1[G * TB];
+  __shared__ __align__(16) float sZK0[G * 2 * kTile], sZK1[G * 2 * kTile];
+  constexpr int kSt = STAGE ? 4 * G * kStageFloats : 4;
   __shared__ __align__(16) float sSt0[kSt], sSt1[kSt];
 
+  const int tid = threadIdx.x, wall = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int grp = G == 2 ? wall >> 2 : 0, w = wall & 3;
   B q;
+  q.grp = grp;
+  // the group offset goes into the per-lane fragment offsets, so that the
+  // LDS reads keep compile-time buffer bases
+  q.goff = grp * TB;
   q.sK[0] = sK0;
   q.sK[1] = sK1;
   q.sV[0] = sV0;
@@ -268,7 +306,6 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   const Geo& g = q.g;
   const int N = g.N;
   q.N = N;
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   q.w = w;
   q.lane = lane;
   q.hl = hl;
@@ -299,10 +336,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   q.ldK.init(a.sk.n, w, lane);
   q.ldV.init(a.sv.n, w, lane);
   if constexpr (B::kHalf) {
-    q.tr.init(lane);
+    q.tr.init(lane, q.goff);
     const int sig = sigma<T>(l32);
 #pragma unroll
-    for (int ks = 0; ks < B::NSD; ++ks) q.kofs[ks] = dt_off<T>(sig, B::KS * ks + B::E * hl);
+    for (int ks = 0; ks < B::NSD; ++ks)
+      q.kofs[ks] = q.goff + dt_off<T>(sig, B::KS * ks + B::E * hl);
   }
 
   QCtx& c = q.c;
@@ -336,8 +374,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   }
   q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
   q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;
-  q.zs.buf[0] = STAGE ? sSt0 + w * kStageFloats : sSt0;
-  q.zs.buf[1] = STAGE ? sSt1 + w * kStageFloats : sSt1;
+  q.zs.buf[0] = STAGE ? sSt0 + wall * kStageFloats : sSt0;
+  q.zs.buf[1] = STAGE ? sSt1 + wall * kStageFloats : sSt1;
   q.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, -1, lane);
   q.dq[0] = zero16();
   q.dq[1] = zero16();
@@ -348,6 +386,34 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   const int t2 = imin(nkt, imax(t1, ceil_div_q(g.hi + i0 + kBlockRows - 1, kTile)));
 
   q.run(t1, t2);
+
+  if constexpr (G == 2) {
+    // group 1 hands dQ and the two sums to group 0 (lane-contiguous, in the
+    // K / V buffers, which every wave is done with after the last barrier)
+    const int t = tid & (4 * 64 - 1);
+    float* x0 = reinterpret_cast<float*>(sK0);
+    float* x1 = reinterpret_cast<float*>(sK1);
+    float* x2 = reinterpret_cast<float*>(sV0);
+    static_assert(G * TB >= 16 * 256 * 4, "combine buffers");
+    if (grp == 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x0[e * 256 + t] = q.dq[0][e];
+        x1[e * 256 + t] = q.dq[1][e];
+      }
+      x2[t] = q.acc_lo;
+      x2[256 + t] = q.acc_hi;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      q.dq[0][e] += x0[e * 256 + t];
+      q.dq[1][e] += x1[e * 256 + t];
+    }
+    q.acc_lo += x2[t];
+    q.acc_hi += x2[256 + t];
+  }
 
   if (iq < N) {
     // dQ = tau * dS K  (plus dZ^Q aQ added by the contraction when aQ is present)
@@ -402,19 +468,26 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_q_kernel
   }
 }
 
-template <typename T>
-static hipError_t launch_bwd_q_t(const AttnArgs& a, hipStream_t st) {
+template <typename T, bool GRP>
+static hipError_t launch_bwd_q_g(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
   const bool zk = a.flags & F_ZK, stage = a.geo.W >= kStageMinW;
+  const int nt = query_threads<T, GRP>();
   if (zk && stage)
-    hipLaunchKernelGGL((bwd_q_kernel<T, true, true>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<T, true, true, GRP>), dim3(total), dim3(nt), 0, st, a);
   else if (zk)
-    hipLaunchKernelGGL((bwd_q_kernel<T, true, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<T, true, false, GRP>), dim3(total), dim3(nt), 0, st, a);
   else if (stage)
-    hipLaunchKernelGGL((bwd_q_kernel<T, false, true>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<T, false, true, GRP>), dim3(total), dim3(nt), 0, st, a);
   else
-    hipLaunchKernelGGL((bwd_q_kernel<T, false, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<T, false, false, GRP>), dim3(total), dim3(nt), 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_bwd_q_t(const AttnArgs& a, hipStream_t st) {
+  if (a.geo.causal && sizeof(T) == 2) return launch_bwd_q_g<T, true>(a, st);
+  return launch_bwd_q_g<T, false>(a, st);
 }
 
 hipError_t launch_bwd_q(int dtype, const AttnArgs& a, hipStream_t st) {
