@@ -57,6 +57,15 @@ SMALL = [
     Workload("n1_bf16", 1, 1, 1, 64, "bf16", IDENTITY, 1 / 8, has_aq=True, has_b=True),
     Workload("n129_causal_f16", 1, 1, 129, 64, "f16", IDENTITY, 1 / 8, has_aq=True, has_b=True,
              causal=True, b_std=0.02),
+    # windows of >= 1024 columns: Z^Q rows staged in LDS by the forward and the
+    # query pass, band stores staged; causal: grouped query / key passes
+    Workload("wide_band_causal_bf16", 1, 2, 1000, 64, "bf16", IDENTITY, 1 / 8, has_aq=True,
+             has_b=True, causal=True, b_std=0.02),
+    Workload("wide_band_all_terms_f16", 1, 1, 1100, 64, "f16", IDENTITY, 1 / 8, has_aq=True,
+             has_ak=True, has_b=True, b_std=0.1),
+    Workload("wide_band_causal_keypad_f16", 2, 1, 1050, 64, "f16",
+             {"kind": "truncated", "lo": -1040, "hi": 1030}, 1 / 8, has_aq=True, has_ak=True,
+             causal=True, key_padding=True, pad_frac=0.2),
 ]
 
 
