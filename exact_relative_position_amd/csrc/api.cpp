@@ -423,6 +423,21 @@ relpos_status project(const Plan& pl, const relpos_problem* prob, const void* Q,
   return RELPOS_OK;
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask* mask,
                    const void* Q, const void* K, const void* V) {
   AttnArgs a{};
@@ -448,6 +463,12 @@ AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask
   a.bunf_hs = pl.b_hs == 0 ? 0 : pl.Runf;
   a.nblk = pl.nblk;
   a.Np = pl.Np;
+  // Causal 16-bit launches whose blocks all fit on the device at once (two
+  // per CU) split each block's tiles between two wave groups: the longest
+  // block then bounds the pass, and splitting halves it.  With more blocks
+  // the longest-first order already balances the CUs.
+  a.split = pl.geo.causal && pl.esz == 2 &&
+            (int64_t)pl.B * pl.H * pl.nblk <= 2 * (int64_t)device_cus();
   return a;
 }
 

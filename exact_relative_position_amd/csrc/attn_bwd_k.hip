@@ -9,17 +9,15 @@
 // two on-chip sums per key.
 //
 // One workgroup = one (batch, head, 128-key block): 4 waves x 32 keys, or,
-// under a causal mask (16-bit inputs), 8 waves in two groups of 4 x 32 keys
-// that take alternate 64-query tiles (each group with its own LDS buffers) and
-// sum their accumulators through LDS at the end: the early key blocks of a
-// causal problem hold most of the work, and splitting their query range
-// halves the longest block.  (Without the mask two independent 4-wave blocks
-// per CU overlap MFMA and vector work better than one 8-wave block whose
-// groups share every barrier.)  Orientation S = Q K^T: lane l owns key l % 32.
-// Q and dO tiles go into LDS row-major by direct loads: they are the
-// operands of S = Q K^T and dP = dO V^T (contracted over d) as they are, and
-// of dV^T = dO^T P and dK^T = Q^T dS (contracted over the queries) through
-// ds_read_b64_tr_b16 transpose reads; the query loop runs in three segments.
+// for a causal 16-bit launch whose blocks all fit on the device at once, 8
+// waves in two groups of 4 x 32 keys that take alternate 64-query tiles (each
+// group with its own LDS buffers) and sum their accumulators through LDS at
+// the end: the early key blocks of a causal problem hold most of the work, so
+// the longest block bounds such a launch, and splitting its query range halves
+// it.  (With more blocks the longest-first order balances the CUs, and two
+// independent 4-wave blocks per CU overlap MFMA and vector work better than
+// one 8-wave block whose groups share every barrier.)  Orientation
+// S = Q K^T: lane l owns key l % 32.
 #include "qside.hpp"
 
 namespace relpos {
@@ -356,9 +354,8 @@ __global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>
   k.hl = hl;
   k.l32 = l32;
   const int total = a.B * a.H * a.nblk;
-  const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / a.nblk;
-  const int kb = lid - bh * a.nblk;  // causal: early key blocks have the most queries
+  int bh, kb;  // causal: early key blocks have the most queries (first)
+  block_of(blockIdx.x, total, a.nblk, g.causal, bh, kb);
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int j0b = kb * kBlockRows, jw0 = j0b + 32 * w, jk = jw0 + l32;
   k.j0b = j0b;
@@ -562,7 +559,7 @@ static hipError_t launch_bwd_k_g(const AttnArgs& a, hipStream_t st) {
 
 template <typename T>
 static hipError_t launch_bwd_k_t(const AttnArgs& a, hipStream_t st) {
-  if (a.geo.causal && sizeof(T) == 2) return launch_bwd_k_g<T, true>(a, st);
+  if (a.split && sizeof(T) == 2) return launch_bwd_k_g<T, true>(a, st);
   return launch_bwd_k_g<T, false>(a, st);
 }
 

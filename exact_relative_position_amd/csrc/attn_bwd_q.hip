@@ -26,7 +26,8 @@ constexpr int kStagePitch = 36;  // floats per staged row (16-byte aligned, bank
 constexpr int kStageFloats = 32 * kStagePitch;
 static_assert(kStageFloats >= RowStage::kFloats, "stage area holds the Z^Q rows");
 
-// Groups of 4 waves per workgroup: under a causal mask (16-bit inputs) two
+// Groups of 4 waves per workgroup: for a causal 16-bit launch whose blocks all
+// fit on the device at once (the longest block bounds it) two
 // groups take alternate key tiles of the block and sum their dQ and
 // saturated-row sums through LDS at the end, which halves the longest
 // (last) query blocks; otherwise one.
@@ -311,10 +312,9 @@ __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, 
   q.hl = hl;
   q.l32 = l32;
   const int total = a.B * a.H * a.nblk;
-  const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / a.nblk;
-  int qb = lid - bh * a.nblk;
-  if (g.causal) qb = a.nblk - 1 - qb;
+  int bh, qb;
+  block_of(blockIdx.x, total, a.nblk, g.causal, bh, qb);
+  if (g.causal) qb = a.nblk - 1 - qb;  // longest rows first
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
   q.i0 = i0;
@@ -486,7 +486,7 @@ static hipError_t launch_bwd_q_g(const AttnArgs& a, hipStream_t st) {
 
 template <typename T>
 static hipError_t launch_bwd_q_t(const AttnArgs& a, hipStream_t st) {
-  if (a.geo.causal && sizeof(T) == 2) return launch_bwd_q_g<T, true>(a, st);
+  if (a.split && sizeof(T) == 2) return launch_bwd_q_g<T, true>(a, st);
   return launch_bwd_q_g<T, false>(a, st);
 }
 

@@ -31,33 +31,52 @@ namespace relpos {
 __device__ inline int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 __device__ inline int ceil_div(int a, int b) { return -floor_div(-a, b); }
 
+// Groups of 4 waves per workgroup: for a causal 16-bit launch whose blocks all
+// fit on the device at once (the longest block bounds it) two
+// groups take alternate key tiles of the 128-query block and merge their
+// softmax states through LDS at the end, which halves the longest (last)
+// blocks; otherwise one.
+template <typename T, bool GRP>
+constexpr int fwd_groups() {
+  return (GRP && sizeof(T) == 2) ? 2 : 1;
+}
 // Waves per SIMD the forward is compiled for: 16-bit inputs without a
-// key-side term or staged rows fit 3 (168 VGPRs), which hides more latency
-// than operand prefetch; the others keep 2.
-template <typename T, bool ZK, bool ZQS>
+// key-side term, staged rows or groups fit 3 (168 VGPRs), which hides more
+// latency than operand prefetch; the others keep 2.
+template <typename T, bool ZK, bool ZQS, bool GRP>
 constexpr int fwd_occupancy() {
-  return (sizeof(T) == 2 && !ZK && !ZQS) ? 3 : (sizeof(T) == 2 ? 2 : 1);
+  return (sizeof(T) == 2 && !ZK && !ZQS && !GRP) ? 3 : (sizeof(T) == 2 ? 2 : 1);
+}
+template <typename T, bool GRP>
+constexpr int fwd_threads() {
+  return kThreads * fwd_groups<T, GRP>();
+}
+template <typename T, bool ZK, bool ZQS, bool GRP>
+constexpr int fwd_blocks_per_cu() {
+  return fwd_occupancy<T, ZK, ZQS, GRP>() / fwd_groups<T, GRP>();
 }
 
 // ZQS: Z^Q band rows staged in LDS (wide bands) instead of gathered per score.
 // OCC3: compiled for 3 waves per SIMD: each subtile reads its own operand
 // fragments (instead of the whole tile's up front), which keeps fewer
 // registers live.
-template <typename T, bool ZQS, bool OCC3>
+template <typename T, bool ZQS, bool OCC3, bool GRP>
 struct Fwd {
   using M = MT<T>;
   using frag = typename M::frag;
   static constexpr bool kHalf = sizeof(T) == 2;
   static constexpr bool kOcc3 = OCC3;
+  static constexpr int kGroups = fwd_groups<T, GRP>();
   static constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
   static constexpr int KPS = 32 / KS;  // MFMA k-steps per 32-key half
   static constexpr int TB = DTile<T>::BYTES;
 
   // LDS buffers, two of each (separate arrays, so that the compiler can tell
   // the asynchronous loads into one buffer from the reads of the other)
-  char* sK[2];    // K tile
+  char* sK[2];    // K tile (group 0's buffers; this group's start goff bytes in)
   char* sV[2];    // V tile
-  float* sZK[2];  // saturated Z^K scalars of the tile's keys [2][kTile]
+  float* sZK[2];  // saturated Z^K scalars of the tile's keys [group][2][kTile]
+  int grp, goff;  // this wave's group, byte offset of its K / V buffers
 
   Geo g;
   QCtx c;
@@ -82,11 +101,11 @@ struct Fwd {
   template <int BUF>
   __device__ __forceinline__ void issue(int t) {
     const int j0 = t * kTile;
-    ldK.load(sK[BUF], Kb + (int64_t)j0 * sk, N - j0, lane);
-    ldV.load(sV[BUF], Vb + (int64_t)j0 * sv, N - j0, lane);
+    ldK.load(sK[BUF] + goff, Kb + (int64_t)j0 * sk, N - j0, lane);
+    ldV.load(sV[BUF] + goff, Vb + (int64_t)j0 * sv, N - j0, lane);
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
-      dword_direct((char*)(sZK[BUF] + w * kTile), p, p != nullptr, lane);
+      dword_direct((char*)(sZK[BUF] + (2 * grp + w) * kTile), p, p != nullptr, lane);
     }
   }
 
@@ -130,7 +149,7 @@ struct Fwd {
     const bool needmask = BAND && ((j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0));
     const char* tK = sK[BUF];
     const char* tV = sV[BUF];
-    const float* zk = sZK[BUF];
+    const float* zk = sZK[BUF] + 2 * grp * kTile;
     const float cst = kind == KIND_LO ? cst_lo : (kind == KIND_HI ? cst_hi : 0.f);
     // 16-bit types at occupancy 2: every operand fragment of the tile is read
     // from LDS up front (one batch), so the reads of the second half overlap
@@ -167,7 +186,7 @@ struct Fwd {
         s = qside_scores<T>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask,
                             ZQS ? zs.row(st, l32) + E * hl : nullptr);
         if (stage_next) {
-          if (st == 0) stage<0>(t + 1); else stage<1>(t + 1);
+          if (st == 0) stage<0>(t + kGroups); else stage<1>(t + kGroups);
         }
       } else
         s = qside_scores<T>(g, c, kf[st], zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
@@ -209,62 +228,73 @@ struct Fwd {
     }
   }
 
-  // Tile t from buffer BUF, with the loads of tile t + 1 into the other
-  // buffer in flight.  Tiles [0, t1) are left-saturated, [t2, nkt)
-  // right-saturated, the rest cross the band; tiles with masked entries
-  // (the key-length edge, the causal diagonal) also take the band body.
+  // Key tile t (none once t >= nkt) from buffer BUF, with the loads of the
+  // group's next tile into the other buffer in flight.  Tiles [0, t1) are
+  // left-saturated, [t2, nkt) right-saturated, the rest cross the band;
+  // tiles with masked entries (the key-length edge, the causal diagonal)
+  // also take the band body.
   template <int BUF>
   __device__ __forceinline__ void step(int t, int t1, int t2) {
-    if (t + 1 < nkt) issue<BUF ^ 1>(t + 1);
-    // Z^Q rows of tile t + 1: staged now when tile t leaves the buffers
-    // free, else from tile t's band path
-    const bool bn = band_here(t + 1), bc = band_here(t);
+    const int tn = t + kGroups;
+    if (tn < nkt) issue<BUF ^ 1>(tn);
+    // Z^Q rows of the group's next tile: staged now when tile t leaves the
+    // buffers free, else from tile t's band path
+    const bool bn = band_here(tn), bc = band_here(t);
     if (bn && !bc) {
-      stage<0>(t + 1);
-      stage<1>(t + 1);
+      stage<0>(tn);
+      stage<1>(tn);
     }
-    const int j0 = t * kTile;
-    const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
-    if ((t >= t1 && t < t2) || masked)
-      tile<true, BUF>(t, KIND_BAND, bn && bc);
-    else
-      tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI, false);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of tile t+1 landed
+    if (kGroups == 1 || t < nkt) {  // (one group: t < nkt always holds)
+      const int j0 = t * kTile;
+      const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
+      if ((t >= t1 && t < t2) || masked)
+        tile<true, BUF>(t, KIND_BAND, bn && bc);
+      else
+        tile<false, BUF>(t, t < t1 ? KIND_LO : KIND_HI, false);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's loads of its next tile landed
     __syncthreads();
   }
 
+  // Group grp takes key tiles grp, grp + kGroups, ...; every group runs the
+  // same number of steps (one workgroup barrier each), step m in buffer m & 1.
   __device__ __forceinline__ void run(int t1, int t2) {
-    if (nkt > 0) issue<0>(0);
-    if (band_here(0)) {
-      stage<0>(0);
-      stage<1>(0);
+    const int t0 = grp;
+    if (t0 < nkt) issue<0>(t0);
+    if (band_here(t0)) {
+      stage<0>(t0);
+      stage<1>(t0);
     }
-    // every load issued so far (Q fragments, tile 0) has landed: inside the
-    // loop a wave only waits for its own next-tile loads, before the barrier
+    // every load issued so far (Q fragments, the first tile) has landed:
+    // inside the loop a wave only waits for its own next-tile loads, before
+    // the barrier
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    for (int t = 0; t < nkt; t += 2) {
-      step<0>(t, t1, t2);
-      if (t + 1 < nkt) step<1>(t + 1, t1, t2);
+    const int nsteps = (nkt + kGroups - 1) / kGroups;
+    for (int m = 0; m < nsteps; m += 2) {
+      step<0>(t0 + kGroups * m, t1, t2);
+      if (m + 1 < nsteps) step<1>(t0 + kGroups * (m + 1), t1, t2);
     }
   }
 };
 
 // ZK: whether the key-side relation term is present (a compile-time switch, so
 // that saturated tiles without it seed their MFMA accumulators with zero and
-// carry no branch); ZQS: Z^Q band rows staged in LDS.
-template <typename T, bool ZK, bool ZQS>
-__global__ __launch_bounds__(kThreads, (fwd_occupancy<T, ZK, ZQS>())) void fwd_kernel(AttnArgs a) {
+// carry no branch); ZQS: Z^Q band rows staged in LDS; GRP: grouped workgroup.
+template <typename T, bool ZK, bool ZQS, bool GRP>
+__global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, ZQS, GRP>()))
+    void fwd_kernel(AttnArgs a) {
   using M = MT<T>;
   constexpr float kLn2 = 0.693147180559945309f;
   constexpr int TB = DTile<T>::BYTES;
+  constexpr int G = fwd_groups<T, GRP>();
 
-  __shared__ __align__(16) char sK0[TB], sK1[TB], sV0[TB], sV1[TB];
-  __shared__ __align__(16) float sZK0[2 * kTile], sZK1[2 * kTile];
-  constexpr int kZQ = ZQS ? 4 * RowStage::kFloats : 4;
+  __shared__ __align__(16) char sK0[G * TB], sK1[G * TB], sV0[G * TB], sV1[G * TB];
+  __shared__ __align__(16) float sZK0[G * 2 * kTile], sZK1[G * 2 * kTile];
+  constexpr int kZQ = ZQS ? 4 * G * RowStage::kFloats : 4;
   __shared__ __align__(16) float sZQ0[kZQ], sZQ1[kZQ];
 
-  using F = Fwd<T, ZQS, fwd_occupancy<T, ZK, ZQS>() == 3>;
+  using F = Fwd<T, ZQS, fwd_occupancy<T, ZK, ZQS, GRP>() == 3, GRP>;
   F f;
   f.sK[0] = sK0;
   f.sK[1] = sK1;
@@ -276,16 +306,20 @@ __global__ __launch_bounds__(kThreads, (fwd_occupancy<T, ZK, ZQS>())) void fwd_k
   const Geo& g = f.g;
   const int N = g.N;
   f.N = N;
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, wall = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int grp = G == 2 ? wall >> 2 : 0, w = wall & 3;
+  f.grp = grp;
+  // the group offset goes into the per-lane fragment offsets, so that the
+  // LDS reads keep compile-time buffer bases
+  f.goff = grp * TB;
   f.tid = tid;
   f.w = w;
   f.lane = lane;
   f.hl = hl;
   f.l32 = l32;
   const int total = a.B * a.H * a.nblk;
-  const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / a.nblk;
-  int qb = lid - bh * a.nblk;
+  int bh, qb;
+  block_of(blockIdx.x, total, a.nblk, g.causal, bh, qb);
   if (g.causal) qb = a.nblk - 1 - qb;  // longest rows first
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
@@ -310,8 +344,8 @@ __global__ __launch_bounds__(kThreads, (fwd_occupancy<T, ZK, ZQS>())) void fwd_k
     const int sig = sigma<T>(l32);
 #pragma unroll
     for (int ks = 0; ks < F::NSD; ++ks)
-      f.kofs[ks] = dt_off<T>(sig, F::KS * ks + F::E * hl);
-    f.tr.init(lane);
+      f.kofs[ks] = f.goff + dt_off<T>(sig, F::KS * ks + F::E * hl);
+    f.tr.init(lane, f.goff);
   }
 
   QCtx& c = f.c;
@@ -327,8 +361,8 @@ __global__ __launch_bounds__(kThreads, (fwd_occupancy<T, ZK, ZQS>())) void fwd_k
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
-  f.zs.buf[0] = ZQS ? sZQ0 + w * RowStage::kFloats : sZQ0;
-  f.zs.buf[1] = ZQS ? sZQ1 + w * RowStage::kFloats : sZQ1;
+  f.zs.buf[0] = ZQS ? sZQ0 + wall * RowStage::kFloats : sZQ0;
+  f.zs.buf[1] = ZQS ? sZQ1 + wall * RowStage::kFloats : sZQ1;
   f.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, -1, lane);
   f.sc2 = a.scale2;
 
@@ -350,6 +384,39 @@ __global__ __launch_bounds__(kThreads, (fwd_occupancy<T, ZK, ZQS>())) void fwd_k
 
   f.run(t1, t2);
 
+  if constexpr (G == 2) {
+    // group 1 hands its softmax state (O accumulator, reference maximum,
+    // partial sum) to group 0 through the K / V buffers; group 0 rescales
+    // both to the larger maximum and adds them
+    const int t = tid & (4 * 64 - 1);
+    float* x0 = reinterpret_cast<float*>(sK0);
+    float* x1 = reinterpret_cast<float*>(sK1);
+    float* x2 = reinterpret_cast<float*>(sV0);
+    static_assert(G * TB >= 16 * 256 * 4, "combine buffers");
+    if (grp == 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x0[e * 256 + t] = f.oacc[0][e];
+        x1[e * 256 + t] = f.oacc[1][e];
+      }
+      x2[t] = f.m_used;
+      x2[256 + t] = f.lsum;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = x2[t], l1 = x2[256 + t];
+    const float m = fmaxf(f.m_used, m1);
+    const float a0 = f.m_used == -INFINITY ? 0.f : exp2_fast(f.m_used - m);
+    const float a1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - m);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      f.oacc[0][e] = f.oacc[0][e] * a0 + x0[e * 256 + t] * a1;
+      f.oacc[1][e] = f.oacc[1][e] * a0 + x1[e * 256 + t] * a1;
+    }
+    f.lsum = f.lsum * a0 + l1 * a1;
+    f.m_used = m;
+  }
+
   const float ltot = sum_xor32(f.lsum);
   if (iq < N) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -367,19 +434,26 @@ __global__ __launch_bounds__(kThreads, (fwd_occupancy<T, ZK, ZQS>())) void fwd_k
   }
 }
 
-template <typename T>
-static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
+template <typename T, bool GRP>
+static hipError_t launch_fwd_g(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
   const bool zk = a.flags & F_ZK, zqs = (a.flags & F_ZQ) && a.geo.W >= kStageMinW;
+  const int nt = fwd_threads<T, GRP>();
   if (zk && zqs)
-    hipLaunchKernelGGL((fwd_kernel<T, true, true>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, true, true, GRP>), dim3(total), dim3(nt), 0, st, a);
   else if (zk)
-    hipLaunchKernelGGL((fwd_kernel<T, true, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, true, false, GRP>), dim3(total), dim3(nt), 0, st, a);
   else if (zqs)
-    hipLaunchKernelGGL((fwd_kernel<T, false, true>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, false, true, GRP>), dim3(total), dim3(nt), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, false, false>), dim3(total), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, false, false, GRP>), dim3(total), dim3(nt), 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
+  if (a.split && sizeof(T) == 2) return launch_fwd_g<T, true>(a, st);
+  return launch_fwd_g<T, false>(a, st);
 }
 
 hipError_t launch_fwd(int dtype, const AttnArgs& a, hipStream_t st) {

@@ -143,6 +143,24 @@ __device__ inline int xcd_remap(int bid, int total) {
   return (bid & 7) * q + (bid >> 3);
 }
 
+// Block of a launch over (B*H) x nblk blocks -> (bh, rank): equal-work
+// launches use xcd_remap (the blocks of one head consecutive on one XCD);
+// causal launches number the blocks rank-major (rank 0 = the longest block of
+// every head first, so that the dispatch order is longest first over the
+// whole grid), and with B*H a multiple of 8 block b still runs on XCD
+// b % 8 = bh % 8, so that a head's blocks share one L2.
+__device__ inline void block_of(int bid, int total, int nblk, bool causal, int& bh, int& rank) {
+  if (causal) {
+    const int nbh = total / nblk;
+    rank = bid / nbh;
+    bh = bid - rank * nbh;
+  } else {
+    const int lid = xcd_remap(bid, total);
+    bh = lid / nblk;
+    rank = lid - bh * nblk;
+  }
+}
+
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Combine a value with the one of lane l ^ 32 (v_permlane32_swap: one VALU

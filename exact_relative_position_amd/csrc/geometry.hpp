@@ -142,6 +142,7 @@ struct AttnArgs {
   float scale2;    // tau * log2(e)
   int flags;
   int nblk;        // blocks per (b, h) along the parallel dimension
+  int split;       // causal launches: two wave groups per block split its tiles
 };
 
 struct RowTermArgs {     // padded backward row terms
