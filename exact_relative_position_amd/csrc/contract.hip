@@ -751,27 +751,29 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
 }
 
 // out[ho][k][d] = sum_{u in [ub[k], ue[k])} sum_s part[s][ho][u][d], u ascending.
-__global__ void fold_kernel(FoldArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n = (int64_t)a.Ho * a.R * 65;
-  if (idx >= n) return;
-  const int d = (int)(idx % 65);
-  const int64_t hk = idx / 65;
-  const int k = (int)(hk % a.R), ho = (int)(hk / a.R);
+// Block (k4, ho): table rows k = 4 k4 .. 4 k4 + 3 of head ho, one thread per
+// (row, d); lane d = 0 also sums the bias column.  Fixed order: u ascending,
+// then the splits.
+__global__ __launch_bounds__(256) void fold_kernel(FoldArgs a) {
+  const int d = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ho = blockIdx.y;
+  if (k >= a.R) return;
   const int b = a.ub ? a.ub[k] : k;
   const int e = a.ub ? a.ue[k] : k + 1;
-  if (d < 64) {
-    if (!a.out) return;
+  const int64_t sstride = (int64_t)a.Ho * a.Rpad;  // rows between splits
+  if (a.out) {
+    const float* p = a.part + ((int64_t)ho * a.Rpad) * 64 + d;
     float s = 0.f;
     for (int u = b; u < e; ++u)
-      for (int sp = 0; sp < a.splits; ++sp)
-        s += a.part[(((int64_t)sp * a.Ho + ho) * a.Rpad + u) * 64 + d];
+      for (int sp = 0; sp < a.splits; ++sp) s += p[(sp * sstride + u) * 64];
     a.out[((int64_t)ho * a.R + k) * 64 + d] = s;
-  } else {
-    if (!a.outb) return;
+  }
+  if (a.outb && d == 0) {
+    const float* p = a.partb + (int64_t)ho * a.Rpad;
     float s = 0.f;
     for (int u = b; u < e; ++u)
-      for (int sp = 0; sp < a.splits; ++sp) s += a.partb[((int64_t)sp * a.Ho + ho) * a.Rpad + u];
+      for (int sp = 0; sp < a.splits; ++sp) s += p[sp * sstride + u];
     a.outb[(int64_t)ho * a.R + k] = s;
   }
 }
@@ -830,9 +832,9 @@ hipError_t launch_cols(int dtype, const ColsArgs& a, int Ho, hipStream_t st) {
 }
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t st) {
-  const int64_t n = (int64_t)a.Ho * a.R * 65;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  if (a.Ho <= 0 || a.R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)((a.R + 3) / 4), (unsigned)a.Ho), dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 

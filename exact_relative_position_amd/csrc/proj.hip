@@ -71,8 +71,14 @@ __global__ void bias_unfold_kernel(BiasArgs a) {
 }
 
 // Z[bh][i][c] = x_i . tab[fold(ws + c)] (+ bias[fold(ws + c)]) for c in the
-// group's live columns [cb, ce).  Block: 128 rows x 64 columns; wave w owns
-// rows 32w..32w+31 and two 32-column MFMA tiles.
+// group's live columns [cb, ce).  Block: 128 rows x proj_cols() columns (256
+// for windows of 2048 columns and more, else 128); wave w
+// owns rows 32w..32w+31, keeps their X fragments in registers and walks the
+// block's 32-column MFMA tiles, loading the next tile's table fragments
+// before it computes and stores the current one, so that the loads overlap
+// the stores (each store instruction writes 128-byte runs of two rows).
+__host__ __device__ inline int proj_cols(const ProjArgs& a) { return a.ncol_tiles >= 32 ? 256 : 128; }
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   using M = MT<T>;
@@ -80,12 +86,14 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   constexpr int KS = M::KS, E = M::E, NSD = kHeadDim / KS;
   const Geo g = a.geo;
   const int N = g.N;
-  const int per_bh = a.ngroups * a.ncol_tiles;
+  const int pc = proj_cols(a);
+  const int nch = (a.ncol_tiles + pc / 64 - 1) / (pc / 64);  // chunks per group
+  const int per_bh = a.ngroups * nch;
   const int total = a.B * a.H * per_bh;
   const int lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / per_bh;
   const int rem = lid - bh * per_bh;
-  const int grp = rem / a.ncol_tiles, ct = rem - grp * a.ncol_tiles;
+  const int grp = rem / nch, ch = rem - grp * nch;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   int cb, ce, ws;
   if (a.key_side) {
@@ -95,8 +103,9 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
     cols_q(g, grp, cb, ce);
     ws = win_q(g, grp);
   }
-  const int c0 = cb + ct * 64;
+  const int c0 = cb + ch * pc;
   if (c0 >= ce) return;
+  const int nsub = (imin(ce - c0, pc) + 31) / 32;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int i = grp * kBlockRows + 32 * w + l32;  // row loaded by this lane (operand A)
 
@@ -106,29 +115,46 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   for (int ks = 0; ks < NSD; ++ks) xf[ks] = i < N ? frag_g<T>(xrow, KS * ks + E * hl) : M::zero();
 
   const T* tab = (const T*)a.tab + hh * a.tab_hs;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const int col = c0 + 32 * sub + l32;  // column of operand B held by this lane
-    const bool cv = col < ce;
+  float* zb = a.z + (int64_t)bh * N * g.Wp;
+  // table fragments (operand B: lane's column) and bias of tile n
+  auto load_tile = [&](int n, frag (&tf)[NSD], float& badd, bool& cv, int& col) {
+    col = c0 + 32 * n + l32;
+    cv = col < ce;
     const int u = ws + col;
     const int r = cv ? (a.fold ? a.fold[u] : u) : 0;
     const T* trow = tab + (int64_t)r * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < NSD; ++ks) tf[ks] = cv ? frag_g<T>(trow, KS * ks + E * hl) : M::zero();
+    badd = (a.bias && cv) ? MT<T>::to_f(((const T*)a.bias)[hh * a.bias_hs + r]) : 0.f;
+  };
+  frag tf[NSD];
+  float badd;
+  bool cv;
+  int col;
+  load_tile(0, tf, badd, cv, col);
+#pragma unroll 1
+  for (int n = 0; n < nsub; ++n) {
+    frag tn[NSD];
+    float bn = 0.f;
+    bool cvn = false;
+    int coln = 0;
+    if (n + 1 < nsub) load_tile(n + 1, tn, bn, cvn, coln);
     f32x16 acc = zero16();
 #pragma unroll
-    for (int ks = 0; ks < NSD; ++ks) {
-      frag tf = cv ? frag_g<T>(trow, KS * ks + E * hl) : M::zero();
-      acc = M::mma(xf[ks], tf, acc);
-    }
-    float badd = 0.f;
-    if (a.bias && cv) badd = MT<T>::to_f(((const T*)a.bias)[hh * a.bias_hs + r]);
+    for (int ks = 0; ks < NSD; ++ks) acc = M::mma(xf[ks], tf[ks], acc);
     if (cv) {
-      float* zc = a.z + (int64_t)bh * N * g.Wp + col;
+      float* zc = zb + col;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = grp * kBlockRows + 32 * w + res_row(hl, e);
         if (row < N) zc[(int64_t)row * g.Wp] = acc[e] + badd;
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < NSD; ++ks) tf[ks] = tn[ks];
+    badd = bn;
+    cv = cvn;
+    col = coln;
   }
 }
 
@@ -161,7 +187,9 @@ hipError_t launch_bias_unfold(int dtype, const BiasArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_proj(int dtype, const ProjArgs& a, hipStream_t st) {
-  const int total = a.B * a.H * a.ngroups * a.ncol_tiles;
+  const int pc = proj_cols(a);
+  const int nch = (a.ncol_tiles + pc / 64 - 1) / (pc / 64);
+  const int total = a.B * a.H * a.ngroups * nch;
   if (total <= 0) return hipSuccess;
   switch (dtype) {
     case 0: hipLaunchKernelGGL(proj_kernel<float>, dim3(total), dim3(kThreads), 0, st, a); break;
