@@ -184,7 +184,7 @@ struct BwdK {
     }
   }
 
-  // One 64-query tile from LDS buffer BUF.  BAND: the block's tile crosses
+  // One 64-query tile from LDS buffer BUF.  BAND: the wave's tile crosses
   // the band or holds masked entries (each wave refines the kind for its
   // own keys); otherwise the whole tile is saturated on side `sat`.
   //
@@ -292,8 +292,7 @@ struct BwdK {
     if (t < ntq) {
       // tiles with masked entries also take the band body
       const int qt0 = t * kTile;
-      const bool masked = (qt0 + kTile > N) || (j0b + kBlockRows > kv_end) ||
-                          (g.causal && j0b + kBlockRows - 1 > qt0);
+      const bool masked = (qt0 + kTile > N) || (jw0 + 32 > kv_end) || (g.causal && jw0 + 31 > qt0);
       if ((t >= tA && t < tB) || masked)
         tile<true, BUF>(t, KIND_BAND);
       else
@@ -433,10 +432,11 @@ __global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>
   k.acc_lo = 0.f;
   k.acc_hi = 0.f;
 
-  // segments over the query tiles [t_begin, ntq): all offsets >= hi first,
-  // band, then all offsets <= lo
-  const int tA = imin(ntq, imax(t_begin, floor_div_k(j0b - (kTile - 1) - g.hi, kTile) + 1));
-  const int tB = imin(ntq, imax(tA, ceil_div_k(j0b + kBlockRows - 1 - g.lo, kTile)));
+  // this wave's segments over the query tiles [t_begin, ntq): for its 32
+  // keys all offsets >= hi first, then the band, then all offsets <= lo (a
+  // tile goes through the band body only for the waves that need it)
+  const int tA = imin(ntq, imax(t_begin, floor_div_k(jw0 - (kTile - 1) - g.hi, kTile) + 1));
+  const int tB = imin(ntq, imax(tA, ceil_div_k(jw0 + 31 - g.lo, kTile)));
 
   k.run(t_begin, tA, tB);
 

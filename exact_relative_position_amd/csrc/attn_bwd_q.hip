@@ -141,7 +141,7 @@ struct BwdQ {
     }
   }
 
-  // One 64-key tile from LDS buffer BUF; BAND: the block's tile crosses the
+  // One 64-key tile from LDS buffer BUF; BAND: the wave's tile crosses the
   // band, otherwise it is saturated on side `sat`.
   // stage_next: the Z^Q rows of tile t + 1 are staged from this tile's band
   // path, each subtile's once its area is free again.
@@ -247,7 +247,7 @@ struct BwdQ {
     if (kGroups == 1 || t < nkt) {
       // tiles with masked entries also take the band body
       const int j0 = t * kTile;
-      const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
+      const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0);
       if ((t >= t1 && t < t2) || masked)
         tile<true, BUF>(t, KIND_BAND, bn && bc);
       else
@@ -382,8 +382,11 @@ __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, 
   q.acc_lo = 0.f;
   q.acc_hi = 0.f;
 
-  const int t1 = imin(nkt, imax(0, floor_div_q(g.lo + i0 - (kTile - 1), kTile) + 1));
-  const int t2 = imin(nkt, imax(t1, ceil_div_q(g.hi + i0 + kBlockRows - 1, kTile)));
+  // this wave's segments: key tiles [0, t1) have all offsets <= lo for its
+  // 32 queries, [t2, nkt) all offsets >= hi, the band in between (a tile
+  // goes through the band body only for the waves that need it)
+  const int t1 = imin(nkt, imax(0, floor_div_q(g.lo + iw0 - (kTile - 1), kTile) + 1));
+  const int t2 = imin(nkt, imax(t1, ceil_div_q(g.hi + iw0 + 31, kTile)));
 
   q.run(t1, t2);
 

@@ -14,11 +14,11 @@
 // tile with ds_read_b64_tr_b16 transpose reads (fp32: element reads).
 //
 // Three-segment key loop: two comparisons per tile against the thresholds
-// split the block's key tiles into a left-saturated run, a band run and a
-// right-saturated run.  Each run is its own loop, compiled for its kind, so
-// the saturated loops contain no per-score lookup and no gather (and the
-// next tile's prefetch is never held up behind one).  Inside the band run
-// each wave refines the kind for its own 32 queries.
+// split each wave's key tiles (for its own 32 queries) into a left-saturated
+// run, a band run and a right-saturated run.  The saturated runs take a body
+// compiled without per-score lookup, gather or mask code (and the next
+// tile's prefetch is never held up behind one); the band run and the tiles
+// with masked entries take the general body.
 //
 // Softmax: base-2 with tau*log2(e) folded into one FMA per score; the
 // reference maximum is only moved when a row's maximum grows by more than
@@ -246,7 +246,7 @@ struct Fwd {
     }
     if (kGroups == 1 || t < nkt) {  // (one group: t < nkt always holds)
       const int j0 = t * kTile;
-      const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > i0);
+      const bool masked = (j0 + kTile > c.kv_end) || (g.causal && j0 + kTile - 1 > iw0);
       if ((t >= t1 && t < t2) || masked)
         tile<true, BUF>(t, KIND_BAND, bn && bc);
       else
@@ -377,10 +377,11 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   f.m_used = -INFINITY;
   f.lsum = 0.f;
 
-  // segment bounds of this block's key tiles: [0, t1) all offsets <= lo,
-  // [t2, nkt) all offsets >= hi, band in between
-  const int t1 = imin(nkt, imax(0, floor_div(g.lo + i0 - (kTile - 1), kTile) + 1));
-  const int t2 = imin(nkt, imax(t1, ceil_div(g.hi + i0 + kBlockRows - 1, kTile)));
+  // this wave's segments: key tiles [0, t1) have all offsets <= lo for its
+  // 32 queries, [t2, nkt) all offsets >= hi, the band in between (a tile
+  // goes through the band body only for the waves that need it)
+  const int t1 = imin(nkt, imax(0, floor_div(g.lo + iw0 - (kTile - 1), kTile) + 1));
+  const int t2 = imin(nkt, imax(t1, ceil_div(g.hi + iw0 + 31, kTile)));
 
   f.run(t1, t2);
 
