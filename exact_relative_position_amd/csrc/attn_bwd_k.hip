@@ -77,6 +77,10 @@ struct BwdK {
   int grp;                                                        // this wave's group
   bool has_zq, has_zk, has_b;
   float off_lo, off_hi, sc2, tau;
+  // Padded keys (key >= the batch's key length) need no mask: a lane's P and
+  // dS only reach its own key's dK, dV and dZ^K, which are written as zeros
+  // at the end (and its band dZ^K stores are skipped), so key padding never
+  // sends a tile to the band body.
   const T* Qb;
   const T* Ob;
   const float* seeds;   // [4][B*H][Np]: LO seed, HI seed, band seed, -D
@@ -179,7 +183,7 @@ struct BwdK {
       const float v = stage[q * kStagePitchK + l32];
       const int j = jw0 + q;
       const int o = j - i;
-      if (o > g.lo && o < g.hi && i < N && j < N && !(g.causal && j > i))
+      if (o > g.lo && o < g.hi && i < N && j < kv_end && !(g.causal && j > i))
         dz_w[(int64_t)q * g.Wp + o - g.lo - wsk] = v;
     }
   }
@@ -195,12 +199,14 @@ struct BwdK {
   template <bool BAND, int BUF>
   __device__ __forceinline__ void tile(int t, int sat) {
     const int qt0 = t * kTile;
+    // (a wave whose keys are all padded contributes nothing: its band tiles
+    // are skipped, and whatever its saturated tiles accumulate is discarded)
     if (BAND && (jw0 >= imin(N, kv_end) || (g.causal && qt0 + kTile - 1 < jw0))) return;
     const int kind = BAND ? tile_kind_k(g, qt0, jw0) : sat;
     // masks are only applied in the band body (a saturated body is only
     // used for tiles that need no mask anywhere in the block)
     const bool needmask =
-        BAND && ((qt0 + kTile > N) || (jw0 + 32 > kv_end) || (g.causal && jw0 + 31 > qt0));
+        BAND && ((qt0 + kTile > N) || (g.causal && jw0 + 31 > qt0));
     const char* tQ = sQ[BUF];
     const char* tO = sO[BUF];
     const float* sr = sR[BUF];
@@ -225,7 +231,7 @@ struct BwdK {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int i = qt0 + 32 * st + kappa<T>(hl, e);
-          if (i >= N || jk >= kv_end || (g.causal && jk > i)) s[e] = -INFINITY;
+          if (i >= N || (g.causal && jk > i)) s[e] = -INFINITY;
         }
       }
       f32x16 dp;
@@ -260,7 +266,7 @@ struct BwdK {
             // (lo == hi: an offset equal to both counts once, on the low side)
             acc_lo += o <= g.lo ? ds[e] : 0.f;
             acc_hi += (o > g.lo && o >= g.hi) ? ds[e] : 0.f;
-            if (!STAGE && o > g.lo && o < g.hi && i < N && jk < N && !(g.causal && jk > i))
+            if (!STAGE && o > g.lo && o < g.hi && i < N && jk < kv_end && !(g.causal && jk > i))
               dz_row[o - g.lo - wsk] = tau * ds[e];
           }
           if constexpr (STAGE) band_store(ds, qt0 + 32 * st);
@@ -292,7 +298,7 @@ struct BwdK {
     if (t < ntq) {
       // tiles with masked entries also take the band body
       const int qt0 = t * kTile;
-      const bool masked = (qt0 + kTile > N) || (jw0 + 32 > kv_end) || (g.causal && jw0 + 31 > qt0);
+      const bool masked = (qt0 + kTile > N) || (g.causal && jw0 + 31 > qt0);
       if ((t >= tA && t < tB) || masked)
         tile<true, BUF>(t, KIND_BAND);
       else
@@ -474,6 +480,15 @@ __global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>
     k.acc_hi += sR0[256 + t];
   }
 
+  if (jk >= kv_end) {
+    // a padded key: exact zeros (its unmasked scores were accumulated)
+    k.dk[0] = zero16();
+    k.dk[1] = zero16();
+    k.dv[0] = zero16();
+    k.dv[1] = zero16();
+    k.acc_lo = 0.f;
+    k.acc_hi = 0.f;
+  }
   if (jk < N) {
     T* vrow = (T*)a.dv + bb * a.sdv.b + hh * a.sdv.h + (int64_t)jk * a.sdv.n;
 #pragma unroll
@@ -524,11 +539,12 @@ __global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>
           if (c1 >= cb && c1 < ce) dz_row[c1] = a.tau * acc_hi;
         }
       }
-      // Queries written by the band stores: [q_lo, q_hi).  Interior columns
-      // of any other query carry no gradient and are zeroed.
+      // Queries written by the band stores: [q_lo, q_hi) (none for a padded
+      // key).  Interior columns of any other query carry no gradient and are
+      // zeroed.
       const bool wave_ran = jw0 < imin(N, kv_end) && t_begin < ntq;
       const int q_lo = t_begin * kTile;
-      const int q_hi = wave_ran ? N : q_lo;
+      const int q_hi = (wave_ran && jk < kv_end) ? N : q_lo;
       const int ib = imax(cb, 1 - wsk), ie = imin(ce, g.R - 1 - wsk);
       // query of column col is jk - (col + wsk + lo) = shift - col
       const int shift = jk - wsk - g.lo;
