@@ -3,8 +3,8 @@
 
 One step = every stage of the path on one batch of seeded synthetic input
 already resident in HBM: map tables and relation projection, fused forward,
-backward row terms, query-parallel pass, key-parallel pass, contraction and
-bucket fold.  The default workload is the 8K layer-benchmark shape of the
+backward row terms, the query- and key-parallel passes (one launch that
+carries the blocks of both), contraction and bucket fold.  The default workload is the 8K layer-benchmark shape of the
 setup section of "Fast and Exact Relative-Position Attention via
 Structure-Aware Kernels" (nanless.github.io digest) for the Shaw mechanism:
 B=1, H=12, N=8192, d=64, fp16, truncation +-128.
@@ -14,8 +14,8 @@ synchronisations.  HIP events are recorded between the stage calls, on the
 stream the library launches on, so each kernel's average duration is measured
 live; the dominant attention kernel gives the roofline figure.
 FLOP convention (FlashAttention): forward 4 d per live (query, key) pair,
-backward 10 d; each backward kernel's own count is its GEMM work (query pass
-6 d, key pass 8 d per pair).  The CPU baseline is the fp64 oracle on a
+backward 10 d; the backward launch's own count is its GEMM work (query pass
+6 d plus key pass 8 d per pair).  The CPU baseline is the fp64 oracle on a
 bounded sample (whole (batch, head) slices of the same workload, about ten
 seconds of work), timed on the host cores.
 
@@ -102,10 +102,11 @@ def cpu_baseline(w, x, min_seconds=10.0):
                       f"at full N={w.N}, fp64 NumPy"}
 
 
+_COMMON = ("qside.hpp", "tiles.hpp", "device.hpp", "geometry.hpp")
 KERNEL_SOURCES = {
-    name: (src, "qside.hpp", "tiles.hpp", "device.hpp", "geometry.hpp")
-    for name, src in (("fwd_kernel", "attn_fwd.hip"), ("bwd_q_kernel", "attn_bwd_q.hip"),
-                      ("bwd_k_kernel", "attn_bwd_k.hip"))
+    "fwd_kernel": ("attn_fwd.hip",) + _COMMON,
+    "bwd_kernel": ("attn_bwd.hpp", "attn_bwd_q.hpp", "attn_bwd_k.hpp", "attn_bwd_f32.hip",
+                   "attn_bwd_f16.hip", "attn_bwd_bf16.hip") + _COMMON,
 }
 
 
@@ -157,6 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="shaw_n8192_f16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-passes", action="store_true",
+                    help="time the query and key passes as two launches (diagnostic)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the warmup "
                          "(calibration of HBM byte counters)")
@@ -186,9 +189,13 @@ def main():
     stages = [("project", lambda: run.fwd(B_.FWD_PROJECT)),
               ("attend", lambda: run.fwd(B_.FWD_ATTEND)),
               ("prepare", lambda: run.bwd(B_.BWD_PREPARE)),
-              ("query_pass", lambda: run.bwd(B_.BWD_QUERY_PASS)),
-              ("key_pass", lambda: run.bwd(B_.BWD_KEY_PASS)),
+              ("passes", lambda: run.bwd(B_.BWD_QUERY_PASS | B_.BWD_KEY_PASS)),
               ("contract", lambda: run.bwd(B_.BWD_CONTRACT))]
+    if args.separate_passes:
+        # diagnostic: one launch per pass (the default step launches both at once)
+        k = [n for n, _ in stages].index("passes")
+        stages[k:k + 1] = [("query_pass", lambda: run.bwd(B_.BWD_QUERY_PASS)),
+                           ("key_pass", lambda: run.bwd(B_.BWD_KEY_PASS))]
 
     for _ in range(args.warmup):
         for _, fn in stages:
@@ -214,7 +221,8 @@ def main():
                 for k, (name, _) in enumerate(stages)}
     gpu_ms = ev[0][0].elapsed_time(ev[K - 1][len(stages)]) / K
     fwd_ms = stage_ms["project"] + stage_ms["attend"]
-    bwd_ms = sum(stage_ms[n] for n in ("prepare", "query_pass", "key_pass", "contract"))
+    bwd_ms = sum(stage_ms[n] for n in ("prepare", "passes", "query_pass", "key_pass", "contract")
+                 if n in stage_ms)
 
     kl = None if x["key_len"] is None else x["key_len"].numpy()
     pairs = live_pairs(w, kl) * w.H
@@ -222,10 +230,13 @@ def main():
     useful = 14.0 * d * pairs
     value = useful / (gpu_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    kern_flops = {"attend": 4.0 * d * pairs, "query_pass": 6.0 * d * pairs,
-                  "key_pass": 8.0 * d * pairs}
-    kern_name = {"attend": "fwd_kernel", "query_pass": "bwd_q_kernel", "key_pass": "bwd_k_kernel"}
-    dom = max(kern_flops, key=lambda n: stage_ms[n])
+    # MFMA work per launch: forward 2 products, query pass 3 (S, dP, dQ), key
+    # pass 4 (S, dP, dV, dK), 2*d flops per live pair each
+    kern_flops = {"attend": 4.0 * d * pairs, "passes": 14.0 * d * pairs,
+                  "query_pass": 6.0 * d * pairs, "key_pass": 8.0 * d * pairs}
+    kern_name = {"attend": "fwd_kernel", "passes": "bwd_kernel", "query_pass": "bwd_kernel",
+                 "key_pass": "bwd_kernel"}
+    dom = max((n for n in kern_flops if n in stage_ms), key=lambda n: stage_ms[n])
     achieved = kern_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
 
     # projection pass: algorithmic bytes = fp32 window written + Q and table read

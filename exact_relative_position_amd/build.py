@@ -24,8 +24,9 @@ SOURCES = [
     "proj.hip",
     "prep.hip",
     "attn_fwd.hip",
-    "attn_bwd_q.hip",
-    "attn_bwd_k.hip",
+    "attn_bwd_f32.hip",
+    "attn_bwd_f16.hip",
+    "attn_bwd_bf16.hip",
     "contract.hip",
 ]
 

@@ -23,8 +23,9 @@
 namespace relpos {
 hipError_t launch_fwd(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_rowterm(int dtype, const RowTermArgs& a, hipStream_t st);
-hipError_t launch_bwd_q(int dtype, const AttnArgs& a, hipStream_t st);
-hipError_t launch_bwd_k(int dtype, const AttnArgs& a, hipStream_t st);
+hipError_t launch_bwd_f32(const AttnArgs& a, bool want_q, bool want_k, hipStream_t st);
+hipError_t launch_bwd_f16(const AttnArgs& a, bool want_q, bool want_k, hipStream_t st);
+hipError_t launch_bwd_bf16(const AttnArgs& a, bool want_q, bool want_k, hipStream_t st);
 hipError_t launch_phi_rows(const PhiArgs& p, int32_t* rows, hipStream_t st);
 hipError_t launch_phi_fold(const PhiArgs& p, int32_t* fold, int32_t* ub, int32_t* ue, int R,
                            hipStream_t st);
@@ -710,12 +711,25 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     if ((s = hip_check(launch_rowterm(pl.dtype, r, st), "backward (row terms)")) != RELPOS_OK)
       return s;
   }
-  if (stages & RELPOS_BWD_QUERY_PASS) {
-    if ((s = hip_check(launch_bwd_q(pl.dtype, a, st), "backward (query pass)")) != RELPOS_OK)
+  // The query and key passes share one launch when both are asked for: a
+  // pass alone may end with a partly filled last round of blocks, the two
+  // together fill it.  Problems that split their blocks between two wave
+  // groups (a.split: every block of a pass fits on the device at once, so
+  // the longest block bounds the pass) gain nothing from that and run the
+  // passes one after the other.
+  const bool want_q = stages & RELPOS_BWD_QUERY_PASS, want_k = stages & RELPOS_BWD_KEY_PASS;
+  auto launch_passes = [&](bool q, bool k) {
+    return pl.dtype == 0   ? launch_bwd_f32(a, q, k, st)
+           : pl.dtype == 1 ? launch_bwd_f16(a, q, k, st)
+                           : launch_bwd_bf16(a, q, k, st);
+  };
+  if (want_q && want_k && a.split) {
+    if ((s = hip_check(launch_passes(true, false), "backward (query pass)")) != RELPOS_OK)
       return s;
-  }
-  if (stages & RELPOS_BWD_KEY_PASS) {
-    if ((s = hip_check(launch_bwd_k(pl.dtype, a, st), "backward (key pass)")) != RELPOS_OK)
+    if ((s = hip_check(launch_passes(false, true), "backward (key pass)")) != RELPOS_OK) return s;
+  } else if (want_q || want_k) {
+    if ((s = hip_check(launch_passes(want_q, want_k), "backward (query and key passes)")) !=
+        RELPOS_OK)
       return s;
   }
   if (!(stages & RELPOS_BWD_CONTRACT)) return RELPOS_OK;

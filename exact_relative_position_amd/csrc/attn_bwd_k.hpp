@@ -1,4 +1,4 @@
-// attn_bwd_k.hip -- key-parallel backward pass.
+// attn_bwd_k.hpp -- the key-parallel backward pass (one block of it).
 //
 // Source: "Fast and Exact Relative-Position Attention via Structure-Aware
 // Kernels" (nanless.github.io digest), section on the backward pass: the
@@ -18,6 +18,7 @@
 // independent 4-wave blocks per CU overlap MFMA and vector work better than
 // one 8-wave block whose groups share every barrier.)  Orientation
 // S = Q K^T: lane l owns key l % 32.
+#pragma once
 #include "qside.hpp"
 
 namespace relpos {
@@ -326,16 +327,18 @@ struct BwdK {
 
 // ZQ: whether the query-side relation term is present (compile-time switch);
 // STAGE: band dZ^K stores staged through LDS; GRP: grouped workgroup.
+// One key block of the pass: block number bid of a launch over B*H*nblk
+// blocks.  LDS (sizes for G = key_groups groups): sQ0..sO1 G*DTile bytes
+// each, sR0/sR1 G*4*kTile floats, sSt (STAGE only) 4*G*32*kStagePitchK
+// floats.
 template <typename T, bool ZQ, bool STAGE, bool GRP>
-__global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>()))
-    void bwd_k_kernel(AttnArgs a) {
+__device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ0, char* sQ1,
+                                            char* sO0, char* sO1, float* sR0, float* sR1,
+                                            float* sSt) {
   using M = MT<T>;
   using K = BwdK<T, STAGE, GRP>;
   constexpr int TB = DTile<T>::BYTES;
   constexpr int G = K::kGroups;
-  __shared__ __align__(16) char sQ0[G * TB], sQ1[G * TB], sO0[G * TB], sO1[G * TB];
-  __shared__ __align__(16) float sR0[G * 4 * kTile], sR1[G * 4 * kTile];
-  __shared__ __align__(16) float sSt[STAGE ? 4 * G * 32 * kStagePitchK : 4];
 
   const int tid = threadIdx.x, wall = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int grp = G == 2 ? wall >> 2 : 0, w = wall & 3;
@@ -360,7 +363,7 @@ __global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>
   k.l32 = l32;
   const int total = a.B * a.H * a.nblk;
   int bh, kb;  // causal: early key blocks have the most queries (first)
-  block_of(blockIdx.x, total, a.nblk, g.causal, bh, kb);
+  block_of(bid, total, a.nblk, g.causal, bh, kb);
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int j0b = kb * kBlockRows, jw0 = j0b + 32 * w, jk = jw0 + l32;
   k.j0b = j0b;
@@ -554,36 +557,6 @@ __global__ __launch_bounds__((key_threads<T, GRP>()), (key_blocks_per_cu<T, GRP>
       const int b_end = imin(ie, shift - q_hi + 1);
       for (int col = ib + hl; col < b_end; col += 2) dz_row[col] = 0.f;
     }
-  }
-}
-
-template <typename T, bool GRP>
-static hipError_t launch_bwd_k_g(const AttnArgs& a, hipStream_t st) {
-  const int total = a.B * a.H * a.nblk;
-  const bool zq = a.flags & F_ZQ, stage = (a.flags & F_ZK) && a.geo.W >= kStageMinWK;
-  const int nt = kThreads * key_groups<T, GRP>();
-  if (zq && stage)
-    hipLaunchKernelGGL((bwd_k_kernel<T, true, true, GRP>), dim3(total), dim3(nt), 0, st, a);
-  else if (zq)
-    hipLaunchKernelGGL((bwd_k_kernel<T, true, false, GRP>), dim3(total), dim3(nt), 0, st, a);
-  else if (stage)
-    hipLaunchKernelGGL((bwd_k_kernel<T, false, true, GRP>), dim3(total), dim3(nt), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_k_kernel<T, false, false, GRP>), dim3(total), dim3(nt), 0, st, a);
-  return hipGetLastError();
-}
-
-template <typename T>
-static hipError_t launch_bwd_k_t(const AttnArgs& a, hipStream_t st) {
-  if (a.split && sizeof(T) == 2) return launch_bwd_k_g<T, true>(a, st);
-  return launch_bwd_k_g<T, false>(a, st);
-}
-
-hipError_t launch_bwd_k(int dtype, const AttnArgs& a, hipStream_t st) {
-  switch (dtype) {
-    case 0: return launch_bwd_k_t<float>(a, st);
-    case 1: return launch_bwd_k_t<_Float16>(a, st);
-    default: return launch_bwd_k_t<__bf16>(a, st);
   }
 }
 

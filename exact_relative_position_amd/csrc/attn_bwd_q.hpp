@@ -1,4 +1,4 @@
-// attn_bwd_q.hip -- backward preprocess D and the query-parallel backward pass.
+// attn_bwd_q.hpp -- the query-parallel backward pass (one block of it).
 //
 // Source: "Fast and Exact Relative-Position Attention via Structure-Aware
 // Kernels" (nanless.github.io digest), section on the backward pass: a
@@ -13,6 +13,7 @@
 // per 64-key tile the K and V rows are loaded straight into LDS (K^T, the
 // operand of dQ = dS K, through transpose reads); the key loop runs in three
 // segments like the forward.
+#pragma once
 #include "qside.hpp"
 
 namespace relpos {
@@ -278,17 +279,18 @@ struct BwdQ {
 
 // ZK: whether the key-side relation term is present (compile-time switch);
 // STAGE: band stores staged through LDS; GRP: grouped workgroup.
+// One query block of the pass: block number bid of a launch over
+// B*H*nblk blocks.  LDS (sizes for G = query_groups groups): sK0..sV1
+// G*DTile bytes each, sZK0/sZK1 G*2*kTile floats, sSt0/sSt1 (STAGE only)
+// 4*G*kStageFloats floats.
 template <typename T, bool ZK, bool STAGE, bool GRP>
-__global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, GRP>()))
-    void bwd_q_kernel(AttnArgs a) {
+__device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK0, char* sK1,
+                                            char* sV0, char* sV1, float* sZK0, float* sZK1,
+                                            float* sSt0, float* sSt1) {
   using M = MT<T>;
   using B = BwdQ<T, STAGE, GRP>;
   constexpr int TB = DTile<T>::BYTES;
   constexpr int G = B::kGroups;
-  __shared__ __align__(16) char sK0[G * TB], sK1[G * TB], sV0[G * TB], sV1[G * TB];
-  __shared__ __align__(16) float sZK0[G * 2 * kTile], sZK1[G * 2 * kTile];
-  constexpr int kSt = STAGE ? 4 * G * kStageFloats : 4;
-  __shared__ __align__(16) float sSt0[kSt], sSt1[kSt];
 
   const int tid = threadIdx.x, wall = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int grp = G == 2 ? wall >> 2 : 0, w = wall & 3;
@@ -313,7 +315,7 @@ __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, 
   q.l32 = l32;
   const int total = a.B * a.H * a.nblk;
   int bh, qb;
-  block_of(blockIdx.x, total, a.nblk, g.causal, bh, qb);
+  block_of(bid, total, a.nblk, g.causal, bh, qb);
   if (g.causal) qb = a.nblk - 1 - qb;  // longest rows first
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
@@ -468,36 +470,6 @@ __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, 
       for (int col = ib + hl; col < a_end; col += 2) dz_row[col] = 0.f;
       for (int col = imax(ib, q.kv_lim - shift) + hl; col < ie; col += 2) dz_row[col] = 0.f;
     }
-  }
-}
-
-template <typename T, bool GRP>
-static hipError_t launch_bwd_q_g(const AttnArgs& a, hipStream_t st) {
-  const int total = a.B * a.H * a.nblk;
-  const bool zk = a.flags & F_ZK, stage = a.geo.W >= kStageMinW;
-  const int nt = query_threads<T, GRP>();
-  if (zk && stage)
-    hipLaunchKernelGGL((bwd_q_kernel<T, true, true, GRP>), dim3(total), dim3(nt), 0, st, a);
-  else if (zk)
-    hipLaunchKernelGGL((bwd_q_kernel<T, true, false, GRP>), dim3(total), dim3(nt), 0, st, a);
-  else if (stage)
-    hipLaunchKernelGGL((bwd_q_kernel<T, false, true, GRP>), dim3(total), dim3(nt), 0, st, a);
-  else
-    hipLaunchKernelGGL((bwd_q_kernel<T, false, false, GRP>), dim3(total), dim3(nt), 0, st, a);
-  return hipGetLastError();
-}
-
-template <typename T>
-static hipError_t launch_bwd_q_t(const AttnArgs& a, hipStream_t st) {
-  if (a.split && sizeof(T) == 2) return launch_bwd_q_g<T, true>(a, st);
-  return launch_bwd_q_g<T, false>(a, st);
-}
-
-hipError_t launch_bwd_q(int dtype, const AttnArgs& a, hipStream_t st) {
-  switch (dtype) {
-    case 0: return launch_bwd_q_t<float>(a, st);
-    case 1: return launch_bwd_q_t<_Float16>(a, st);
-    default: return launch_bwd_q_t<__bf16>(a, st);
   }
 }
 

@@ -152,6 +152,42 @@ def test_strided_layout_bnhd():
             np.testing.assert_array_equal(got[n], ref[n], err_msg=n)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fused_passes_match_separate_launches(causal):
+    """The query and key passes in one launch (causal: dealt rank by rank)
+    give bit for bit the outputs of one launch per pass; the shape has more
+    blocks per pass than the device holds at once, so the causal launch is
+    not split between wave groups."""
+    import exact_relative_position_amd._binding as B_
+    dev = require_gpu()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    N = 1536
+    nblk = N // 128
+    H = (2 * cus) // nblk + 1
+    w = Workload("fused_passes", 1, H, N, 64, "f16", {"kind": "truncated", "lo": -300, "hi": 300},
+                 1 / 8, has_aq=True, has_ak=True, has_b=True, causal=causal)
+    x = make_inputs(w)
+    t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    _say(f"[gpu] fused vs separate passes causal={causal} H={H}")
+    run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
+                      tau=w.tau, causal=causal, key_len=t["key_len"], keep_z=True)
+    outs = ("dq", "dk", "dv", "daq", "dak", "db")
+    got = []
+    for passes in ((B_.BWD_QUERY_PASS | B_.BWD_KEY_PASS,), (B_.BWD_QUERY_PASS, B_.BWD_KEY_PASS)):
+        for n in outs:
+            getattr(run, n).fill_(float("nan"))
+        run.fwd()
+        run.bwd(B_.BWD_PREPARE)
+        for p in passes:
+            run.bwd(p)
+        run.bwd(B_.BWD_CONTRACT)
+        torch.cuda.synchronize(dev)
+        got.append({n: getattr(run, n).cpu().clone() for n in outs})
+    for n in outs:
+        assert torch.isfinite(got[0][n]).all(), n
+        assert torch.equal(got[0][n], got[1][n]), n
+
+
 FULL = ["shaw_n256_f32", "shaw_n8192_f16", "deberta_n8192_f16", "t5_n8192_f16",
         "txl_n4096_bf16", "txl_n8192_f16"]
 
