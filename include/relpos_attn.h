@@ -181,6 +181,8 @@ relpos_status relpos_attn_bwd(const relpos_problem* prob, const relpos_phi* phi,
  *                row terms D_i = sum_d dO_id O_id
  *  BWD_QUERY_PASS  dQ (partial when aQ is present) and dZ^Q per offset
  *  BWD_KEY_PASS    dK (partial when aK is present), dV and dZ^K per offset
+ *                  (with BWD_QUERY_PASS in the same call, both passes
+ *                  usually share one launch; the results are identical)
  *  BWD_CONTRACT    dQ += dZ^Q aQ, dK += dZ^K aK, daQ, daK, db, bucket fold
  * relpos_attn_fwd_stages / relpos_attn_bwd_stages take the same arguments as
  * relpos_attn_fwd / relpos_attn_bwd plus a stage mask; the stages given run
