@@ -137,10 +137,11 @@ __device__ inline void tile_store_tr(T* lds, const Chunk (&r)[TileCfg<T>::NCH], 
 // stored unpadded (ROWB bytes); inside a row the 16-byte chunks are permuted
 // by an XOR with swz(row).  The MFMA operand reads are ds_read_b128 of one
 // chunk column over 16 rows at a time, either 16 consecutive rows or the
-// sigma-permuted set {0-3, 8-11, 4-7, 12-15}; with 128-byte rows (16-bit
-// types) the swizzle below puts each such group of 16 rows, and each group
-// of 8 consecutive lanes within it, on distinct 16-byte bank groups of a
-// 256-byte LDS window, so the reads are free of bank conflicts.
+// sigma-permuted set {0-3, 8-11, 4-7, 12-15}; the transpose reads (below)
+// take two adjacent chunks of 4 consecutive rows per 16 lanes.  With
+// 128-byte rows (16-bit types) the swizzle below keeps both kinds of read
+// free of bank conflicts whether the LDS serves 128 bytes a cycle (8 lanes of
+// a 16-byte read, 16 lanes of an 8-byte read) or 256.
 // Rows beyond the valid count are zero-filled with ordinary LDS stores.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -155,13 +156,17 @@ struct DTile {
   static constexpr int PER_WAVE = 64 * CPR / 64 / 4;  // 64-lane loads per wave per tile
 };
 
-// Chunk permutation of row r.  16-bit: r & 7, with 5 XORed in for the odd
-// 8-row half (a linear map of the row bits whose restrictions to the even
-// rows, to the odd rows, to rows {0-3, 8-11} and to rows 0-7 are bijective).
+// Chunk permutation of row r.  16-bit, with r3..r0 the low row bits: chunk
+// bits 2..1 = (r1 r0) ^ r3 and bit 0 = r2 ^ r3.  Bits 2..1 take 4 distinct
+// values on every 4 aligned rows (so the chunk pairs {2m, 2m+1} of a
+// transpose read's 4 rows are disjoint), bit 2 differs between rows 4k and
+// 4k+2 and between 4k+1 and 4k+3 (its 4-chunk spans at 256 bytes), and the
+// map is a bijection on rows 0-7, 8-15, {0-3, 8-11}, {4-7, 12-15}, the even
+// rows of 16 and the odd rows of 16 (the 16-byte operand reads).
 template <typename T>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (sizeof(T) == 2) {
-    return (r & 7) ^ (((r >> 3) & 1) * 5);
+    return (((r & 3) ^ ((r >> 3) & 1)) << 1) | (((r >> 2) ^ (r >> 3)) & 1);
   } else {
     return (r + ((r >> 3) << 2)) & (DTile<T>::CPR - 1);
   }
