@@ -151,6 +151,95 @@ def copy_probe(torch, dev, mib):
     del a, c
 
 
+def stage_list(B_, run, separate_passes=False):
+    """The stages of one step, in order, as (name, call) pairs."""
+    stages = [("project", lambda: run.fwd(B_.FWD_PROJECT)),
+              ("attend", lambda: run.fwd(B_.FWD_ATTEND)),
+              ("prepare", lambda: run.bwd(B_.BWD_PREPARE)),
+              ("passes", lambda: run.bwd(B_.BWD_QUERY_PASS | B_.BWD_KEY_PASS)),
+              ("contract", lambda: run.bwd(B_.BWD_CONTRACT))]
+    if separate_passes:
+        # diagnostic: one launch per pass (the default step launches both at once)
+        k = [n for n, _ in stages].index("passes")
+        stages[k:k + 1] = [("query_pass", lambda: run.bwd(B_.BWD_QUERY_PASS)),
+                           ("key_pass", lambda: run.bwd(B_.BWD_KEY_PASS))]
+    return stages
+
+
+def time_stages(torch, dev, stages, warmup, steps):
+    """W untimed steps, then K timed steps with HIP events between the stage
+    calls on the launch stream.  Returns (average ms per stage, GPU ms per
+    step, wall seconds of the timed steps)."""
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for k, (_, fn) in enumerate(stages):
+            fn()
+            ev[s][k + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    stage_ms = {name: sum(ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(steps)) / steps
+                for k, (name, _) in enumerate(stages)}
+    gpu_ms = ev[0][0].elapsed_time(ev[steps - 1][len(stages)]) / steps
+    return stage_ms, gpu_ms, wall
+
+
+def run_sweep(args):
+    """The layer benchmark's length sweep: for each mechanism, N from 128 to
+    8192 at a fixed budget of 16384 tokens per batch (B = 16384 / N), 12
+    heads, d = 64, fp16, bidirectional.  One JSON line per (mechanism, N):
+    forward and backward ms, their TFLOP/s (4 d and 10 d per live pair) and
+    the device memory allocated beyond the inputs."""
+    import torch
+
+    import exact_relative_position_amd._binding as B_
+    from relpos_synth import make_inputs, sweep_workloads
+
+    dev = torch.device("cuda:0")
+    mechs = None if args.sweep == "all" else set(args.sweep.split(","))
+    for name, w in sweep_workloads().items():
+        if mechs is not None and name.split("_")[0] not in mechs:
+            continue
+        x = make_inputs(w)
+        t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+        torch.cuda.synchronize(dev)
+        mem_inputs = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
+                          tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True)
+        stage_ms, gpu_ms, _ = time_stages(torch, dev, stage_list(B_, run), args.warmup,
+                                          args.steps)
+        peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs
+        fwd_ms = stage_ms["project"] + stage_ms["attend"]
+        bwd_ms = stage_ms["prepare"] + stage_ms["passes"] + stage_ms["contract"]
+        kl = None if x["key_len"] is None else x["key_len"].numpy()
+        pairs = live_pairs(w, kl) * w.H
+        peak = PEAK_TFLOPS[w.dtype]
+        zbytes = run.zs.numel() if run.zs is not None else 0
+        out = {"metric": "layer sweep: fwd and bwd ms, TFLOP/s, extra memory", "config":
+               describe(w), "dtype": w.dtype, "fwd_ms": round(fwd_ms, 4),
+               "bwd_ms": round(bwd_ms, 4), "ms_per_step": round(gpu_ms, 4),
+               "fwd_tflops": round(4.0 * w.d * pairs / (fwd_ms * 1e-3) / 1e12, 2),
+               "bwd_tflops": round(10.0 * w.d * pairs / (bwd_ms * 1e-3) / 1e12, 2),
+               "fwd_pct_peak": round(100.0 * 4.0 * w.d * pairs / (fwd_ms * 1e-3) / 1e12 / peak,
+                                     2),
+               "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+               "peak_extra_bytes": int(peak_extra),
+               "peak_extra_bytes_fwd": int(run.O.numel() * run.O.element_size()
+                                           + run.lse.numel() * 4 + zbytes + run.ws_f.numel()),
+               "steps": args.steps, "warmup": args.warmup}
+        print(json.dumps(out), flush=True)
+        del run, t, x
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +249,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-passes", action="store_true",
                     help="time the query and key passes as two launches (diagnostic)")
+    ap.add_argument("--sweep", default=None, metavar="MECHS",
+                    help="instead of the one-line step benchmark, run the layer sweep "
+                         "(N = 128 .. 8192 at 16384 tokens) for 'all' or a comma list of "
+                         "shaw, txl, deberta, t5; one JSON line per point")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the warmup "
                          "(calibration of HBM byte counters)")
@@ -168,6 +261,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is a "
               "single-device operator and no multi-GPU figure is produced.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
 
     import torch
 
@@ -186,40 +282,10 @@ def main():
 
     run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
                       tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True)
-    stages = [("project", lambda: run.fwd(B_.FWD_PROJECT)),
-              ("attend", lambda: run.fwd(B_.FWD_ATTEND)),
-              ("prepare", lambda: run.bwd(B_.BWD_PREPARE)),
-              ("passes", lambda: run.bwd(B_.BWD_QUERY_PASS | B_.BWD_KEY_PASS)),
-              ("contract", lambda: run.bwd(B_.BWD_CONTRACT))]
-    if args.separate_passes:
-        # diagnostic: one launch per pass (the default step launches both at once)
-        k = [n for n, _ in stages].index("passes")
-        stages[k:k + 1] = [("query_pass", lambda: run.bwd(B_.BWD_QUERY_PASS)),
-                           ("key_pass", lambda: run.bwd(B_.BWD_KEY_PASS))]
-
-    for _ in range(args.warmup):
-        for _, fn in stages:
-            fn()
-    torch.cuda.synchronize(dev)
+    stages = stage_list(B_, run, args.separate_passes)
+    stage_ms, gpu_ms, wall = time_stages(torch, dev, stages, args.warmup, args.steps)
     peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for k, (_, fn) in enumerate(stages):
-            fn()
-            ev[s][k + 1].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-
     K = args.steps
-    stage_ms = {name: sum(ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(K)) / K
-                for k, (name, _) in enumerate(stages)}
-    gpu_ms = ev[0][0].elapsed_time(ev[K - 1][len(stages)]) / K
     fwd_ms = stage_ms["project"] + stage_ms["attend"]
     bwd_ms = sum(stage_ms[n] for n in ("prepare", "passes", "query_pass", "key_pass", "contract")
                  if n in stage_ms)

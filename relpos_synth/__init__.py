@@ -96,6 +96,30 @@ WORKLOADS = {
 }
 
 
+# The layer benchmark's length sweep (same setup section): a budget of 16384
+# tokens per batch, N from 128 to 8192 (B = 16384 / N), 12 heads, head dim
+# 64, FP16, bidirectional attention; each mechanism with its map and terms
+# as in the workloads above, without masks.
+SWEEP_NS = (128, 256, 512, 1024, 2048, 4096, 8192)
+SWEEP_TOKENS = 16384
+
+
+def sweep_workloads():
+    """Name -> Workload for every (mechanism, N) point of the sweep."""
+    mechs = {
+        "shaw": dict(phi=SHAW128, tau=1 / 8, has_aq=True),
+        "txl": dict(phi=IDENTITY, tau=1 / 8, has_aq=True, has_b=True, b_std=0.02),
+        "deberta": dict(phi=DEBERTA256, tau=1 / math.sqrt(192), has_aq=True, has_ak=True),
+        "t5": dict(phi=T5_32_128, tau=1.0, has_b=True, b_std=1.0),
+    }
+    out = {}
+    for m, kw in mechs.items():
+        for N in SWEEP_NS:
+            name = f"{m}_sweep_n{N}"
+            out[name] = Workload(name, SWEEP_TOKENS // N, 12, N, 64, "f16", **kw)
+    return out
+
+
 def make_inputs(w: Workload):
     """Return a dict of CPU torch tensors in the workload dtype (tables too).
 

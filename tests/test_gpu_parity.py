@@ -16,7 +16,8 @@ import torch
 
 from parity_util import compare, gpu_run, make_inputs, oracle_run, rel_err, require_gpu, \
     tolerances
-from relpos_synth import DEBERTA256, IDENTITY, SHAW16, T5_32_128, WORKLOADS, Workload
+from relpos_synth import DEBERTA256, IDENTITY, SHAW16, T5_32_128, WORKLOADS, Workload, \
+    sweep_workloads
 
 pytestmark = pytest.mark.gpu
 
@@ -195,8 +196,20 @@ FULL = ["shaw_n256_f32", "shaw_n8192_f16", "deberta_n8192_f16", "t5_n8192_f16",
 @pytest.mark.parametrize("name", FULL)
 def test_full_shape_parity(name):
     """Every output of head 0 (all batches) in full, O/LSE on sampled rows elsewhere."""
+    _full_parity(WORKLOADS[name])
+
+
+@pytest.mark.parametrize("name", list(sweep_workloads()))
+def test_sweep_parity(name):
+    """The layer sweep's points (N = 128 .. 8192 at 16384 tokens, each
+    mechanism): head 0 over every batch in full, O/LSE on sampled rows of a
+    few other heads."""
+    _full_parity(sweep_workloads()[name], n_others=2)
+
+
+def _full_parity(w, n_others=6):
     dev = require_gpu()
-    w = WORKLOADS[name]
+    name = w.name
     x = make_inputs(w)
     _say(f"[gpu] full-shape parity {name} B{w.B} H{w.H} N{w.N} {w.dtype}")
     got = gpu_run(w, x, dev)
@@ -217,7 +230,7 @@ def test_full_shape_parity(name):
         assert err <= tg, f"{name} {n}: {err:.3e}"
     rng = np.random.default_rng(1)
     rows = np.sort(rng.choice(w.N, size=min(w.N, 48), replace=False))
-    others = [(b, h) for b in range(w.B) for h in range(1, w.H)][:6]
+    others = [(b, h) for b in range(w.B) for h in range(1, w.H)][:n_others]
     if others:
         refo = oracle_run(w, x, bh=others, query_rows=rows, backward=False)
         for (b, h) in others:
