@@ -22,9 +22,9 @@ storage).
 Modules
 -------
 phi        offset maps phi: truncated (Shaw, DeBERTa as configured), T5 buckets,
-           identity (Transformer-XL).
+           DeBERTa log buckets, identity (Transformer-XL).
 attention  forward (O, LSE) and backward (dQ, dK, dV, daQ, daK, db).
 """
 
-from .phi import phi_rows, num_rows, t5_bucket  # noqa: F401
+from .phi import phi_rows, num_rows, t5_bucket, log_bucket  # noqa: F401
 from .attention import forward, backward  # noqa: F401

@@ -20,11 +20,21 @@ setup section lists the maps per mechanism:
   upper half), exact buckets for n < max_exact, logarithmic buckets from
   max_exact up to max_distance, clamped to the last bucket.
 
+* log buckets (DeBERTa): the setup section names "256 log buckets to 512
+  distance" for DeBERTa without printing the function; the reading adopted
+  is DeBERTa's published log-bucket position scheme (He et al., 2021), with
+  num_buckets = k, max_distance = m, mid = k / 2 and o = j - i: offsets with
+  |o| <= mid keep their own bucket o; beyond, the bucket is
+  sign(o) * (mid + ceil((mid - 1) * ln(|o| / mid) / ln((m - 1) / mid)));
+  the row is the bucket plus k, clamped to [0, 2k - 1] (R = 2k rows).  The
+  ceiling is taken exactly (integer arithmetic, no rounding of logarithms).
+
 A phi descriptor is a dict:
   {"kind": "truncated", "lo": int, "hi": int}
   {"kind": "identity"}
   {"kind": "t5", "num_buckets": int, "max_distance": int,
    "bidirectional": bool, "max_exact": int or None}
+  {"kind": "log", "num_buckets": int, "max_distance": int}
 """
 
 import math
@@ -63,6 +73,53 @@ def t5_bucket(o, num_buckets=32, max_distance=128, bidirectional=True, max_exact
     return base + out
 
 
+def _log_step(n, mid, m):
+    """ceil((mid - 1) * ln(n / mid) / ln((m - 1) / mid)) for integers n > mid,
+    m - 1 > mid, exactly.
+
+    With c = (m - 1) / mid > 1, the value is the least integer t with
+    t >= (mid - 1) * ln(n / mid) / ln(c), i.e. with c**t >= (n / mid)**(mid - 1),
+    i.e. (m - 1)**t * mid**(mid - 1) >= n**(mid - 1) * mid**t (positive
+    integers, compared exactly).  A float64 estimate gives the start; the
+    exact test moves it to the least such t.
+    """
+    def ok(t):
+        return (m - 1) ** t * mid ** (mid - 1) >= n ** (mid - 1) * mid ** t
+    t = max(0, math.ceil((mid - 1) * math.log(n / mid) / math.log((m - 1) / mid)))
+    while t > 0 and ok(t - 1):
+        t -= 1
+    while not ok(t):
+        t += 1
+    return t
+
+
+def log_bucket(o, num_buckets=256, max_distance=512):
+    """Row (in [0, 2 * num_buckets)) of the log-bucket map for offset(s) o = key - query:
+      n = |o|, mid = num_buckets // 2
+      bucket = o                                         if n <= mid
+             = sign(o) * (mid + _log_step(n, mid, m))      otherwise
+      row = clip(bucket + num_buckets, 0, 2 * num_buckets - 1)
+    """
+    o = np.asarray(o, dtype=np.int64)
+    k, m = int(num_buckets), int(max_distance)
+    mid = k // 2
+    steps = {}
+    out = np.empty(o.shape, dtype=np.int64)
+    flat = o.reshape(-1)
+    res = out.reshape(-1)
+    for idx in range(flat.size):
+        oo = int(flat[idx])
+        n = abs(oo)
+        if n <= mid:
+            b = oo
+        else:
+            if n not in steps:
+                steps[n] = _log_step(n, mid, m)
+            b = (mid + steps[n]) * (1 if oo > 0 else -1)
+        res[idx] = min(max(b + k, 0), 2 * k - 1)
+    return out
+
+
 def num_rows(phi, N):
     """Number of relation-table rows R that the map indexes."""
     kind = phi["kind"]
@@ -72,6 +129,8 @@ def num_rows(phi, N):
         return 2 * int(N) - 1
     if kind == "t5":
         return int(phi["num_buckets"])
+    if kind == "log":
+        return 2 * int(phi["num_buckets"])
     raise ValueError(f"unknown phi kind {kind!r}")
 
 
@@ -87,6 +146,8 @@ def phi_of_offset(phi, o, N):
     if kind == "t5":
         return t5_bucket(o, phi["num_buckets"], phi["max_distance"],
                          phi.get("bidirectional", True), phi.get("max_exact"))
+    if kind == "log":
+        return log_bucket(o, phi["num_buckets"], phi["max_distance"])
     raise ValueError(f"unknown phi kind {kind!r}")
 
 

@@ -1,5 +1,10 @@
 """Pins for the oracle's offset maps (oracle/phi.py).
 
+The log-bucket map (DeBERTa reading) is pinned by hand-derived rows
+(tests/golden/log_bucket_points.txt), by a second exact evaluation through
+60-digit decimal thresholds, and by structure (exact region equal to the
+truncated DeBERTa map, sign symmetry, monotonicity, every row reached).
+
 The T5 map is pinned three ways that do not share the oracle's float-log code:
 the integer closed form f(n) = min(15, 1 + bitlen(n^2)) for n >= 8 (exact, from
 8 + floor(2 log2(n/8)) = 2 + floor(log2 n^2)), the hand-derived bucket starts
@@ -12,7 +17,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import phi_rows, num_rows, t5_bucket
+from oracle import log_bucket, phi_rows, num_rows, t5_bucket
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -106,3 +111,77 @@ def test_small_n_rows(N):
         r = phi_rows(phi, N)
         assert r.shape == (2 * N - 1,)
         assert r.min() >= 0 and r.max() < num_rows(phi, N)
+
+
+def test_log_bucket_golden_points():
+    rows = [l.split() for l in open(os.path.join(GOLD, "log_bucket_points.txt"))
+            if l.strip() and not l.startswith("#")]
+    for o, r in ((int(a), int(b)) for a, b in rows):
+        assert int(log_bucket(o, 256, 512)) == r, o
+
+
+def _decimal_buckets(n_max, k, m):
+    """Buckets (before the row clamp) of offsets 0..n_max by thresholds: for
+    n > mid the step t is the least t with mid * ((m-1)/mid)^(t/(mid-1)) >= n,
+    the thresholds taken at 60 significant digits (an evaluation independent
+    of the oracle's)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    mid = k // 2
+    c = (Decimal(m - 1) / Decimal(mid)).ln()
+    thr = []
+    t = 0
+    while True:
+        u = Decimal(mid) * (c * Decimal(t) / Decimal(mid - 1)).exp()
+        thr.append(u)
+        if u >= n_max or t > 4 * k:
+            break
+        t += 1
+    out = []
+    j = 0
+    for n in range(n_max + 1):
+        if n <= mid:
+            out.append(n)
+            continue
+        while thr[j] < n:
+            j += 1
+        out.append(mid + j)
+    return np.array(out, dtype=np.int64)
+
+
+@pytest.mark.parametrize("k,m", [(256, 512), (64, 300), (32, 40)])
+def test_log_bucket_matches_decimal_thresholds(k, m):
+    n = np.arange(0, 6000)
+    bucket = _decimal_buckets(5999, k, m)
+    assert np.array_equal(log_bucket(n, k, m), np.minimum(bucket + k, 2 * k - 1))
+    # negative offsets take the negated bucket
+    assert np.array_equal(log_bucket(-n, k, m), np.maximum(k - bucket, 0))
+
+
+def test_log_bucket_structure():
+    k, m = 256, 512
+    o = np.arange(-20000, 20001)
+    r = log_bucket(o, k, m)
+    assert r.min() == 0 and r.max() == 2 * k - 1
+    assert np.all(np.diff(r) >= 0)
+    assert set(r.tolist()) == set(range(2 * k))
+    near = np.abs(o) <= k // 2
+    # inside the exact range the map equals the truncated DeBERTa map
+    assert np.array_equal(r[near], np.clip(o[near], -256, 255) + 256)
+    inner = np.abs(o) <= m - 1
+    assert np.array_equal(r[inner][::-1], 2 * k - r[inner])
+    assert num_rows({"kind": "log", "num_buckets": k, "max_distance": m}, 8192) == 2 * k
+
+
+def test_log_bucket_float64_has_no_near_ties():
+    """The direct float64 evaluation of the ceiling equals the exact one for
+    every offset below 20000 at these parameters, so a float64 evaluation
+    (the HIP path's) can be bit-exact."""
+    import math
+    for k, m in ((256, 512), (64, 300), (32, 40)):
+        mid = k // 2
+        n = np.arange(mid + 1, 20000)
+        f = np.array([mid + math.ceil(math.log(x / mid) / math.log((m - 1) / mid) * (mid - 1))
+                      for x in n.tolist()])
+        want = np.minimum(f + k, 2 * k - 1)
+        assert np.array_equal(log_bucket(n, k, m), want), (k, m)
