@@ -60,6 +60,8 @@ def describe(w):
         ps = f"truncated[{phi['lo']},{phi['hi']}]"
     elif phi["kind"] == "t5":
         ps = f"t5[{phi['num_buckets']} buckets, max {phi['max_distance']}]"
+    elif phi["kind"] == "log":
+        ps = f"log[{phi['num_buckets']} buckets, max {phi['max_distance']}]"
     else:
         ps = "identity"
     terms = "+".join(t for t, f in (("aQ", w.has_aq), ("aK", w.has_ak), ("b", w.has_b)) if f)

@@ -18,7 +18,7 @@ RELPOS_OK = 0
 STATUS = {0: "RELPOS_OK", -1: "RELPOS_ERR_INVALID_ARG", -2: "RELPOS_ERR_UNSUPPORTED",
           -3: "RELPOS_ERR_WORKSPACE", -4: "RELPOS_ERR_HIP"}
 DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-PHI_KIND = {"truncated": 0, "t5": 1, "identity": 2}
+PHI_KIND = {"truncated": 0, "t5": 1, "identity": 2, "log": 3}
 MASK_CAUSAL, MASK_KEY_PADDING = 1, 2
 TERM_AQ, TERM_AK, TERM_B = 1, 2, 4
 PASS_FWD, PASS_BWD = 0, 1
@@ -97,7 +97,7 @@ def _check(status):
 
 
 def phi_struct(phi):
-    """C descriptor of a phi dict ({"kind": "truncated"|"t5"|"identity", ...})."""
+    """C descriptor of a phi dict ({"kind": "truncated"|"t5"|"identity"|"log", ...})."""
     kind = phi["kind"]
     s = Phi()
     s.kind = PHI_KIND[kind]
@@ -108,6 +108,9 @@ def phi_struct(phi):
         s.max_exact = int(phi.get("max_exact") or 0)
         s.max_distance = int(phi["max_distance"])
         s.bidirectional = 1 if phi.get("bidirectional", True) else 0
+    elif kind == "log":
+        s.num_buckets = int(phi["num_buckets"])
+        s.max_distance = int(phi["max_distance"])
     return s
 
 

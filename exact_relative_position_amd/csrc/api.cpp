@@ -3,7 +3,7 @@
 //
 // Forward (pipeline section of "Fast and Exact Relative-Position Attention via
 // Structure-Aware Kernels", nanless.github.io digest):
-//   map tables (T5 unfold) -> relation projection of the reachable window ->
+//   map tables (bucket unfold) -> relation projection of the reachable window ->
 //   fused tiled forward.
 // Backward (backward section of the same page):
 //   the padded row terms (LSE, D, the key pass's seeds) ->
@@ -18,7 +18,7 @@
 
 #include "geometry.hpp"
 #include "relpos_attn.h"
-#include "t5.hpp"
+#include "buckets.hpp"
 
 namespace relpos {
 hipError_t launch_fwd(int dtype, const AttnArgs& a, hipStream_t st);
@@ -65,7 +65,7 @@ struct Plan {
   PhiArgs phi{};
   int R = 0;       // rows of the caller's tables
   int Runf = 0;    // rows of the unfolded truncated map
-  bool t5 = false;
+  bool bucketed = false;  // T5 or log buckets: unfolded, gradients folded back
   bool has_aq = false, has_ak = false, has_b = false;
   bool keypad = false;
   int64_t aq_hs = 0, ak_hs = 0, b_hs = 0;
@@ -118,6 +118,32 @@ relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& 
       hi = p.bidirectional ? nsat : 0;
       return RELPOS_OK;
     }
+    case RELPOS_PHI_BUCKET_LOG: {
+      const int k = p.num_buckets, m = p.max_distance;
+      if (k < 4 || k > 4096 || (k & 1))
+        return fail(RELPOS_ERR_INVALID_ARG, "log-bucket num_buckets must be even, in [4, 4096]");
+      if (m < k / 2 + 2 || m > (1 << 24))
+        return fail(RELPOS_ERR_INVALID_ARG, "log-bucket max_distance must be in [k/2 + 2, 2^24]");
+      // the row is monotone in o and reaches 2k - 1 by o = m - 1 and 0 by
+      // o = -m: the first offsets of the two constant runs
+      int nhi = m - 1, nlo = m;
+      for (int n = 0; n < m; ++n) {
+        if (log_bucket_dev(n, k, m) == 2 * k - 1) {
+          nhi = n;
+          break;
+        }
+      }
+      for (int n = 0; n <= m; ++n) {
+        if (log_bucket_dev(-n, k, m) == 0) {
+          nlo = n;
+          break;
+        }
+      }
+      R = 2 * k;
+      lo = -nlo;
+      hi = nhi;
+      return RELPOS_OK;
+    }
     default:
       return fail(RELPOS_ERR_INVALID_ARG, "unknown phi kind");
   }
@@ -153,7 +179,7 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   pl.has_ak = terms & RELPOS_TERM_AK;
   pl.has_b = terms & RELPOS_TERM_B;
   pl.keypad = mask->flags & RELPOS_MASK_KEY_PADDING;
-  pl.t5 = phi->kind == RELPOS_PHI_BUCKET_T5;
+  pl.bucketed = phi->kind == RELPOS_PHI_BUCKET_T5 || phi->kind == RELPOS_PHI_BUCKET_LOG;
   const int64_t Nn = pl.N > 0 ? pl.N : 1;
   int64_t R, lo, hi;
   relpos_status s = unfold_range(*phi, Nn, R, lo, hi);
@@ -290,7 +316,7 @@ bool need_bunf(const Plan& pl) { return pl.has_b && !pl.has_aq; }
 
 size_t carve_fwd(const Plan& pl, bool zsave_given, void* base, WsFwd& w) {
   Carve c(base);
-  if (pl.t5) w.fold = c.take<int32_t>(sizeof(int32_t) * pl.Runf);
+  if (pl.bucketed) w.fold = c.take<int32_t>(sizeof(int32_t) * pl.Runf);
   if (need_bunf(pl)) w.bunf = c.take<float>(sizeof(float) * pl.Runf * pl.ho_b);
   if (!zsave_given) {
     if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
@@ -302,7 +328,7 @@ size_t carve_fwd(const Plan& pl, bool zsave_given, void* base, WsFwd& w) {
 size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
   Carve c(base);
   const size_t bhn = (size_t)pl.B * pl.H * pl.N;
-  if (pl.t5) {
+  if (pl.bucketed) {
     w.fold = c.take<int32_t>(sizeof(int32_t) * pl.Runf);
     w.ub = c.take<int32_t>(sizeof(int32_t) * pl.R);
     w.ue = c.take<int32_t>(sizeof(int32_t) * pl.R);
@@ -358,7 +384,7 @@ int terms_of(const void* aQ, const void* aK, const void* b) {
   return (aQ ? RELPOS_TERM_AQ : 0) | (aK ? RELPOS_TERM_AK : 0) | (b ? RELPOS_TERM_B : 0);
 }
 
-// Map tables needed by both passes: T5 fold table (+ ranges), unfolded bias.
+// Map tables needed by both passes: bucket fold table (+ ranges), unfolded bias.
 // Column contraction: 16-bit problems stream their dZ rows through the
 // 64-row tiled kernel (grouped windows shift the loaded columns per group);
 // fp32 inputs use the general kernel.
@@ -369,12 +395,12 @@ hipError_t cols(const Plan& pl, const ColsArgs& c, int Ho, hipStream_t st) {
 
 relpos_status prepare_tables(const Plan& pl, const void* b, int32_t* fold, int32_t* ub,
                              int32_t* ue, float* bunf, hipStream_t st) {
-  if (pl.t5) {
+  if (pl.bucketed) {
     relpos_status s = hip_check(launch_phi_fold(pl.phi, fold, ub, ue, pl.R, st), "phi fold");
     if (s != RELPOS_OK) return s;
   }
   if (bunf) {
-    BiasArgs ba{b, pl.b_hs, pl.t5 ? fold : nullptr, bunf, pl.ho_b, pl.Runf};
+    BiasArgs ba{b, pl.b_hs, pl.bucketed ? fold : nullptr, bunf, pl.ho_b, pl.Runf};
     relpos_status s = hip_check(launch_bias_unfold(pl.dtype, ba, st), "bias unfold");
     if (s != RELPOS_OK) return s;
   }
@@ -392,7 +418,7 @@ relpos_status project(const Plan& pl, const relpos_problem* prob, const void* Q,
     pa.tab_hs = pl.aq_hs;
     pa.bias = pl.has_b ? b : nullptr;
     pa.bias_hs = pl.b_hs;
-    pa.fold = pl.t5 ? fold : nullptr;
+    pa.fold = pl.bucketed ? fold : nullptr;
     pa.z = zq;
     pa.B = pl.B;
     pa.H = pl.H;
@@ -410,7 +436,7 @@ relpos_status project(const Plan& pl, const relpos_problem* prob, const void* Q,
     pa.tab = aK;
     pa.tab_hs = pl.ak_hs;
     pa.bias = nullptr;
-    pa.fold = pl.t5 ? fold : nullptr;
+    pa.fold = pl.bucketed ? fold : nullptr;
     pa.z = zk;
     pa.B = pl.B;
     pa.H = pl.H;
@@ -741,7 +767,7 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     return pl.dtype == 1 ? (void*)((uint16_t*)t + (size_t)ho * tu_hs) : nullptr;
   };
   if (pl.has_aq) {
-    TabUnfoldArgs t{aQ, pl.aq_hs, pl.t5 ? w.fold : nullptr, w.tunf_q, tab_lo(w.tunf_q, pl.ho_aq),
+    TabUnfoldArgs t{aQ, pl.aq_hs, pl.bucketed ? w.fold : nullptr, w.tunf_q, tab_lo(w.tunf_q, pl.ho_aq),
                     pl.ho_aq, pl.Runf};
     if ((s = hip_check(launch_tab_unfold(pl.dtype, t, st), "table unfold aQ")) != RELPOS_OK)
       return s;
@@ -750,7 +776,7 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     if ((s = hip_check(launch_rows(pl.dtype, r, st), "contraction dQ")) != RELPOS_OK) return s;
   }
   if (pl.has_ak) {
-    TabUnfoldArgs t{aK, pl.ak_hs, pl.t5 ? w.fold : nullptr, w.tunf_k, tab_lo(w.tunf_k, pl.ho_ak),
+    TabUnfoldArgs t{aK, pl.ak_hs, pl.bucketed ? w.fold : nullptr, w.tunf_k, tab_lo(w.tunf_k, pl.ho_ak),
                     pl.ho_ak, pl.Runf};
     if ((s = hip_check(launch_tab_unfold(pl.dtype, t, st), "table unfold aK")) != RELPOS_OK)
       return s;
@@ -768,8 +794,8 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     if ((s = hip_check(launch_xsplit(x, st), "split K")) != RELPOS_OK) return s;
   }
   // table gradients: dZ^T Q, dZ^T K, column sums of dZ^Q; then the fold
-  const int32_t* ub = pl.t5 ? w.ub : nullptr;
-  const int32_t* ue = pl.t5 ? w.ue : nullptr;
+  const int32_t* ub = pl.bucketed ? w.ub : nullptr;
+  const int32_t* ue = pl.bucketed ? w.ue : nullptr;
   const bool joint_b = pl.has_aq && pl.has_b && pl.ho_aq == pl.ho_b && pl.split_q == pl.split_b;
   if (pl.has_aq) {
     ColsArgs c{};

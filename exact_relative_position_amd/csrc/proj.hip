@@ -19,7 +19,7 @@
 
 #include "device.hpp"
 #include "tiles.hpp"
-#include "t5.hpp"
+#include "buckets.hpp"
 
 namespace relpos {
 
@@ -27,6 +27,7 @@ __device__ inline int phi_row(const PhiArgs& p, int o) {
   switch (p.kind) {
     case 0: return imin(imax(o, p.lo), p.hi) - p.lo;
     case 1: return t5_bucket_dev(o, p.num_buckets, p.max_exact, p.max_distance, p.bidirectional);
+    case 3: return log_bucket_dev(o, p.num_buckets, p.max_distance);
     default: return o + p.N - 1;
   }
 }
@@ -44,20 +45,26 @@ __global__ void phi_fold_kernel(PhiArgs p, int32_t* fold) {
   if (u < R) fold[u] = phi_row(p, u + p.lo_unf);
 }
 
-// For each table row k: the unfolded rows [ub[k], ue[k]) that copy it (each
-// bucket covers one contiguous offset range; empty buckets get ub = ue = 0).
-__global__ void fold_range_kernel(const int32_t* fold, int Runf, int R, int32_t* ub, int32_t* ue) {
+// For each table row k: the unfolded rows [ub[k], ue[k]) that copy it.  Each
+// bucket covers one contiguous offset range, so the unfolded row u that
+// starts (ends) a run of equal rows writes its row's ub (ue); buckets with no
+// unfolded row keep ub = ue = 0 from fold_range_clear_kernel (launched
+// first: a fill kernel rather than a memset, so the sequence can be
+// captured in a graph).
+__global__ void fold_range_clear_kernel(int R, int32_t* ub, int32_t* ue) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= R) return;
-  int b = -1, e = -1;
-  for (int u = 0; u < Runf; ++u) {
-    if (fold[u] == k) {
-      if (b < 0) b = u;
-      e = u + 1;
-    }
+  if (k < R) {
+    ub[k] = 0;
+    ue[k] = 0;
   }
-  ub[k] = b < 0 ? 0 : b;
-  ue[k] = b < 0 ? 0 : e;
+}
+
+__global__ void fold_range_kernel(const int32_t* fold, int Runf, int32_t* ub, int32_t* ue) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= Runf) return;
+  const int k = fold[u];
+  if (u == 0 || fold[u - 1] != k) ub[k] = u;
+  if (u == Runf - 1 || fold[u + 1] != k) ue[k] = u + 1;
 }
 
 // bunf[h][u] = b[h][fold[u]] as fp32 (fold null: identity)
@@ -171,8 +178,11 @@ hipError_t launch_phi_fold(const PhiArgs& p, int32_t* fold, int32_t* ub, int32_t
   hipLaunchKernelGGL(phi_fold_kernel, dim3((Runf + 255) / 256), dim3(256), 0, st, p, fold);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !ub) return e;
-  hipLaunchKernelGGL(fold_range_kernel, dim3((R + 255) / 256), dim3(256), 0, st, (const int32_t*)fold,
-                     Runf, R, ub, ue);
+  hipLaunchKernelGGL(fold_range_clear_kernel, dim3((R + 255) / 256), dim3(256), 0, st, R, ub, ue);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fold_range_kernel, dim3((Runf + 255) / 256), dim3(256), 0, st,
+                     (const int32_t*)fold, Runf, ub, ue);
   return hipGetLastError();
 }
 

@@ -59,19 +59,27 @@ typedef enum relpos_dtype { RELPOS_F32 = 0, RELPOS_F16 = 1, RELPOS_BF16 = 2 } re
  *            library the bucketed map is unfolded into a truncated map whose
  *            rows are copies of bucket rows (section on constant tiles), and
  *            the copied gradient columns are folded back in ascending offset.
- *  IDENTITY (Transformer-XL): r = o + N - 1, R = 2N - 1. */
+ *  IDENTITY (Transformer-XL): r = o + N - 1, R = 2N - 1.
+ *  BUCKET_LOG (DeBERTa; the page names 256 log buckets to distance 512): the
+ *            log-bucket positions of DeBERTa (num_buckets = k, max_distance
+ *            = m, mid = k / 2): bucket = o for |o| <= mid, otherwise
+ *            sign(o) (mid + ceil((mid - 1) ln(|o| / mid) / ln((m - 1) / mid)));
+ *            r = clip(bucket + k, 0, 2k - 1), R = 2k.  Unfolded and folded
+ *            like BUCKET_T5. */
 typedef enum relpos_phi_kind {
   RELPOS_PHI_TRUNCATED = 0,
   RELPOS_PHI_BUCKET_T5 = 1,
-  RELPOS_PHI_IDENTITY = 2
+  RELPOS_PHI_IDENTITY = 2,
+  RELPOS_PHI_BUCKET_LOG = 3
 } relpos_phi_kind;
 
 typedef struct relpos_phi {
   int32_t kind;           /* relpos_phi_kind */
   int32_t lo, hi;         /* TRUNCATED: lo <= hi */
-  int32_t num_buckets;    /* BUCKET_T5: >= 2 (even when bidirectional) */
+  int32_t num_buckets;    /* BUCKET_T5: >= 2 (even when bidirectional);
+                             BUCKET_LOG: k, even, in [4, 4096] (the table has 2k rows) */
   int32_t max_exact;      /* BUCKET_T5: 0 = default (half of the buckets per side, halved) */
-  int32_t max_distance;   /* BUCKET_T5: > max_exact */
+  int32_t max_distance;   /* BUCKET_T5: > max_exact; BUCKET_LOG: m, k / 2 + 2 <= m <= 2^24 */
   int32_t bidirectional;  /* BUCKET_T5: 1 = keys after the query use the upper half */
 } relpos_phi;
 
@@ -174,7 +182,7 @@ relpos_status relpos_attn_bwd(const relpos_problem* prob, const relpos_phi* phi,
  * kernel).  The pipeline section of the page orders the forward as relation
  * projection, then the fused tiled attention; the backward section as the
  * query-parallel pass, the key-parallel pass, then the final contraction.
- *  FWD_PROJECT   map tables (T5 unfold) and Z^Q, Z^K of the reachable window
+ *  FWD_PROJECT   map tables (bucket unfold) and Z^Q, Z^K of the reachable window
  *                (Eq. 3; section on the grouped reachable range)
  *  FWD_ATTEND    fused forward: O and LSE
  *  BWD_PREPARE   map tables, projections (only when zsave is NULL) and the
@@ -220,8 +228,8 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
 
 /* Host-side facts about a map at length N: R (rows of the caller's tables),
  * and the truncated map the library unfolds it into, [lo_unf, hi_unf]
- * (R_unf = hi_unf - lo_unf + 1 rows).  For T5 the unfolded thresholds are
- * the first offsets beyond which the bucket no longer changes. */
+ * (R_unf = hi_unf - lo_unf + 1 rows).  For the bucketed maps the unfolded
+ * thresholds are the first offsets beyond which the row no longer changes. */
 relpos_status relpos_phi_info(const relpos_phi* phi, int64_t N, int64_t* R, int64_t* lo_unf,
                               int64_t* hi_unf);
 

@@ -65,6 +65,8 @@ def rows_for(phi, N):
         return 2 * N - 1
     if kind == "t5":
         return phi["num_buckets"]
+    if kind == "log":
+        return 2 * phi["num_buckets"]
     raise ValueError(kind)
 
 
@@ -74,6 +76,8 @@ DEBERTA256 = {"kind": "truncated", "lo": -256, "hi": 255}
 T5_32_128 = {"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": True,
              "max_exact": 8}
 IDENTITY = {"kind": "identity"}
+# DeBERTa's own map on the pages: 256 log buckets to distance 512 (2 * 256 rows)
+DEBERTA_LOG = {"kind": "log", "num_buckets": 256, "max_distance": 512}
 
 WORKLOADS = {
     # Shaw truncation +-16, 1x1x256x64, fp32, aQ only, seed 0.
@@ -84,6 +88,10 @@ WORKLOADS = {
     # DeBERTa-style content-to-position and position-to-content, clip(-256, 255).
     "deberta_n8192_f16": Workload("deberta_n8192_f16", 1, 12, 8192, 64, "f16", DEBERTA256,
                                   1 / math.sqrt(192), has_aq=True, has_ak=True),
+    # The same with DeBERTa's log-bucket map (256 buckets to distance 512).
+    "deberta_log_n8192_f16": Workload("deberta_log_n8192_f16", 1, 12, 8192, 64, "f16",
+                                      DEBERTA_LOG, 1 / math.sqrt(192), has_aq=True,
+                                      has_ak=True),
     # T5 32 bidirectional buckets to distance 128, scalar bias, key padding.
     "t5_n8192_f16": Workload("t5_n8192_f16", 1, 12, 8192, 64, "f16", T5_32_128, 1.0,
                              has_b=True, key_padding=True, b_std=1.0),
@@ -99,7 +107,8 @@ WORKLOADS = {
 # The layer benchmark's length sweep (same setup section): a budget of 16384
 # tokens per batch, N from 128 to 8192 (B = 16384 / N), 12 heads, head dim
 # 64, FP16, bidirectional attention; each mechanism with its map and terms
-# as in the workloads above, without masks.
+# as in the workloads above, without masks, and DeBERTa with the pages'
+# log-bucket map.
 SWEEP_NS = (128, 256, 512, 1024, 2048, 4096, 8192)
 SWEEP_TOKENS = 16384
 
@@ -109,7 +118,7 @@ def sweep_workloads():
     mechs = {
         "shaw": dict(phi=SHAW128, tau=1 / 8, has_aq=True),
         "txl": dict(phi=IDENTITY, tau=1 / 8, has_aq=True, has_b=True, b_std=0.02),
-        "deberta": dict(phi=DEBERTA256, tau=1 / math.sqrt(192), has_aq=True, has_ak=True),
+        "deberta": dict(phi=DEBERTA_LOG, tau=1 / math.sqrt(192), has_aq=True, has_ak=True),
         "t5": dict(phi=T5_32_128, tau=1.0, has_b=True, b_std=1.0),
     }
     out = {}

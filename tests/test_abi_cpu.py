@@ -73,6 +73,25 @@ def test_phi_info_closed_forms():
     R, lo, hi = b.phi_info({"kind": "t5", "num_buckets": 32, "max_distance": 128,
                             "bidirectional": False}, 100)
     assert (R, hi) == (32, 0) and lo < 0
+    # log buckets 256 to 512 (hand-derived in tests/golden/log_bucket_points.txt):
+    # 2 * 256 rows, the last row from o = 506 on, the first from o = -512 down
+    assert b.phi_info({"kind": "log", "num_buckets": 256, "max_distance": 512}, 8192) == \
+        (512, -512, 506)
+
+
+@pytest.mark.parametrize("k,m", [(256, 512), (64, 300), (32, 40), (4, 5)])
+def test_phi_info_log_matches_oracle(k, m):
+    """The unfolded thresholds are where the oracle's rows reach their two
+    constant runs."""
+    import numpy as np
+    from oracle import log_bucket
+    n = np.arange(0, 2 * m + 2)
+    pos = log_bucket(n, k, m)
+    neg = log_bucket(-n, k, m)
+    hi = int(np.argmax(pos == 2 * k - 1))
+    lo = -int(np.argmax(neg == 0))
+    assert b.phi_info({"kind": "log", "num_buckets": k, "max_distance": m}, 4096) == \
+        (2 * k, lo, hi)
 
 
 def test_zsave_size_closed_form(L):
@@ -124,6 +143,9 @@ def test_bad_problem(L, field, value, code):
     {"kind": "t5", "num_buckets": 32, "max_distance": 4, "bidirectional": True},
     {"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": True,
      "max_exact": 16},
+    {"kind": "log", "num_buckets": 255, "max_distance": 512},
+    {"kind": "log", "num_buckets": 2, "max_distance": 512},
+    {"kind": "log", "num_buckets": 256, "max_distance": 129},
 ])
 def test_bad_phi(L, phi):
     st, _ = _ws(L, _prob(), b.phi_struct(phi))

@@ -16,8 +16,8 @@ import torch
 
 from parity_util import compare, gpu_run, make_inputs, oracle_run, rel_err, require_gpu, \
     tolerances
-from relpos_synth import DEBERTA256, IDENTITY, SHAW16, T5_32_128, WORKLOADS, Workload, \
-    sweep_workloads
+from relpos_synth import DEBERTA256, DEBERTA_LOG, IDENTITY, SHAW16, T5_32_128, WORKLOADS, \
+    Workload, sweep_workloads
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +67,14 @@ SMALL = [
     Workload("wide_band_causal_keypad_f16", 2, 1, 1050, 64, "f16",
              {"kind": "truncated", "lo": -1040, "hi": 1030}, 1 / 8, has_aq=True, has_ak=True,
              causal=True, key_padding=True, pad_frac=0.2),
+    # log buckets: unfolded to [-300, 279] (580 columns: staged key-pass band
+    # stores), every term, copied columns folded back
+    Workload("log_buckets_f16", 1, 2, 900, 64, "f16",
+             {"kind": "log", "num_buckets": 64, "max_distance": 300}, 1 / 8, has_aq=True,
+             has_ak=True, has_b=True),
+    Workload("log_buckets_keypad_bf16", 2, 2, 420, 64, "bf16",
+             {"kind": "log", "num_buckets": 32, "max_distance": 40}, 1 / 8, has_aq=True,
+             has_b=True, key_padding=True, pad_frac=0.3),
 ]
 
 
@@ -189,8 +197,8 @@ def test_fused_passes_match_separate_launches(causal):
         assert torch.equal(got[0][n], got[1][n]), n
 
 
-FULL = ["shaw_n256_f32", "shaw_n8192_f16", "deberta_n8192_f16", "t5_n8192_f16",
-        "txl_n4096_bf16", "txl_n8192_f16"]
+FULL = ["shaw_n256_f32", "shaw_n8192_f16", "deberta_n8192_f16", "deberta_log_n8192_f16",
+        "t5_n8192_f16", "txl_n4096_bf16", "txl_n8192_f16"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -249,7 +257,10 @@ def test_phi_tables_bit_exact():
              ({"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": False},
               5000),
              ({"kind": "t5", "num_buckets": 64, "max_distance": 1000, "bidirectional": True},
-              20000)]
+              20000),
+             (DEBERTA_LOG, 8192),
+             ({"kind": "log", "num_buckets": 64, "max_distance": 300}, 2000),
+             ({"kind": "log", "num_buckets": 32, "max_distance": 40}, 20000)]
     for phi, N in cases:
         _say(f"[gpu] phi rows {phi['kind']} N{N}")
         rows, fold = rp.phi_rows(phi, N, device=dev)
