@@ -95,6 +95,49 @@ def test_small_parity(w):
     _say(f"  {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in rep.items()))
 
 
+def _random_workloads(n, seed=7):
+    """Seeded random small configurations: map kind and parameters, terms,
+    masks, dtype, shared tables and a ragged N (fixed by the seed, so every
+    run checks the same cases)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        N = int(rng.integers(1, 700))
+        kind = ["truncated", "t5", "identity", "log"][c % 4]
+        if kind == "truncated":
+            lo = int(rng.integers(-300, 1))
+            phi = {"kind": kind, "lo": lo, "hi": int(rng.integers(lo, 300))}
+        elif kind == "t5":
+            nb = int(rng.choice([8, 16, 32, 64]))
+            bi = bool(rng.integers(0, 2))
+            per = nb // 2 if bi else nb
+            phi = {"kind": kind, "num_buckets": nb, "bidirectional": bi,
+                   "max_distance": int(rng.integers(per // 2 + 1, 400))}
+        elif kind == "identity":
+            phi = {"kind": kind}
+        else:
+            k = int(rng.choice([4, 16, 64, 128]))
+            phi = {"kind": kind, "num_buckets": k,
+                   "max_distance": int(rng.integers(k // 2 + 2, 3 * k))}
+        terms = rng.integers(0, 2, size=3).astype(bool)
+        dtype = ["f16", "bf16", "f32"][int(rng.integers(0, 3))]
+        out.append(Workload(f"random{c}_{kind}_{dtype}", int(rng.integers(1, 3)),
+                            int(rng.integers(1, 4)), N, 64, dtype, phi,
+                            float(rng.choice([1 / 8, 0.3, 1.0])), has_aq=bool(terms[0]),
+                            has_ak=bool(terms[1]), has_b=bool(terms[2]),
+                            causal=bool(rng.integers(0, 2)),
+                            key_padding=bool(rng.integers(0, 2)), pad_frac=0.4,
+                            shared_tables=bool(rng.integers(0, 2)), b_std=0.3,
+                            seed=100 + c))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_workloads(16), ids=lambda w: w.name)
+def test_random_small_parity(w):
+    """Seeded random configurations, every output against the oracle."""
+    test_small_parity(w)
+
+
 def test_fully_masked_batch():
     dev = require_gpu()
     w = Workload("dead_rows_f16", 2, 2, 200, 64, "f16", SHAW16, 1 / 8, has_aq=True, has_b=True,
