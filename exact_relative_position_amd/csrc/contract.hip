@@ -750,10 +750,32 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
   }
 }
 
+// s += the `splits` values at p, p + stride, ... in that order.  BATCH: the
+// loads of 8 splits are issued together before their adds (many splits);
+// otherwise one at a time (few splits: a smaller kernel, for launches of
+// many short blocks).
+template <bool BATCH>
+__device__ __forceinline__ float sum_splits(float s, const float* p, int64_t stride, int splits) {
+  if constexpr (!BATCH) {
+    for (int sp = 0; sp < splits; ++sp) s += p[sp * stride];
+    return s;
+  }
+  for (int sp = 0; sp < splits; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = sp + j < splits ? p[(sp + j) * stride] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (sp + j < splits) s += v[j];
+  }
+  return s;
+}
+
 // out[ho][k][d] = sum_{u in [ub[k], ue[k])} sum_s part[s][ho][u][d], u ascending.
 // Block (k4, ho): table rows k = 4 k4 .. 4 k4 + 3 of head ho, one thread per
 // (row, d); lane d = 0 also sums the bias column.  Fixed order: u ascending,
 // then the splits.
+template <bool BATCH>
 __global__ __launch_bounds__(256) void fold_kernel(FoldArgs a) {
   const int d = threadIdx.x & 63;
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -766,14 +788,13 @@ __global__ __launch_bounds__(256) void fold_kernel(FoldArgs a) {
     const float* p = a.part + ((int64_t)ho * a.Rpad) * 64 + d;
     float s = 0.f;
     for (int u = b; u < e; ++u)
-      for (int sp = 0; sp < a.splits; ++sp) s += p[(sp * sstride + u) * 64];
+      s = sum_splits<BATCH>(s, p + (int64_t)u * 64, sstride * 64, a.splits);
     a.out[((int64_t)ho * a.R + k) * 64 + d] = s;
   }
   if (a.outb && d == 0) {
     const float* p = a.partb + (int64_t)ho * a.Rpad;
     float s = 0.f;
-    for (int u = b; u < e; ++u)
-      for (int sp = 0; sp < a.splits; ++sp) s += p[sp * sstride + u];
+    for (int u = b; u < e; ++u) s = sum_splits<BATCH>(s, p + u, sstride, a.splits);
     a.outb[(int64_t)ho * a.R + k] = s;
   }
 }
@@ -833,8 +854,11 @@ hipError_t launch_cols(int dtype, const ColsArgs& a, int Ho, hipStream_t st) {
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t st) {
   if (a.Ho <= 0 || a.R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)((a.R + 3) / 4), (unsigned)a.Ho), dim3(256), 0,
-                     st, a);
+  const dim3 grid((unsigned)((a.R + 3) / 4), (unsigned)a.Ho);
+  if (a.splits > 4)
+    hipLaunchKernelGGL(fold_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(fold_kernel<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
