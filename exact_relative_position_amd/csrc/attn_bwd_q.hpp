@@ -69,6 +69,7 @@ struct BwdQ {
   QCtx c;
   int w, lane, hl, l32, i0, iw0, nkt, N, kv_lim;
   float cst_lo, cst_hi, sc2, tau, lse2, Dl;
+  f32x16 dseed;  // -D in every entry: the starting value of dP
   bool need_dz;
   const T* Kb;
   const T* Vb;
@@ -171,7 +172,8 @@ struct BwdQ {
       else
         s = qside_scores<T>(g, c, kf, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
                             needmask);
-      f32x16 dp = M::mma(kfrag<T>(tV, kofs, c, st, 0), df[0], zero16());
+      // dP' = dP - D: the product accumulates onto -D
+      f32x16 dp = M::mma(kfrag<T>(tV, kofs, c, st, 0), df[0], dseed);
 #pragma unroll
       for (int ks = 1; ks < NSD; ++ks) dp = M::mma(kfrag<T>(tV, kofs, c, st, ks), df[ks], dp);
 
@@ -179,7 +181,7 @@ struct BwdQ {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = exp2_fast(fmaf(s[e], sc2, off));
-        ds[e] = p * (dp[e] - Dl);
+        ds[e] = p * dp[e];
       }
       if (need_dz) {
         if (!BAND || kind != KIND_BAND) {
@@ -373,6 +375,8 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
     // padded row terms: +inf / 0 beyond N and for rows with every key masked
     q.lse2 = a.L2[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
     q.Dl = a.D[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) q.dseed[e] = -q.Dl;
   }
   q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
   q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;
