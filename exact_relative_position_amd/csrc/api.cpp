@@ -77,6 +77,17 @@ struct Plan {
   int ho_aq = 1, ho_ak = 1, ho_b = 1;
 };
 
+// Least n in [lo, hi] with pred(n), for a predicate that is false then true
+// over the range and true at hi.
+template <typename P>
+int first_true(int lo, int hi, P pred) {
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (pred(mid)) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
 // Unfolded thresholds of a map: the first offsets on each side beyond which
 // the row no longer changes.
 relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& lo, int64_t& hi) {
@@ -105,14 +116,12 @@ relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& 
         return fail(RELPOS_ERR_INVALID_ARG, "T5 max_exact must be in [1, buckets per side)");
       if (p.max_distance <= me || p.max_distance > (1 << 24))
         return fail(RELPOS_ERR_INVALID_ARG, "T5 max_distance must exceed max_exact");
-      int nsat = p.max_distance;
-      for (int n = 0; n <= p.max_distance; ++n) {
-        if (t5_bucket_dev(-n, p.num_buckets, p.max_exact, p.max_distance, p.bidirectional) ==
-            nb - 1) {
-          nsat = n;
-          break;
-        }
-      }
+      // the bucket of -n is non-decreasing in n and reaches nb - 1 by
+      // n = max_distance: the first such n by bisection
+      const int nsat = first_true(0, p.max_distance, [&](int n) {
+        return t5_bucket_dev(-n, p.num_buckets, p.max_exact, p.max_distance, p.bidirectional) ==
+               nb - 1;
+      });
       R = p.num_buckets;
       lo = -nsat;
       hi = p.bidirectional ? nsat : 0;
@@ -125,20 +134,9 @@ relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& 
       if (m < k / 2 + 2 || m > (1 << 24))
         return fail(RELPOS_ERR_INVALID_ARG, "log-bucket max_distance must be in [k/2 + 2, 2^24]");
       // the row is monotone in o and reaches 2k - 1 by o = m - 1 and 0 by
-      // o = -m: the first offsets of the two constant runs
-      int nhi = m - 1, nlo = m;
-      for (int n = 0; n < m; ++n) {
-        if (log_bucket_dev(n, k, m) == 2 * k - 1) {
-          nhi = n;
-          break;
-        }
-      }
-      for (int n = 0; n <= m; ++n) {
-        if (log_bucket_dev(-n, k, m) == 0) {
-          nlo = n;
-          break;
-        }
-      }
+      // o = -m: the first offsets of the two constant runs, by bisection
+      const int nhi = first_true(0, m - 1, [&](int n) { return log_bucket_dev(n, k, m) == 2 * k - 1; });
+      const int nlo = first_true(0, m, [&](int n) { return log_bucket_dev(-n, k, m) == 0; });
       R = 2 * k;
       lo = -nlo;
       hi = nhi;
