@@ -7,14 +7,15 @@ Structure-Aware Kernels", nanless.github.io digest):
     S_ij = tau * (q_i.k_j + q_i.aQ[phi(i,j)] + k_j.aK[phi(i,j)] + b[phi(i,j)]) + M_ij
     O    = softmax(S) V
 
-with phi a truncated (Shaw, DeBERTa), bucketed (T5) or identity
-(Transformer-XL) offset map.  Forward and backward run in the HIP library
+with phi a truncated (Shaw, DeBERTa), bucketed (T5 buckets, DeBERTa log
+buckets) or identity (Transformer-XL) offset map.  Forward and backward run in the HIP library
 ``librelpos_attn.so`` (C ABI in include/relpos_attn.h); this package only
 marshals arguments and lets PyTorch own device memory and streams.
 
 phi is a dict: {"kind": "truncated", "lo": lo, "hi": hi},
 {"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": True},
-or {"kind": "identity"}.
+{"kind": "log", "num_buckets": 256, "max_distance": 512} (2 * num_buckets
+table rows), or {"kind": "identity"}.
 """
 
 import torch
