@@ -24,7 +24,9 @@ Modules
 phi        offset maps phi: truncated (Shaw, DeBERTa as configured), T5 buckets,
            DeBERTa log buckets, identity (Transformer-XL).
 attention  forward (O, LSE) and backward (dQ, dK, dV, daQ, daK, db).
+dropout    attention dropout: Philox4x32-10 random bytes and the keep mask.
 """
 
 from .phi import phi_rows, num_rows, t5_bucket, log_bucket  # noqa: F401
 from .attention import forward, backward  # noqa: F401
+from .dropout import philox4x32_10, random_bytes, keep_mask  # noqa: F401

@@ -30,10 +30,17 @@ Tables may be per head (aQ, aK: [H, R, d]; b: [H, R]) or shared by all heads
 (aQ, aK: [R, d]; b: [R]); the gradient has the shape of its table.
 Everything is computed in float64 one (batch, head) pair and one block of
 query rows at a time, with library matmuls, exp and bincount as the steps.
+
+Optional attention dropout (``dropout`` = (t, seed, offset), drop probability
+t / 256; the readings are in ``oracle/dropout.py``): the weights P are
+replaced by P * K / (1 - p) in O = P V, and in the backward dV uses the same
+weights while dP = (dO V^T) * K / (1 - p); D_i and dS = P * (dP - D) keep
+their form.
 """
 
 import numpy as np
 
+from .dropout import keep_mask, keep_scale
 from .phi import num_rows, phi_rows
 
 
@@ -83,7 +90,7 @@ def _pairs(B, H, bh):
 
 
 def forward(q, k, v, aQ=None, aK=None, b=None, *, phi, tau, causal=False,
-            key_len=None, row_block=512, bh=None, query_rows=None):
+            key_len=None, row_block=512, bh=None, query_rows=None, dropout=None):
     """Return (O [B,H,N,d], LSE [B,H,N]) in float64.
 
     ``bh`` restricts the work to a list of (batch, head) pairs and
@@ -111,6 +118,8 @@ def forward(q, k, v, aQ=None, aK=None, b=None, *, phi, tau, causal=False,
                            tau, causal, kl)
             sel = rows - rows[0]
             P, lse = _softmax_rows(S[sel])
+            if dropout is not None:
+                P = P * keep_mask(dropout, bi * H + h, rows, N) * keep_scale(dropout)
             O[bi, h, rows] = P @ vh
             LSE[bi, h, rows] = lse
     return O, LSE
@@ -129,7 +138,7 @@ def _row_blocks(N, row_block, query_rows):
 
 
 def backward(q, k, v, aQ=None, aK=None, b=None, *, dO, phi, tau, causal=False,
-             key_len=None, row_block=512, bh=None, query_rows=None):
+             key_len=None, row_block=512, bh=None, query_rows=None, dropout=None):
     """Exact gradients of sum(O * dO).
 
     Returns a dict with dq, dk, dv ([B,H,N,d]) and daq, dak, db (shape of
@@ -172,11 +181,16 @@ def backward(q, k, v, aQ=None, aK=None, b=None, *, dO, phi, tau, causal=False,
             S, r = S[sel], r[sel]
             P, _ = _softmax_rows(S)
             dP = dOh[rows] @ vh.T
+            Pv = P  # the weights that multiply V in the forward
+            if dropout is not None:
+                Km = keep_mask(dropout, bi * H + h, rows, N) * keep_scale(dropout)
+                Pv = P * Km
+                dP = dP * Km
             Drow = (P * dP).sum(axis=1)
             G = tau * (P * (dP - Drow[:, None]))
             dQh[rows] = G @ kh
             if not rows_only:
-                dVh += P.T @ dOh[rows]
+                dVh += Pv.T @ dOh[rows]
                 dKh += G.T @ qh[rows]
             nb = len(rows)
             if aQh is not None or bvec is not None:
