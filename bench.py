@@ -66,8 +66,11 @@ def describe(w):
         ps = "identity"
     terms = "+".join(t for t, f in (("aQ", w.has_aq), ("aK", w.has_ak), ("b", w.has_b)) if f)
     mask = "+".join(m for m, f in (("causal", w.causal), ("key_padding", w.key_padding)) if f)
-    return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "phi": ps,
-            "terms": terms or "none", "mask": mask or "none", "tau": round(w.tau, 6)}
+    out = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "phi": ps,
+           "terms": terms or "none", "mask": mask or "none", "tau": round(w.tau, 6)}
+    if w.dropout is not None:
+        out["dropout_p"] = w.dropout[0] / 256.0
+    return out
 
 
 def cpu_baseline(w, x, min_seconds=10.0):
@@ -90,9 +93,10 @@ def cpu_baseline(w, x, min_seconds=10.0):
     t0 = time.perf_counter()
     for bh in slices:
         oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi, tau=w.tau,
-                       causal=w.causal, key_len=kl, bh=[bh])
+                       causal=w.causal, key_len=kl, bh=[bh], dropout=w.dropout)
         oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"],
-                        phi=w.phi, tau=w.tau, causal=w.causal, key_len=kl, bh=[bh])
+                        phi=w.phi, tau=w.tau, causal=w.causal, key_len=kl, bh=[bh],
+                        dropout=w.dropout)
         done.append(bh)
         flops += 14.0 * w.d * live_pairs(w.with_(B=1), None if kl is None else kl[bh[0]:bh[0] + 1])
         if time.perf_counter() - t0 >= min_seconds:
@@ -104,7 +108,7 @@ def cpu_baseline(w, x, min_seconds=10.0):
                       f"at full N={w.N}, fp64 NumPy"}
 
 
-_COMMON = ("qside.hpp", "tiles.hpp", "device.hpp", "geometry.hpp")
+_COMMON = ("qside.hpp", "tiles.hpp", "device.hpp", "geometry.hpp", "dropout.hpp")
 KERNEL_SOURCES = {
     "fwd_kernel": ("attn_fwd.hip",) + _COMMON,
     "bwd_kernel": ("attn_bwd.hpp", "attn_bwd_q.hpp", "attn_bwd_k.hpp", "attn_bwd_f32.hip",
@@ -255,6 +259,9 @@ def main():
                     help="instead of the one-line step benchmark, run the layer sweep "
                          "(N = 128 .. 8192 at 16384 tokens) for 'all' or a comma list of "
                          "shaw, txl, deberta, t5; one JSON line per point")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="attention dropout probability (fp16/bf16; rounded to a multiple "
+                         "of 1/256; generator seed 2024, offset 0)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB before the warmup "
                          "(calibration of HBM byte counters)")
@@ -273,6 +280,9 @@ def main():
     from relpos_synth import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    t_drop = int(round(args.dropout * 256))
+    if t_drop > 0:
+        w = w.with_(name=f"{w.name}_dropout{t_drop}", dropout=(t_drop, 2024, 0))
     dev = torch.device("cuda:0")
     x = make_inputs(w)
     if args.copy_probe_mib > 0:
@@ -282,8 +292,10 @@ def main():
     mem_inputs = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
 
+    drop = None if w.dropout is None else (w.dropout[0] / 256.0, w.dropout[1], w.dropout[2])
     run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
-                      tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True)
+                      tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True,
+                      dropout=drop)
     stages = stage_list(B_, run, args.separate_passes)
     stage_ms, gpu_ms, wall = time_stages(torch, dev, stages, args.warmup, args.steps)
     peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs

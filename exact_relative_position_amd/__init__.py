@@ -16,6 +16,11 @@ phi is a dict: {"kind": "truncated", "lo": lo, "hi": hi},
 {"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": True},
 {"kind": "log", "num_buckets": 256, "max_distance": 512} (2 * num_buckets
 table rows), or {"kind": "identity"}.
+
+Attention dropout (fp16 / bf16): ``dropout=(p, seed, offset)`` drops each
+weight of P with probability p (rounded to a multiple of 1/256) and scales the
+kept ones by 1 / (1 - p); the keep mask is a function of (seed, offset, batch,
+head, query, key) only, recomputed by the backward.
 """
 
 import torch
@@ -34,25 +39,27 @@ class RelPosAttention(torch.autograd.Function):
     """Autograd wrapper: the forward keeps O, LSE and the relation projections."""
 
     @staticmethod
-    def forward(ctx, q, k, v, aq, ak, b, phi, tau, causal, key_len):
+    def forward(ctx, q, k, v, aq, ak, b, phi, tau, causal, key_len, dropout=None):
         O, lse, zs = _binding.forward(q, k, v, aq, ak, b, phi=phi, tau=tau, causal=causal,
-                                      key_len=key_len, keep_z=True)
+                                      key_len=key_len, keep_z=True, dropout=dropout)
         ctx.save_for_backward(q, k, v, aq, ak, b, O, lse, zs, key_len)
-        ctx.cfg = (phi, tau, causal)
+        ctx.cfg = (phi, tau, causal, dropout)
         return O
 
     @staticmethod
     def backward(ctx, dO):
         q, k, v, aq, ak, b, O, lse, zs, key_len = ctx.saved_tensors
-        phi, tau, causal = ctx.cfg
+        phi, tau, causal, dropout = ctx.cfg
         dq, dk, dv, daq, dak, db = _binding.backward(
             q, k, v, aq, ak, b, O, lse, dO.contiguous(), zs, phi=phi, tau=tau, causal=causal,
-            key_len=key_len)
+            key_len=key_len, dropout=dropout)
         cast = lambda g, t: None if g is None else g.to(t.dtype)  # noqa: E731
-        return dq, dk, dv, cast(daq, aq), cast(dak, ak), cast(db, b), None, None, None, None
+        return (dq, dk, dv, cast(daq, aq), cast(dak, ak), cast(db, b), None, None, None, None,
+                None)
 
 
 def relpos_attention(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False,
-                     key_len=None):
-    """Differentiable relative-position attention; q, k, v are [B, H, N, 64] on the GPU."""
-    return RelPosAttention.apply(q, k, v, aq, ak, b, phi, tau, causal, key_len)
+                     key_len=None, dropout=None):
+    """Differentiable relative-position attention; q, k, v are [B, H, N, 64] on the GPU;
+    ``dropout`` = (p, seed, offset) or None."""
+    return RelPosAttention.apply(q, k, v, aq, ak, b, phi, tau, causal, key_len, dropout)

@@ -45,7 +45,9 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("d", ctypes.c_int64), ("dtype", ctypes.c_int32), ("tau", ctypes.c_float),
                 ("strides", (ctypes.c_int64 * 3) * 8), ("aq_head_stride", ctypes.c_int64),
-                ("ak_head_stride", ctypes.c_int64), ("b_head_stride", ctypes.c_int64)]
+                ("ak_head_stride", ctypes.c_int64), ("b_head_stride", ctypes.c_int64),
+                ("dropout_p", ctypes.c_float), ("dropout_offset", ctypes.c_uint32),
+                ("dropout_seed", ctypes.c_uint64)]
 
 
 class RelposError(RuntimeError):
@@ -135,8 +137,9 @@ def _table_hs(t, vec):
     return 0 if shared else t.stride(0)
 
 
-def problem(q, tau, tensors, aq=None, ak=None, b=None):
-    """Problem descriptor; ``tensors`` maps a role index to its [B,H,N,d] tensor."""
+def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None):
+    """Problem descriptor; ``tensors`` maps a role index to its [B,H,N,d] tensor;
+    ``dropout`` = (p, seed, offset) or None."""
     B, H, N, d = q.shape
     p = Problem()
     p.B, p.H, p.N, p.d = B, H, N, d
@@ -148,6 +151,10 @@ def problem(q, tau, tensors, aq=None, ak=None, b=None):
     p.aq_head_stride = _table_hs(aq, True)
     p.ak_head_stride = _table_hs(ak, True)
     p.b_head_stride = _table_hs(b, False)
+    if dropout is not None:
+        p.dropout_p = float(dropout[0])
+        p.dropout_seed = int(dropout[1]) & 0xFFFFFFFFFFFFFFFF
+        p.dropout_offset = int(dropout[2]) & 0xFFFFFFFF
     return p
 
 
@@ -206,13 +213,14 @@ def phi_rows(phi, N, device="cuda"):
 
 
 def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_len=None,
-            keep_z=True, out=None):
-    """O, LSE (and the saved projections, or None) of the relative-position attention."""
+            keep_z=True, out=None, dropout=None):
+    """O, LSE (and the saved projections, or None) of the relative-position
+    attention; ``dropout`` = (p, seed, offset) or None."""
     dev = q.device
     O = torch.empty_like(q) if out is None else out
     B, H, N, _ = q.shape
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b)
+    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     terms = _terms(aq, ak, b)
@@ -228,7 +236,7 @@ def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_le
 
 
 def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=False,
-             key_len=None):
+             key_len=None, dropout=None):
     """dQ, dK, dV (input dtype) and daQ, daK, db (fp32, shape of their table, or None)."""
     dev = q.device
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -236,7 +244,7 @@ def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=Fal
     dak = None if ak is None else torch.empty(ak.shape, dtype=torch.float32, device=dev)
     db = None if b is None else torch.empty(b.shape, dtype=torch.float32, device=dev)
     prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: o, T_DO: do, T_DQ: dq, T_DK: dk,
-                            T_DV: dv}, aq, ak, b)
+                            T_DV: dv}, aq, ak, b, dropout)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     terms = _terms(aq, ak, b)
@@ -255,7 +263,7 @@ class Prepared:
     library calls (nothing is allocated in between)."""
 
     def __init__(self, q, k, v, aq, ak, b, do, *, phi, tau, causal=False, key_len=None,
-                 keep_z=True):
+                 keep_z=True, dropout=None):
         dev = q.device
         self.dev = dev
         self.q, self.k, self.v, self.aq, self.ak, self.b, self.do = q, k, v, aq, ak, b, do
@@ -269,7 +277,7 @@ class Prepared:
         self.dak = None if ak is None else torch.empty(ak.shape, **f32)
         self.db = None if b is None else torch.empty(b.shape, **f32)
         self.prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: self.O, T_DO: do, T_DQ: self.dq,
-                                     T_DK: self.dk, T_DV: self.dv}, aq, ak, b)
+                                     T_DK: self.dk, T_DV: self.dv}, aq, ak, b, dropout)
         self.phi_s = phi_struct(phi)
         self.mask_s = mask_struct(causal, key_len)
         terms = _terms(aq, ak, b)

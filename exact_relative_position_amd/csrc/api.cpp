@@ -68,6 +68,7 @@ struct Plan {
   bool bucketed = false;  // T5 or log buckets: unfolded, gradients folded back
   bool has_aq = false, has_ak = false, has_b = false;
   bool keypad = false;
+  int drop_t = 0;      // dropout threshold t (p = t / 256), 0 = off
   int64_t aq_hs = 0, ak_hs = 0, b_hs = 0;
   int nblk = 0;        // 128-row blocks per (b, h)
   int ncol_q = 0, ncol_k = 0;
@@ -167,6 +168,13 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
     return fail(RELPOS_ERR_INVALID_ARG, "key padding needs key_len");
   if (terms & ~(RELPOS_TERM_AQ | RELPOS_TERM_AK | RELPOS_TERM_B))
     return fail(RELPOS_ERR_INVALID_ARG, "unknown term bits");
+  if (!(prob->dropout_p >= 0.f) || !(prob->dropout_p < 1.f))
+    return fail(RELPOS_ERR_INVALID_ARG, "dropout_p must be in [0, 1)");
+  pl.drop_t = (int)std::nearbyint(prob->dropout_p * 256.f);
+  if (pl.drop_t > 255)
+    return fail(RELPOS_ERR_INVALID_ARG, "dropout_p rounds to 1 (t = 256 of 256)");
+  if (pl.drop_t > 0 && elem_size(prob->dtype) != 2)
+    return fail(RELPOS_ERR_UNSUPPORTED, "dropout is implemented for fp16 and bf16 inputs");
   pl.dtype = prob->dtype;
   pl.esz = elem_size(prob->dtype);
   pl.B = (int)prob->B;
@@ -485,6 +493,15 @@ AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask
   a.scale2 = prob->tau * 1.4426950408889634f;
   a.flags = (pl.has_aq ? F_ZQ : 0) | (pl.has_ak ? F_ZK : 0) | (need_bunf(pl) ? F_B : 0) |
             (pl.keypad ? F_KEYPAD : 0) | ((pl.has_aq || pl.has_b) ? F_ZQ_NEEDED : 0);
+  if (pl.drop_t > 0) {
+    a.flags |= F_DROP;
+    a.seed_lo = (uint32_t)(prob->dropout_seed & 0xFFFFFFFFu);
+    a.seed_hi = (uint32_t)(prob->dropout_seed >> 32);
+    a.drop_off = prob->dropout_offset;
+    a.drop_t = (uint32_t)pl.drop_t;
+    a.drop_scale = 256.f / (float)(256 - pl.drop_t);
+    a.drop_keep = (float)(256 - pl.drop_t) / 256.f;
+  }
   a.bunf_hs = pl.b_hs == 0 ? 0 : pl.Runf;
   a.nblk = pl.nblk;
   a.Np = pl.Np;
@@ -729,9 +746,10 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   a.dzq = w.dzq;
   a.dzk = w.dzk;
   if (stages & RELPOS_BWD_PREPARE) {
+    const float dseed_scale = pl.drop_t > 0 ? (float)(256 - pl.drop_t) / 256.f : 1.f;
     RowTermArgs r{O,      dO,    str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), lse,
-                  w.L2,   w.D,   w.kseed, w.zq, pl.geo, prob->tau * 1.4426950408889634f,
-                  pl.B,   pl.H,  pl.N,    pl.Np};
+                  w.L2,   w.D,   w.kseed, dseed_scale, w.zq, pl.geo,
+                  prob->tau * 1.4426950408889634f, pl.B, pl.H, pl.N, pl.Np};
     if ((s = hip_check(launch_rowterm(pl.dtype, r, st), "backward (row terms)")) != RELPOS_OK)
       return s;
   }

@@ -38,9 +38,9 @@ __device__ __forceinline__ const AttnArgs& branch_args() {
 }
 
 // ZQ/ZK: relation tables present; SQ/SK: staged band stores of the query /
-// key pass; GRP: two wave groups per block.  The AttnArgs are the kernel's
-// first argument (offset 0 of the kernarg segment).
-template <typename T, bool ZQ, bool ZK, bool SQ, bool SK, bool GRP>
+// key pass; GRP: two wave groups per block; DROP: attention dropout.  The
+// AttnArgs are the kernel's first argument (offset 0 of the kernarg segment).
+template <typename T, bool ZQ, bool ZK, bool SQ, bool SK, bool GRP, bool DROP>
 __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, GRP>()))
     void bwd_kernel(AttnArgs a, int kblocks, int weave) {
   static_assert(query_threads<T, GRP>() == key_threads<T, GRP>() &&
@@ -66,30 +66,30 @@ __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, 
     if (!key) bid -= kblocks;
   }
   if (key)
-    bwd_k_block<T, ZQ, SK, GRP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0);
+    bwd_k_block<T, ZQ, SK, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0);
   else
-    bwd_q_block<T, ZK, SQ, GRP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0, st1);
+    bwd_q_block<T, ZK, SQ, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0, st1);
 }
 
-template <typename T, bool GRP, bool ZQ, bool ZK, bool SQ, bool SK>
+template <typename T, bool GRP, bool DROP, bool ZQ, bool ZK, bool SQ, bool SK>
 static void launch_bwd_v(const AttnArgs& a, int grid, int kblocks, int weave, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_kernel<T, ZQ, ZK, SQ, SK, GRP>), dim3(grid),
+  hipLaunchKernelGGL((bwd_kernel<T, ZQ, ZK, SQ, SK, GRP, DROP>), dim3(grid),
                      dim3(query_threads<T, GRP>()), 0, st, a, kblocks, weave);
 }
 
-template <typename T, bool GRP, bool ZQ>
+template <typename T, bool GRP, bool DROP, bool ZQ>
 static void launch_bwd_z(const AttnArgs& a, bool zk, bool sq, bool sk, int grid, int kblocks,
                          int weave, hipStream_t st) {
   // sq (W >= kStageMinW) implies W >= kStageMinWK, so sk == zk whenever sq
   if (!zk) {
-    if (sq) launch_bwd_v<T, GRP, ZQ, false, true, false>(a, grid, kblocks, weave, st);
-    else launch_bwd_v<T, GRP, ZQ, false, false, false>(a, grid, kblocks, weave, st);
+    if (sq) launch_bwd_v<T, GRP, DROP, ZQ, false, true, false>(a, grid, kblocks, weave, st);
+    else launch_bwd_v<T, GRP, DROP, ZQ, false, false, false>(a, grid, kblocks, weave, st);
   } else if (sq) {
-    launch_bwd_v<T, GRP, ZQ, true, true, true>(a, grid, kblocks, weave, st);
+    launch_bwd_v<T, GRP, DROP, ZQ, true, true, true>(a, grid, kblocks, weave, st);
   } else if (sk) {
-    launch_bwd_v<T, GRP, ZQ, true, false, true>(a, grid, kblocks, weave, st);
+    launch_bwd_v<T, GRP, DROP, ZQ, true, false, true>(a, grid, kblocks, weave, st);
   } else {
-    launch_bwd_v<T, GRP, ZQ, true, false, false>(a, grid, kblocks, weave, st);
+    launch_bwd_v<T, GRP, DROP, ZQ, true, false, false>(a, grid, kblocks, weave, st);
   }
 }
 
@@ -105,14 +105,24 @@ hipError_t launch_bwd_t(const AttnArgs& a, bool want_q, bool want_k, hipStream_t
   const bool zq = a.flags & F_ZQ, zk = a.flags & F_ZK;
   const bool sq = a.geo.W >= kStageMinW, sk = zk && a.geo.W >= kStageMinWK;
   if constexpr (sizeof(T) == 2) {
+    if (a.flags & F_DROP) {
+      if (a.split) {
+        if (zq) launch_bwd_z<T, true, true, true>(a, zk, sq, sk, grid, kblocks, weave, st);
+        else launch_bwd_z<T, true, true, false>(a, zk, sq, sk, grid, kblocks, weave, st);
+      } else {
+        if (zq) launch_bwd_z<T, false, true, true>(a, zk, sq, sk, grid, kblocks, weave, st);
+        else launch_bwd_z<T, false, true, false>(a, zk, sq, sk, grid, kblocks, weave, st);
+      }
+      return hipGetLastError();
+    }
     if (a.split) {
-      if (zq) launch_bwd_z<T, true, true>(a, zk, sq, sk, grid, kblocks, weave, st);
-      else launch_bwd_z<T, true, false>(a, zk, sq, sk, grid, kblocks, weave, st);
+      if (zq) launch_bwd_z<T, true, false, true>(a, zk, sq, sk, grid, kblocks, weave, st);
+      else launch_bwd_z<T, true, false, false>(a, zk, sq, sk, grid, kblocks, weave, st);
       return hipGetLastError();
     }
   }
-  if (zq) launch_bwd_z<T, false, true>(a, zk, sq, sk, grid, kblocks, weave, st);
-  else launch_bwd_z<T, false, false>(a, zk, sq, sk, grid, kblocks, weave, st);
+  if (zq) launch_bwd_z<T, false, false, true>(a, zk, sq, sk, grid, kblocks, weave, st);
+  else launch_bwd_z<T, false, false, false>(a, zk, sq, sk, grid, kblocks, weave, st);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@
 // one 8-wave block whose groups share every barrier.)  Orientation
 // S = Q K^T: lane l owns key l % 32.
 #pragma once
+#include "dropout.hpp"
 #include "qside.hpp"
 
 namespace relpos {
@@ -54,8 +55,8 @@ constexpr int key_blocks_per_cu() {
 }
 
 // STAGE: band dZ^K stores go through an LDS staging area; GRP: two groups
-// of waves split the query tiles.
-template <typename T, bool STAGE, bool GRP>
+// of waves split the query tiles; DROP: attention dropout.
+template <typename T, bool STAGE, bool GRP, bool DROP>
 struct BwdK {
   static constexpr int kGroups = key_groups<T, GRP>();
   using M = MT<T>;
@@ -102,6 +103,7 @@ struct BwdK {
   frag kf[NSD], vf[NSD];
   f32x16 dk[2], dv[2];
   float acc_lo, acc_hi;
+  DropCtx dr;  // DROP only
 
   template <int BUF>
   __device__ __forceinline__ void issue(int t) {
@@ -251,6 +253,20 @@ struct BwdK {
         p[e] = exp2_fast(fmaf(s[e], sc2, off));
         ds[e] = p[e] * dp[e];
       }
+      if constexpr (DROP) {
+        // dP' was seeded at -D (1 - p): kept, dS = P dP' / (1 - p); dropped,
+        // dS = -P D = P * seed / (1 - p); dV takes the kept P only (its
+        // 1 / (1 - p) is applied once, at the end)
+        const uint32_t kb = drop_bits<T, false>(dr, jk, qt0 + 32 * st, hl);
+        float v[16];
+        lds_rows16<T>(sr + 3 * kTile + 32 * st, hl, v);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool kp = (kb >> e) & 1u;
+          ds[e] = p[e] * dr.scale * (kp ? dp[e] : v[e]);
+          p[e] = kp ? p[e] : 0.f;
+        }
+      }
       if (has_zk) {
         if (!BAND || kind != KIND_BAND) {
           float tsum = 0.f;
@@ -331,12 +347,12 @@ struct BwdK {
 // blocks.  LDS (sizes for G = key_groups groups): sQ0..sO1 G*DTile bytes
 // each, sR0/sR1 G*4*kTile floats, sSt (STAGE only) 4*G*32*kStagePitchK
 // floats.
-template <typename T, bool ZQ, bool STAGE, bool GRP>
+template <typename T, bool ZQ, bool STAGE, bool GRP, bool DROP>
 __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ0, char* sQ1,
                                             char* sO0, char* sO1, float* sR0, float* sR1,
                                             float* sSt) {
   using M = MT<T>;
-  using K = BwdK<T, STAGE, GRP>;
+  using K = BwdK<T, STAGE, GRP, DROP>;
   constexpr int TB = DTile<T>::BYTES;
   constexpr int G = K::kGroups;
 
@@ -408,6 +424,7 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
   k.stage = STAGE ? sSt + wall * 32 * kStagePitchK : sSt;
   k.sc2 = a.scale2;
   k.tau = a.tau;
+  if constexpr (DROP) k.dr = drop_ctx(a, bh, lane);
 
   // Key-side constants of saturated tiles, Z^K[j, first/last row] + b, in
   // the exp2 domain.
@@ -483,6 +500,13 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
     k.acc_hi += sR0[256 + t];
   }
 
+  if constexpr (DROP) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      k.dv[0][e] *= a.drop_scale;
+      k.dv[1][e] *= a.drop_scale;
+    }
+  }
   if (jk >= kv_end) {
     // a padded key: exact zeros (its unmasked scores were accumulated)
     k.dk[0] = zero16();

@@ -14,6 +14,7 @@
 // operand of dQ = dS K, through transpose reads); the key loop runs in three
 // segments like the forward.
 #pragma once
+#include "dropout.hpp"
 #include "qside.hpp"
 
 namespace relpos {
@@ -47,8 +48,8 @@ constexpr int query_blocks_per_cu() {
 }
 
 // STAGE: band stores go through an LDS staging area (chosen for wide bands);
-// GRP: two groups of waves split the key tiles.
-template <typename T, bool STAGE, bool GRP>
+// GRP: two groups of waves split the key tiles; DROP: attention dropout.
+template <typename T, bool STAGE, bool GRP, bool DROP>
 struct BwdQ {
   static constexpr int kGroups = query_groups<T, GRP>();
   using M = MT<T>;
@@ -69,7 +70,8 @@ struct BwdQ {
   QCtx c;
   int w, lane, hl, l32, i0, iw0, nkt, N, kv_lim;
   float cst_lo, cst_hi, sc2, tau, lse2, Dl;
-  f32x16 dseed;  // -D in every entry: the starting value of dP
+  f32x16 dseed;  // -D in every entry (-D (1 - p) under dropout): the starting value of dP
+  DropCtx dr;    // DROP only
   bool need_dz;
   const T* Kb;
   const T* Vb;
@@ -178,10 +180,21 @@ struct BwdQ {
       for (int ks = 1; ks < NSD; ++ks) dp = M::mma(kfrag<T>(tV, kofs, c, st, ks), df[ks], dp);
 
       float ds[16];
+      if constexpr (DROP) {
+        // kept: dS = P (dP / (1 - p) - D) = P (dP' / (1 - p)) with dP' seeded
+        // at -D (1 - p); dropped: dS = -P D
+        const uint32_t kb = drop_bits<T, true>(dr, c.iq, j0 + 32 * st, hl);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2_fast(fmaf(s[e], sc2, off));
-        ds[e] = p * dp[e];
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2_fast(fmaf(s[e], sc2, off));
+          ds[e] = p * (((kb >> e) & 1u) ? dr.scale * dp[e] : -Dl);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2_fast(fmaf(s[e], sc2, off));
+          ds[e] = p * dp[e];
+        }
       }
       if (need_dz) {
         if (!BAND || kind != KIND_BAND) {
@@ -285,12 +298,12 @@ struct BwdQ {
 // B*H*nblk blocks.  LDS (sizes for G = query_groups groups): sK0..sV1
 // G*DTile bytes each, sZK0/sZK1 G*2*kTile floats, sSt0/sSt1 (STAGE only)
 // 4*G*kStageFloats floats.
-template <typename T, bool ZK, bool STAGE, bool GRP>
+template <typename T, bool ZK, bool STAGE, bool GRP, bool DROP>
 __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK0, char* sK1,
                                             char* sV0, char* sV1, float* sZK0, float* sZK1,
                                             float* sSt0, float* sSt1) {
   using M = MT<T>;
-  using B = BwdQ<T, STAGE, GRP>;
+  using B = BwdQ<T, STAGE, GRP, DROP>;
   constexpr int TB = DTile<T>::BYTES;
   constexpr int G = B::kGroups;
 
@@ -363,6 +376,7 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
   qside_consts(g, c, qb, q.cst_lo, q.cst_hi);
   q.sc2 = a.scale2;
   q.tau = a.tau;
+  if constexpr (DROP) q.dr = drop_ctx(a, bh, lane);
 
   {
     const T* qrow = (const T*)a.q + bb * a.sq.b + hh * a.sq.h + (int64_t)iq * a.sq.n;
@@ -375,8 +389,9 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
     // padded row terms: +inf / 0 beyond N and for rows with every key masked
     q.lse2 = a.L2[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
     q.Dl = a.D[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
+    const float dsd = DROP ? -q.Dl * a.drop_keep : -q.Dl;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) q.dseed[e] = -q.Dl;
+    for (int e = 0; e < 16; ++e) q.dseed[e] = dsd;
   }
   q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
   q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;

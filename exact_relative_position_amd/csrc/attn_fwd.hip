@@ -24,6 +24,11 @@
 // reference maximum is only moved when a row's maximum grows by more than
 // 2^8, so most tiles skip the rescaling of the accumulator (exact: the final
 // division uses the same reference).
+//
+// Attention dropout (16-bit inputs): the P V operand takes the kept weights
+// only, the normaliser sums all of them, and the final division carries the
+// 1 / (1 - p) factor; the keep bits come from dropout.hpp.
+#include "dropout.hpp"
 #include "qside.hpp"
 
 namespace relpos {
@@ -41,26 +46,26 @@ constexpr int fwd_groups() {
   return (GRP && sizeof(T) == 2) ? 2 : 1;
 }
 // Waves per SIMD the forward is compiled for: 16-bit inputs without a
-// key-side term, staged rows or groups fit 3 (168 VGPRs), which hides more
-// latency than operand prefetch; the others keep 2.
-template <typename T, bool ZK, bool ZQS, bool GRP>
+// key-side term, staged rows, groups or dropout fit 3 (168 VGPRs), which
+// hides more latency than operand prefetch; the others keep 2.
+template <typename T, bool ZK, bool ZQS, bool GRP, bool DROP>
 constexpr int fwd_occupancy() {
-  return (sizeof(T) == 2 && !ZK && !ZQS && !GRP) ? 3 : (sizeof(T) == 2 ? 2 : 1);
+  return (sizeof(T) == 2 && !ZK && !ZQS && !GRP && !DROP) ? 3 : (sizeof(T) == 2 ? 2 : 1);
 }
 template <typename T, bool GRP>
 constexpr int fwd_threads() {
   return kThreads * fwd_groups<T, GRP>();
 }
-template <typename T, bool ZK, bool ZQS, bool GRP>
+template <typename T, bool ZK, bool ZQS, bool GRP, bool DROP>
 constexpr int fwd_blocks_per_cu() {
-  return fwd_occupancy<T, ZK, ZQS, GRP>() / fwd_groups<T, GRP>();
+  return fwd_occupancy<T, ZK, ZQS, GRP, DROP>() / fwd_groups<T, GRP>();
 }
 
 // ZQS: Z^Q band rows staged in LDS (wide bands) instead of gathered per score.
 // OCC3: compiled for 3 waves per SIMD: each subtile reads its own operand
 // fragments (instead of the whole tile's up front), which keeps fewer
-// registers live.
-template <typename T, bool ZQS, bool OCC3, bool GRP>
+// registers live.  DROP: attention dropout.
+template <typename T, bool ZQS, bool OCC3, bool GRP, bool DROP>
 struct Fwd {
   using M = MT<T>;
   using frag = typename M::frag;
@@ -96,6 +101,7 @@ struct Fwd {
   f32x16 oacc[2];
   float m_used, lsum;
   RowStage zs;  // Z^Q band rows of this wave, staged per subtile
+  DropCtx dr;   // DROP only
 
   // Issue the loads of tile t into LDS buffer BUF (asynchronous).
   template <int BUF>
@@ -219,6 +225,14 @@ struct Fwd {
         pf[kk] = M::pack(&p[kk * E]);
         lsum = M::sum_acc(pf[kk], lsum);
       }
+      if constexpr (DROP) {
+        // the dropped weights go into P V (the normaliser above keeps all)
+        const uint32_t kb = drop_bits<T, true>(dr, c.iq, j0 + 32 * st, hl);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[e] = keep_or_zero(kb, e, p[e]);
+#pragma unroll
+        for (int kk = 0; kk < KPS; ++kk) pf[kk] = M::pack(&p[kk * E]);
+      }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -280,9 +294,10 @@ struct Fwd {
 
 // ZK: whether the key-side relation term is present (a compile-time switch, so
 // that saturated tiles without it seed their MFMA accumulators with zero and
-// carry no branch); ZQS: Z^Q band rows staged in LDS; GRP: grouped workgroup.
-template <typename T, bool ZK, bool ZQS, bool GRP>
-__global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, ZQS, GRP>()))
+// carry no branch); ZQS: Z^Q band rows staged in LDS; GRP: grouped workgroup;
+// DROP: attention dropout.
+template <typename T, bool ZK, bool ZQS, bool GRP, bool DROP>
+__global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, ZQS, GRP, DROP>()))
     void fwd_kernel(AttnArgs a) {
   using M = MT<T>;
   constexpr float kLn2 = 0.693147180559945309f;
@@ -294,7 +309,7 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   constexpr int kZQ = ZQS ? 4 * G * RowStage::kFloats : 4;
   __shared__ __align__(16) float sZQ0[kZQ], sZQ1[kZQ];
 
-  using F = Fwd<T, ZQS, fwd_occupancy<T, ZK, ZQS, GRP>() == 3, GRP>;
+  using F = Fwd<T, ZQS, fwd_occupancy<T, ZK, ZQS, GRP, DROP>() == 3, GRP, DROP>;
   F f;
   f.sK[0] = sK0;
   f.sK[1] = sK1;
@@ -365,6 +380,7 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   f.zs.buf[1] = ZQS ? sZQ1 + wall * RowStage::kFloats : sZQ1;
   f.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, -1, lane);
   f.sc2 = a.scale2;
+  if constexpr (DROP) f.dr = drop_ctx(a, bh, lane);
 
   {
     const T* qrow = Qp + (int64_t)iq * a.sq.n;
@@ -420,7 +436,7 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
 
   const float ltot = sum_xor32(f.lsum);
   if (iq < N) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float inv = ltot > 0.f ? (DROP ? a.drop_scale : 1.f) / ltot : 0.f;
     T* orow = (T*)a.o_out + bb * a.so.b + hh * a.so.h + (int64_t)iq * a.so.n;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -435,26 +451,32 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   }
 }
 
-template <typename T, bool GRP>
+template <typename T, bool GRP, bool DROP>
 static hipError_t launch_fwd_g(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
   const bool zk = a.flags & F_ZK, zqs = (a.flags & F_ZQ) && a.geo.W >= kStageMinW;
   const int nt = fwd_threads<T, GRP>();
   if (zk && zqs)
-    hipLaunchKernelGGL((fwd_kernel<T, true, true, GRP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, true, true, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
   else if (zk)
-    hipLaunchKernelGGL((fwd_kernel<T, true, false, GRP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, true, false, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
   else if (zqs)
-    hipLaunchKernelGGL((fwd_kernel<T, false, true, GRP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, false, true, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, false, false, GRP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, false, false, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
-  if (a.split && sizeof(T) == 2) return launch_fwd_g<T, true>(a, st);
-  return launch_fwd_g<T, false>(a, st);
+  if constexpr (sizeof(T) == 2) {
+    if (a.flags & F_DROP) {
+      if (a.split) return launch_fwd_g<T, true, true>(a, st);
+      return launch_fwd_g<T, false, true>(a, st);
+    }
+    if (a.split) return launch_fwd_g<T, true, false>(a, st);
+  }
+  return launch_fwd_g<T, false, false>(a, st);
 }
 
 hipError_t launch_fwd(int dtype, const AttnArgs& a, hipStream_t st) {

@@ -80,7 +80,7 @@ RP_HD void cols_k(const Geo& g, int grp, int& cb, int& ce) {
   ce = imin(g.W, rrow(g, omax) - ws + 1);
 }
 
-enum : int { F_ZQ = 1, F_ZK = 2, F_B = 4, F_KEYPAD = 8, F_ZQ_NEEDED = 16 };
+enum : int { F_ZQ = 1, F_ZK = 2, F_B = 4, F_KEYPAD = 8, F_ZQ_NEEDED = 16, F_DROP = 32 };
 
 // Strides of a [B, H, N, d] tensor in elements.
 struct Str {
@@ -143,6 +143,10 @@ struct AttnArgs {
   int flags;
   int nblk;        // blocks per (b, h) along the parallel dimension
   int split;       // causal launches: two wave groups per block split its tiles
+  // attention dropout (F_DROP): Philox key, counter word 3, threshold t
+  // (drop probability t / 256), 1 / (1 - p) and 1 - p
+  uint32_t seed_lo, seed_hi, drop_off, drop_t;
+  float drop_scale, drop_keep;
 };
 
 struct RowTermArgs {     // padded backward row terms
@@ -158,6 +162,7 @@ struct RowTermArgs {     // padded backward row terms
   //  2:     -L2 / (tau log2 e)                              (band tiles)
   //  3:     -D
   float* kseed;
+  float dseed_scale;     // multiplies -D in seed 3 (1 - p under dropout, else 1)
   const float* zq;       // [B*H][N][W] or null
   Geo geo;
   float scale2;          // tau * log2(e)

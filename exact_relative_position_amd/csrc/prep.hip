@@ -7,7 +7,8 @@
 //    dS = P (dP - D) in the FlashAttention backward; and the per-query seeds
 //    of the key pass, which start its score accumulator at the row's
 //    -LSE (plus, on saturated tiles, the query-side saturated relation
-//    scalar) and its dP accumulator at -D.
+//    scalar) and its dP accumulator at -D (at -D (1 - p) under attention
+//    dropout, where the key pass rescales the kept entries by 1 / (1 - p)).
 #include "device.hpp"
 #include "tiles.hpp"
 #include "qside.hpp"
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void rowterm_kernel(RowTermArgs a) {
     a.kseed[row] = zlo + base;
     a.kseed[rows + row] = zhi + base;
     a.kseed[2 * rows + row] = base;
-    a.kseed[3 * rows + row] = -acc;
+    a.kseed[3 * rows + row] = -acc * a.dseed_scale;
   }
 }
 

@@ -102,6 +102,17 @@ enum {
 };
 
 /* Problem descriptor.
+ *  - Attention dropout (the digest page's section on reproduction asks for
+ *    dropout whose random numbers the backward recomputes): the weights P of
+ *    O = P V are replaced by P * K / (1 - p), with drop probability
+ *    p = t / 256, t = dropout_p * 256 rounded to the nearest integer (it must
+ *    be <= 255; dropout_p = 0 turns dropout off).  K_ij = 1 iff the random
+ *    byte u_ij >= t, where u_ij is byte j % 4 of word i % 4 of Philox4x32-10
+ *    (Salmon et al., SC 2011) at counter (j / 4, i / 4, batch * H + head,
+ *    dropout_offset) under the key dropout_seed (low word first).  The LSE
+ *    output is that of the undropped softmax.  The backward must be given
+ *    the forward's dropout_p, dropout_seed and dropout_offset.  Dropout is
+ *    implemented for fp16 and bf16 (ERR_UNSUPPORTED for fp32).
  *  - Tensors are [B, H, N, d] with d contiguous; strides[role] = {batch, head,
  *    row} strides in ELEMENTS.  Each stride must be a multiple of 8 elements
  *    (16 bytes) and every tensor pointer 16-byte aligned.
@@ -118,6 +129,9 @@ typedef struct relpos_problem {
   int64_t aq_head_stride;   /* elements; 0 = shared */
   int64_t ak_head_stride;
   int64_t b_head_stride;
+  float dropout_p;          /* in [0, 1); 0 = no dropout */
+  uint32_t dropout_offset;  /* counter word 3 of the generator */
+  uint64_t dropout_seed;    /* generator key */
 } relpos_problem;
 
 /* Which relation terms are present (a "= 0" table is simply absent). */

@@ -51,6 +51,9 @@ class Workload:
     do_std: float = 1.0
     shared_tables: bool = False       # one table for all heads
     seed: int = 0
+    # attention dropout: (t, generator seed, generator offset), drop
+    # probability t / 256; None = no dropout
+    dropout: Optional[tuple] = None
 
     def with_(self, **kw):
         return dataclasses.replace(self, **kw)

@@ -31,16 +31,24 @@ def require_gpu():
     return torch.device("cuda:0")
 
 
+def gpu_dropout(w):
+    """The library's (p, seed, offset) for a workload's (t, seed, offset)."""
+    return None if w.dropout is None else (w.dropout[0] / 256.0, w.dropout[1], w.dropout[2])
+
+
 def gpu_run(w, x, dev, keep_z=True, backward=True):
     import exact_relative_position_amd as rp
     t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    drop = gpu_dropout(w)
     O, lse, zs = rp.forward(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], phi=w.phi,
-                            tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=keep_z)
+                            tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=keep_z,
+                            dropout=drop)
     out = {"O": O, "lse": lse}
     if backward:
         dq, dk, dv, daq, dak, db = rp.backward(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"],
                                                O, lse, t["do"], zs, phi=w.phi, tau=w.tau,
-                                               causal=w.causal, key_len=t["key_len"])
+                                               causal=w.causal, key_len=t["key_len"],
+                                               dropout=drop)
         out.update(dq=dq, dk=dk, dv=dv, daq=daq, dak=dak, db=db)
     torch.cuda.synchronize(dev)
     return {k: (None if v is None else v.detach().cpu().double().numpy()) for k, v in out.items()}
@@ -50,12 +58,13 @@ def oracle_run(w, x, bh=None, query_rows=None, backward=True):
     f = {k: as_f64(v) for k, v in x.items() if k != "key_len"}
     kl = None if x["key_len"] is None else x["key_len"].numpy()
     O, L = oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi, tau=w.tau,
-                          causal=w.causal, key_len=kl, bh=bh, query_rows=query_rows)
+                          causal=w.causal, key_len=kl, bh=bh, query_rows=query_rows,
+                          dropout=w.dropout)
     out = {"O": O, "lse": L}
     if backward:
         g = oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"],
                             phi=w.phi, tau=w.tau, causal=w.causal, key_len=kl, bh=bh,
-                            query_rows=query_rows)
+                            query_rows=query_rows, dropout=w.dropout)
         out.update(g)
     return out
 

@@ -137,6 +137,30 @@ def test_bad_problem(L, field, value, code):
     assert L.relpos_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("dtype,p,code", [
+    (1, -0.1, -1), (1, 1.0, -1), (2, float("nan"), -1),
+    (1, 0.999, -1),      # rounds to t = 256 of 256
+    (0, 0.1, -2),        # dropout is implemented for 16-bit inputs only
+    (0, 0.001, 0),       # rounds to t = 0: no dropout, fine for fp32
+    (2, 0.1, 0), (1, 255 / 256, 0),
+])
+def test_dropout_probability(L, dtype, p, code):
+    pr = _prob(dtype=dtype)
+    pr.dropout_p = p
+    pr.dropout_seed = 0xFFFFFFFFFFFFFFFF
+    pr.dropout_offset = 0xFFFFFFFF
+    phi = b.phi_struct({"kind": "truncated", "lo": -4, "hi": 4})
+    assert _ws(L, pr, phi)[0] == code
+
+
+def test_problem_struct_layout():
+    # the dropout fields follow the table strides, 8-byte aligned seed last
+    assert b.Problem.dropout_p.offset == b.Problem.b_head_stride.offset + 8
+    assert b.Problem.dropout_offset.offset == b.Problem.dropout_p.offset + 4
+    assert b.Problem.dropout_seed.offset == b.Problem.dropout_offset.offset + 4
+    assert ctypes.sizeof(b.Problem) == b.Problem.dropout_seed.offset + 8
+
+
 @pytest.mark.parametrize("phi", [
     {"kind": "truncated", "lo": 5, "hi": 4},
     {"kind": "t5", "num_buckets": 31, "max_distance": 128, "bidirectional": True},

@@ -75,6 +75,23 @@ SMALL = [
     Workload("log_buckets_keypad_bf16", 2, 2, 420, 64, "bf16",
              {"kind": "log", "num_buckets": 32, "max_distance": 40}, 1 / 8, has_aq=True,
              has_b=True, key_padding=True, pad_frac=0.3),
+    # attention dropout (t / 256), with every kernel variant it reaches:
+    # plain, key-side term, staged rows, grouped causal blocks, padding
+    Workload("dropout_shaw_ragged_f16", 2, 2, 333, 64, "f16", SHAW16, 1 / 8, has_aq=True,
+             dropout=(26, 0x9E3779B97F4A7C15, 3)),
+    Workload("dropout_all_terms_keypad_bf16", 2, 2, 600, 64, "bf16",
+             {"kind": "truncated", "lo": -40, "hi": 31}, 1 / math.sqrt(192), has_aq=True,
+             has_ak=True, has_b=True, key_padding=True, pad_frac=0.3,
+             dropout=(64, 12345, 0)),
+    Workload("dropout_wide_band_causal_f16", 1, 2, 1000, 64, "f16", IDENTITY, 1 / 8,
+             has_aq=True, has_b=True, causal=True, b_std=0.02, dropout=(128, 7, 0xFFFFFFFF)),
+    Workload("dropout_t5_keypad_bf16", 2, 2, 500, 64, "bf16", T5_32_128, 1.0, has_b=True,
+             key_padding=True, pad_frac=0.3, dropout=(200, 2 ** 63 + 11, 5)),
+    Workload("dropout_shared_tables_f16", 2, 3, 270, 64, "f16",
+             {"kind": "truncated", "lo": -64, "hi": 64}, 1 / 8, has_aq=True, has_ak=True,
+             has_b=True, shared_tables=True, dropout=(13, 99, 1)),
+    Workload("dropout_nearly_all_n5_f16", 1, 1, 5, 64, "f16", SHAW16, 1 / 8, has_aq=True,
+             has_ak=True, has_b=True, dropout=(255, 3, 0)),
 ]
 
 
@@ -248,6 +265,48 @@ FULL = ["shaw_n256_f32", "shaw_n8192_f16", "deberta_n8192_f16", "deberta_log_n81
 def test_full_shape_parity(name):
     """Every output of head 0 (all batches) in full, O/LSE on sampled rows elsewhere."""
     _full_parity(WORKLOADS[name])
+
+
+@pytest.mark.parametrize("name", ["shaw_n8192_f16", "deberta_n8192_f16", "txl_n4096_bf16"])
+def test_full_shape_dropout_parity(name):
+    """The 8K workloads with attention dropout p = 26/256 (about 0.1)."""
+    w = WORKLOADS[name]
+    _full_parity(w.with_(name=name + "_dropout", dropout=(26, 2024, 0)))
+
+
+def test_dropout_zero_is_bitwise_no_dropout():
+    dev = require_gpu()
+    w = SMALL[0]
+    x = make_inputs(w)
+    a = gpu_run(w, x, dev)
+    b = gpu_run(w.with_(dropout=(0, 5, 5)), x, dev)
+    for n in ALL:
+        if a[n] is not None:
+            assert np.array_equal(a[n], b[n]), n
+
+
+def test_dropout_offset_changes_the_mask_and_is_deterministic():
+    dev = require_gpu()
+    w = next(v for v in SMALL if v.name == "dropout_shaw_ragged_f16")
+    x = make_inputs(w)
+    a = gpu_run(w, x, dev)
+    a2 = gpu_run(w, x, dev)
+    c = gpu_run(w.with_(dropout=(w.dropout[0], w.dropout[1], w.dropout[2] + 1)), x, dev)
+    for n in ALL:
+        if a[n] is not None:
+            assert np.array_equal(a[n], a2[n]), n
+    assert not np.array_equal(a["O"], c["O"])
+    assert np.array_equal(a["lse"], c["lse"])  # the LSE is that of the undropped softmax
+
+
+def test_dropout_fp32_is_rejected():
+    dev = require_gpu()
+    import exact_relative_position_amd as rp
+    w = next(v for v in SMALL if v.dtype == "f32")
+    x = {k: (None if v is None else v.to(dev)) for k, v in make_inputs(w).items()}
+    with pytest.raises(rp.RelposError, match="UNSUPPORTED"):
+        rp.forward(x["q"], x["k"], x["v"], x["aq"], None, None, phi=w.phi, tau=w.tau,
+                   dropout=(0.1, 1, 0))
 
 
 @pytest.mark.parametrize("name", list(sweep_workloads()))
