@@ -46,11 +46,12 @@ constexpr int fwd_groups() {
   return (GRP && sizeof(T) == 2) ? 2 : 1;
 }
 // Waves per SIMD the forward is compiled for: 16-bit inputs without a
-// key-side term, staged rows, groups or dropout fit 3 (168 VGPRs), which
-// hides more latency than operand prefetch; the others keep 2.
+// key-side term, staged rows or groups fit 3 (168 VGPRs), which hides more
+// latency than operand prefetch (with dropout too: its few spills cost less
+// than the third wave gains); the others keep 2.
 template <typename T, bool ZK, bool ZQS, bool GRP, bool DROP>
 constexpr int fwd_occupancy() {
-  return (sizeof(T) == 2 && !ZK && !ZQS && !GRP && !DROP) ? 3 : (sizeof(T) == 2 ? 2 : 1);
+  return (sizeof(T) == 2 && !ZK && !ZQS && !GRP) ? 3 : (sizeof(T) == 2 ? 2 : 1);
 }
 template <typename T, bool GRP>
 constexpr int fwd_threads() {

@@ -32,15 +32,16 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
                                               uint32_t& c3, uint32_t k0, uint32_t k1) {
   constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
   constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+  // each 32 x 32 -> 64-bit product as one 64-bit multiply (one v_mad_u64_u32
+  // gives both halves)
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo0 = kM0 * c0, hi0 = __umulhi(kM0, c0);
-    const uint32_t lo1 = kM1 * c2, hi1 = __umulhi(kM1, c2);
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    const uint64_t p0 = (uint64_t)kM0 * c0, p1 = (uint64_t)kM1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = lo1;
+    c1 = (uint32_t)p1;
     c2 = n2;
-    c3 = lo0;
+    c3 = (uint32_t)p0;
     k0 += kW0;
     k1 += kW1;
   }
