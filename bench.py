@@ -209,10 +209,16 @@ def run_sweep(args):
     from relpos_synth import make_inputs, sweep_workloads
 
     dev = torch.device("cuda:0")
-    mechs = None if args.sweep == "all" else set(args.sweep.split(","))
-    for name, w in sweep_workloads().items():
-        if mechs is not None and name.split("_")[0] not in mechs:
-            continue
+    if args.memory_scaling:
+        from relpos_synth import memory_scaling_workloads
+        todo = memory_scaling_workloads()
+        metric = "memory scaling in N (Shaw, 1x12xN fp16): fwd and bwd ms, extra memory"
+    else:
+        mechs = None if args.sweep == "all" else set(args.sweep.split(","))
+        todo = {n: w for n, w in sweep_workloads().items()
+                if mechs is None or n.split("_")[0] in mechs}
+        metric = "layer sweep: fwd and bwd ms, TFLOP/s, extra memory"
+    for name, w in todo.items():
         x = make_inputs(w)
         t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
         torch.cuda.synchronize(dev)
@@ -229,7 +235,7 @@ def run_sweep(args):
         pairs = live_pairs(w, kl) * w.H
         peak = PEAK_TFLOPS[w.dtype]
         zbytes = run.zs.numel() if run.zs is not None else 0
-        out = {"metric": "layer sweep: fwd and bwd ms, TFLOP/s, extra memory", "config":
+        out = {"metric": metric, "config":
                describe(w), "dtype": w.dtype, "fwd_ms": round(fwd_ms, 4),
                "bwd_ms": round(bwd_ms, 4), "ms_per_step": round(gpu_ms, 4),
                "fwd_tflops": round(4.0 * w.d * pairs / (fwd_ms * 1e-3) / 1e12, 2),
@@ -259,6 +265,10 @@ def main():
                     help="instead of the one-line step benchmark, run the layer sweep "
                          "(N = 128 .. 8192 at 16384 tokens) for 'all' or a comma list of "
                          "shaw, txl, deberta, t5; one JSON line per point")
+    ap.add_argument("--memory-scaling", action="store_true",
+                    help="instead of the one-line step benchmark, run the Shaw workload "
+                         "(1x12xN fp16) at N = 1K .. 16K; one JSON line per N with the "
+                         "memory allocated beyond the inputs")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="attention dropout probability (fp16/bf16; rounded to a multiple "
                          "of 1/256; generator seed 2024, offset 0)")
@@ -270,7 +280,7 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is a "
               "single-device operator and no multi-GPU figure is produced.", file=sys.stderr)
         sys.exit(2)
-    if args.sweep:
+    if args.sweep or args.memory_scaling:
         run_sweep(args)
         return
 

@@ -132,6 +132,18 @@ def sweep_workloads():
     return out
 
 
+# Memory scaling in N at a fixed batch (the Shaw workload, 1 x 12 x N, fp16):
+# the method keeps O(N d + N R) bytes per sequence, so the extra memory should
+# about double per doubling of N.
+MEMORY_NS = (1024, 2048, 4096, 8192, 16384)
+
+
+def memory_scaling_workloads():
+    """Name -> Workload of the Shaw workload at each N of MEMORY_NS."""
+    base = WORKLOADS["shaw_n8192_f16"]
+    return {f"shaw_n{N}_f16": base.with_(name=f"shaw_n{N}_f16", N=N) for N in MEMORY_NS}
+
+
 def make_inputs(w: Workload):
     """Return a dict of CPU torch tensors in the workload dtype (tables too).
 

@@ -309,6 +309,12 @@ def test_dropout_fp32_is_rejected():
                    dropout=(0.1, 1, 0))
 
 
+def test_shaw_n16384_parity():
+    """The largest point of the memory-scaling run (Shaw, 1 x 12 x 16384)."""
+    from relpos_synth import memory_scaling_workloads
+    _full_parity(memory_scaling_workloads()["shaw_n16384_f16"], n_others=2)
+
+
 @pytest.mark.parametrize("name", list(sweep_workloads()))
 def test_sweep_parity(name):
     """The layer sweep's points (N = 128 .. 8192 at 16384 tokens, each
