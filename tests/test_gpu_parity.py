@@ -267,9 +267,12 @@ def test_full_shape_parity(name):
     _full_parity(WORKLOADS[name])
 
 
-@pytest.mark.parametrize("name", ["shaw_n8192_f16", "deberta_n8192_f16", "txl_n4096_bf16"])
+@pytest.mark.parametrize("name", ["shaw_n8192_f16", "deberta_n8192_f16", "txl_n4096_bf16",
+                                  "txl_n8192_f16"])
 def test_full_shape_dropout_parity(name):
-    """The 8K workloads with attention dropout p = 26/256 (about 0.1)."""
+    """Full-size workloads with attention dropout p = 26/256 (about 0.1): the
+    fused launch, the two-group split (Transformer-XL 4K) and the causal
+    rank-by-rank launch (Transformer-XL 8K)."""
     w = WORKLOADS[name]
     _full_parity(w.with_(name=name + "_dropout", dropout=(26, 2024, 0)))
 
