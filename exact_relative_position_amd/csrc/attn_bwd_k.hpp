@@ -85,7 +85,7 @@ struct BwdK {
   // sends a tile to the band body.
   const T* Qb;
   const T* Ob;
-  const float* seeds;   // [4][B*H][Np]: LO seed, HI seed, band seed, -D
+  const float* seeds;   // [4][B*H][Np]: LO seed, HI seed, band seed, -D (-D (1 - p): dropout)
   int64_t seed_stride;  // B*H*Np
   const float* zq_bh;
   const float* zk_row;
@@ -198,7 +198,8 @@ struct BwdK {
   // Per 32-query half: S' = seed + Q K^T, where the seed (per query, from
   // the row-term pass) already holds -LSE/(tau log2 e) and, on saturated
   // tiles, the query-side saturated relation scalar; P = exp2(S' * tau
-  // log2 e + key-side constant).  dP' = -D + dO V^T, so dS = P * dP'.
+  // log2 e + key-side constant).  dP' = -D + dO V^T, so dS = P * dP' (the
+  // dropout variant below rescales it).
   template <bool BAND, int BUF>
   __device__ __forceinline__ void tile(int t, int sat) {
     const int qt0 = t * kTile;

@@ -160,7 +160,7 @@ struct RowTermArgs {     // padded backward row terms
   // score before the tau * log2(e) scale:
   //  0 / 1: Z^Q[i, first / last row] - L2 / (tau log2 e)  (saturated tiles)
   //  2:     -L2 / (tau log2 e)                              (band tiles)
-  //  3:     -D
+  //  3:     -D (-D (1 - p) under attention dropout)
   float* kseed;
   float dseed_scale;     // multiplies -D in seed 3 (1 - p under dropout, else 1)
   const float* zq;       // [B*H][N][W] or null
