@@ -181,9 +181,10 @@ def test_padded_keys_have_exact_zero_grads():
     assert np.all(got["dk"][0, :, 500:] == 0) and np.all(got["dv"][0, :, 500:] == 0)
 
 
-def test_recompute_projection_matches_saved():
+@pytest.mark.parametrize("dropout", [None, (26, 77, 1)])
+def test_recompute_projection_matches_saved(dropout):
     dev = require_gpu()
-    w = SMALL[2]
+    w = SMALL[2].with_(dropout=dropout)
     x = make_inputs(w)
     _say("[gpu] zsave vs recompute")
     a = gpu_run(w, x, dev, keep_z=True)
@@ -205,10 +206,12 @@ def test_bitwise_deterministic():
             np.testing.assert_array_equal(a[n], b[n], err_msg=n)
 
 
-def test_strided_layout_bnhd():
+@pytest.mark.parametrize("dropout", [None, (26, 77, 1)])
+def test_strided_layout_bnhd(dropout):
     """Q, K, V given as [B, N, H, d] memory viewed as [B, H, N, d]."""
     dev = require_gpu()
-    w = Workload("strided_f16", 2, 3, 257, 64, "f16", SHAW16, 1 / 8, has_aq=True, has_ak=True)
+    w = Workload("strided_f16", 2, 3, 257, 64, "f16", SHAW16, 1 / 8, has_aq=True, has_ak=True,
+                 dropout=dropout)
     x = make_inputs(w)
     _say("[gpu] strided layout")
     ref = gpu_run(w, x, dev)
@@ -300,6 +303,34 @@ def test_dropout_offset_changes_the_mask_and_is_deterministic():
             assert np.array_equal(a[n], a2[n]), n
     assert not np.array_equal(a["O"], c["O"])
     assert np.array_equal(a["lse"], c["lse"])  # the LSE is that of the undropped softmax
+
+
+def test_autograd_wrapper_with_dropout():
+    """relpos_attention keeps the dropout descriptor for its backward: its
+    gradients are the binding-level backward's, bit for bit, and match the
+    oracle."""
+    dev = require_gpu()
+    import exact_relative_position_amd as rp
+    from parity_util import gpu_dropout
+    w = next(v for v in SMALL if v.name == "dropout_all_terms_keypad_bf16")
+    x = make_inputs(w)
+    got = gpu_run(w, x, dev)
+    t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    leaves = {n: t[n].clone().requires_grad_(True) for n in ("q", "k", "v", "aq", "ak", "b")}
+    O = rp.relpos_attention(leaves["q"], leaves["k"], leaves["v"], leaves["aq"], leaves["ak"],
+                            leaves["b"], phi=w.phi, tau=w.tau, causal=w.causal,
+                            key_len=t["key_len"], dropout=gpu_dropout(w))
+    O.backward(t["do"])
+    torch.cuda.synchronize(dev)
+    f64 = lambda z: z.detach().cpu().double().numpy()  # noqa: E731
+    assert np.array_equal(f64(O), got["O"])
+    for n, g in (("q", "dq"), ("k", "dk"), ("v", "dv")):
+        assert np.array_equal(f64(leaves[n].grad), got[g]), n
+    # table gradients come back in the table dtype (bf16 here)
+    for n, g in (("aq", "daq"), ("ak", "dak"), ("b", "db")):
+        np.testing.assert_array_equal(f64(leaves[n].grad),
+                                      torch.from_numpy(got[g]).to(torch.bfloat16).double().numpy(),
+                                      err_msg=n)
 
 
 def test_dropout_fp32_is_rejected():
