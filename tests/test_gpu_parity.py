@@ -114,9 +114,11 @@ def test_small_parity(w):
 
 def _random_workloads(n, seed=7):
     """Seeded random small configurations: map kind and parameters, terms,
-    masks, dtype, shared tables and a ragged N (fixed by the seed, so every
-    run checks the same cases)."""
+    masks, dtype, shared tables, a ragged N and, for 16-bit inputs, attention
+    dropout half of the time (fixed by the seed, so every run checks the same
+    cases)."""
     rng = np.random.default_rng(seed)
+    rng_drop = np.random.default_rng(seed + 1)  # its own stream: the other draws stay put
     out = []
     for c in range(n):
         N = int(rng.integers(1, 700))
@@ -138,18 +140,23 @@ def _random_workloads(n, seed=7):
                    "max_distance": int(rng.integers(k // 2 + 2, 3 * k))}
         terms = rng.integers(0, 2, size=3).astype(bool)
         dtype = ["f16", "bf16", "f32"][int(rng.integers(0, 3))]
-        out.append(Workload(f"random{c}_{kind}_{dtype}", int(rng.integers(1, 3)),
+        drop = (int(rng_drop.integers(1, 256)), int(rng_drop.integers(0, 2 ** 63)),
+                int(rng_drop.integers(0, 2 ** 32)))
+        if dtype == "f32" or rng_drop.random() < 0.5:
+            drop = None
+        tag = "" if drop is None else f"_drop{drop[0]}"
+        out.append(Workload(f"random{c}_{kind}_{dtype}{tag}", int(rng.integers(1, 3)),
                             int(rng.integers(1, 4)), N, 64, dtype, phi,
                             float(rng.choice([1 / 8, 0.3, 1.0])), has_aq=bool(terms[0]),
                             has_ak=bool(terms[1]), has_b=bool(terms[2]),
                             causal=bool(rng.integers(0, 2)),
                             key_padding=bool(rng.integers(0, 2)), pad_frac=0.4,
                             shared_tables=bool(rng.integers(0, 2)), b_std=0.3,
-                            seed=100 + c))
+                            seed=100 + c, dropout=drop))
     return out
 
 
-@pytest.mark.parametrize("w", _random_workloads(16), ids=lambda w: w.name)
+@pytest.mark.parametrize("w", _random_workloads(24), ids=lambda w: w.name)
 def test_random_small_parity(w):
     """Seeded random configurations, every output against the oracle."""
     test_small_parity(w)
