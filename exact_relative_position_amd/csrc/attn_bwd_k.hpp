@@ -239,7 +239,9 @@ struct BwdK {
         }
       }
       f32x16 dp;
-      {
+      if constexpr (DROP) {
+        dp = zero16();  // the seed is added per entry below
+      } else {
         float v[16];
         lds_rows16<T>(sr + 3 * kTile + 32 * st, hl, v);
 #pragma unroll
@@ -255,16 +257,17 @@ struct BwdK {
         ds[e] = p[e] * dp[e];
       }
       if constexpr (DROP) {
-        // dP' was seeded at -D (1 - p): kept, dS = P dP' / (1 - p); dropped,
-        // dS = -P D = P * seed / (1 - p); dV takes the kept P only (its
-        // 1 / (1 - p) is applied once, at the end)
+        // with the seed v = -D (1 - p) of each query: kept, dS = P (dP /
+        // (1 - p) - D) = P (dP + v) / (1 - p); dropped, dS = -P D = P v /
+        // (1 - p); dV takes the kept P only (its 1 / (1 - p) is applied once,
+        // at the end)
         const uint32_t kb = drop_bits<T, false>(dr, jk, qt0 + 32 * st, hl);
         float v[16];
         lds_rows16<T>(sr + 3 * kTile + 32 * st, hl, v);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const bool kp = (kb >> e) & 1u;
-          ds[e] = p[e] * dr.scale * (kp ? dp[e] : v[e]);
+          ds[e] = p[e] * dr.scale * (kp ? dp[e] + v[e] : v[e]);
           p[e] = kp ? p[e] : 0.f;
         }
       }
