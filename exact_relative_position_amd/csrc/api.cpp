@@ -500,7 +500,6 @@ AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask
     a.drop_off = prob->dropout_offset;
     a.drop_t = (uint32_t)pl.drop_t;
     a.drop_scale = 256.f / (float)(256 - pl.drop_t);
-    a.drop_keep = (float)(256 - pl.drop_t) / 256.f;
   }
   a.bunf_hs = pl.b_hs == 0 ? 0 : pl.Runf;
   a.nblk = pl.nblk;

@@ -70,7 +70,7 @@ struct BwdQ {
   QCtx c;
   int w, lane, hl, l32, i0, iw0, nkt, N, kv_lim;
   float cst_lo, cst_hi, sc2, tau, lse2, Dl;
-  f32x16 dseed;  // -D in every entry (-D (1 - p) under dropout): the starting value of dP
+  f32x16 dseed;  // -D in every entry: the starting value of dP (unused under dropout)
   DropCtx dr;    // DROP only
   bool need_dz;
   const T* Kb;
@@ -174,20 +174,20 @@ struct BwdQ {
       else
         s = qside_scores<T>(g, c, kf, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
                             needmask);
-      // dP' = dP - D: the product accumulates onto -D
-      f32x16 dp = M::mma(kfrag<T>(tV, kofs, c, st, 0), df[0], dseed);
+      // dP' = dP - D: the product accumulates onto -D (from zero under
+      // dropout, whose kept entries scale dP before D is subtracted)
+      f32x16 dp = M::mma(kfrag<T>(tV, kofs, c, st, 0), df[0], DROP ? zero16() : dseed);
 #pragma unroll
       for (int ks = 1; ks < NSD; ++ks) dp = M::mma(kfrag<T>(tV, kofs, c, st, ks), df[ks], dp);
 
       float ds[16];
       if constexpr (DROP) {
-        // kept: dS = P (dP / (1 - p) - D) = P (dP' / (1 - p)) with dP' seeded
-        // at -D (1 - p); dropped: dS = -P D
+        // kept: dS = P (dP / (1 - p) - D); dropped: dS = -P D
         const uint32_t kb = drop_bits<T, true>(dr, c.iq, j0 + 32 * st, hl);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float p = exp2_fast(fmaf(s[e], sc2, off));
-          ds[e] = p * (((kb >> e) & 1u) ? dr.scale * dp[e] : -Dl);
+          ds[e] = p * (((kb >> e) & 1u) ? fmaf(dr.scale, dp[e], -Dl) : -Dl);
         }
       } else {
 #pragma unroll
@@ -389,9 +389,8 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
     // padded row terms: +inf / 0 beyond N and for rows with every key masked
     q.lse2 = a.L2[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
     q.Dl = a.D[(int64_t)bh * a.Np + imin(iq, a.Np - 1)];
-    const float dsd = DROP ? -q.Dl * a.drop_keep : -q.Dl;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) q.dseed[e] = dsd;
+    for (int e = 0; e < 16; ++e) q.dseed[e] = -q.Dl;
   }
   q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
   q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;

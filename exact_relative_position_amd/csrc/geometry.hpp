@@ -144,9 +144,9 @@ struct AttnArgs {
   int nblk;        // blocks per (b, h) along the parallel dimension
   int split;       // causal launches: two wave groups per block split its tiles
   // attention dropout (F_DROP): Philox key, counter word 3, threshold t
-  // (drop probability t / 256), 1 / (1 - p) and 1 - p
+  // (drop probability t / 256) and 1 / (1 - p)
   uint32_t seed_lo, seed_hi, drop_off, drop_t;
-  float drop_scale, drop_keep;
+  float drop_scale;
 };
 
 struct RowTermArgs {     // padded backward row terms
