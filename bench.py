@@ -14,10 +14,14 @@ synchronisations.  HIP events are recorded between the stage calls, on the
 stream the library launches on, so each kernel's average duration is measured
 live; the dominant attention kernel gives the roofline figure.
 FLOP convention (FlashAttention): forward 4 d per live (query, key) pair,
-backward 10 d; the backward launch's own count is its GEMM work (query pass
-6 d plus key pass 8 d per pair).  The CPU baseline is the fp64 oracle on a
-bounded sample (whole (batch, head) slices of the same workload, about ten
-seconds of work), timed on the host cores.
+backward 10 d; the roofline fraction of a kernel counts that useful work, and
+the backward launch's executed GEMM work (query pass 6 d plus key pass 8 d
+per pair, S and dP computed by both passes) is reported beside it.  Peak
+memory is the allocator's high-water mark of one forward and one backward
+call beyond what is resident when each starts.  The CPU baseline is the fp64
+oracle on a bounded sample (whole (batch, head) slices of the same workload,
+about ten seconds of work), forward and backward timed separately on every
+host core the process may use.
 
 Prints one JSON line.
 """
@@ -74,38 +78,85 @@ def describe(w):
 
 
 def cpu_baseline(w, x, min_seconds=10.0):
-    """fp64 oracle, forward + backward of whole (batch, head) slices at the full
-    length, taken in order until about `min_seconds` of CPU work is done."""
-    import numpy as np  # noqa: F401
-
+    """fp64 oracle, forward then backward of whole (batch, head) slices at the
+    full length, taken in order until about `min_seconds` of CPU work is done.
+    It runs on every core the process may use, with the BLAS thread pool set
+    to that count; the forward and the backward are timed separately, and
+    the rate counts the same useful work as the GPU figure (4 d and 10 d
+    flops per live pair)."""
     import oracle
     from relpos_synth import as_f64
+    cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+        libs = [f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+                for p in threadpool_info() if p.get("user_api") == "blas"]
+        blas = "; ".join(libs) or blas
     except Exception:  # noqa: BLE001
-        threads = 1
+        pass
     f = {k: as_f64(v) for k, v in x.items() if k != "key_len"}
     kl = None if x["key_len"] is None else x["key_len"].numpy()
     slices = [(b, h) for b in range(w.B) for h in range(w.H)]
     done = []
-    flops = 0.0
-    t0 = time.perf_counter()
-    for bh in slices:
-        oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi, tau=w.tau,
-                       causal=w.causal, key_len=kl, bh=[bh], dropout=w.dropout)
-        oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"],
-                        phi=w.phi, tau=w.tau, causal=w.causal, key_len=kl, bh=[bh],
-                        dropout=w.dropout)
-        done.append(bh)
-        flops += 14.0 * w.d * live_pairs(w.with_(B=1), None if kl is None else kl[bh[0]:bh[0] + 1])
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    pairs = 0
+    t_fwd = t_bwd = 0.0
+    try:
+        for bh in slices:
+            t0 = time.perf_counter()
+            oracle.forward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], phi=w.phi,
+                           tau=w.tau, causal=w.causal, key_len=kl, bh=[bh], dropout=w.dropout)
+            t1 = time.perf_counter()
+            oracle.backward(f["q"], f["k"], f["v"], f["aq"], f["ak"], f["b"], dO=f["do"],
+                            phi=w.phi, tau=w.tau, causal=w.causal, key_len=kl, bh=[bh],
+                            dropout=w.dropout)
+            t2 = time.perf_counter()
+            t_fwd += t1 - t0
+            t_bwd += t2 - t1
+            done.append(bh)
+            pairs += live_pairs(w.with_(B=1), None if kl is None else kl[bh[0]:bh[0] + 1])
+            if t_fwd + t_bwd >= min_seconds:
+                break
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    dt = t_fwd + t_bwd
+    return {"value": 14.0 * w.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"forward+backward of {len(done)} of {len(slices)} (batch, head) slices "
-                      f"at full N={w.N}, fp64 NumPy"}
+            "fwd_s": round(t_fwd, 3), "bwd_s": round(t_bwd, 3),
+            "fwd_tflops": 4.0 * w.d * pairs / t_fwd / 1e12,
+            "bwd_tflops": 10.0 * w.d * pairs / t_bwd / 1e12,
+            "blas": blas,
+            "sample": f"forward and backward of {len(done)} of {len(slices)} (batch, head) "
+                      f"slices at full N={w.N}, fp64 NumPy"}
+
+
+def window_columns(w, key_side=False):
+    """Z entries the projection computes for one (batch, head): each group of
+    128 queries (keys) computes the contiguous window of unfolded rows its
+    offsets reach, or every row of the unfolded map when that is no wider
+    than N + 127 (one group for all); a causal mask keeps offsets <= 0 only.
+    This is the algorithmic size of Z^Q (key_side: Z^K), in entries."""
+    import exact_relative_position_amd._binding as B_
+    N = w.N
+    _, lo, hi = B_.phi_info(w.phi, N)
+    R = hi - lo + 1
+
+    def row(o):
+        return min(max(o, lo), hi) - lo
+
+    G = 128
+    groups = [(0, N - 1)] if R <= N + G - 1 else \
+        [(g0, min(N - 1, g0 + G - 1)) for g0 in range(0, N, G)]
+    total = 0
+    for first, last in groups:
+        omin, omax = (first - (N - 1), last) if key_side else (-last, N - 1 - first)
+        if w.causal:
+            omax = min(omax, 0)
+        total += (last - first + 1) * (row(omax) - row(omin) + 1)
+    return total
 
 
 _COMMON = ("qside.hpp", "tiles.hpp", "device.hpp", "geometry.hpp", "dropout.hpp")
@@ -155,6 +206,32 @@ def copy_probe(torch, dev, mib):
     c.copy_(a)
     torch.cuda.synchronize(dev)
     del a, c
+
+
+def measure_peak_memory(torch, dev, t, w, drop):
+    """Peak device memory of one forward and one backward call beyond what is
+    allocated when each starts (the pages' measure: extra allocation beyond
+    the inputs), by the allocator's high-water mark.  The forward's extra
+    memory is O, LSE, the kept projections and its workspace; the backward's
+    (with the forward's outputs resident) is dQ, dK, dV, the table gradients
+    and its workspace.  Run outside the timed region."""
+    import exact_relative_position_amd as rp
+    args = (t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"])
+    kw = dict(phi=w.phi, tau=w.tau, causal=w.causal, key_len=t["key_len"], dropout=drop)
+    torch.cuda.synchronize(dev)
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    O, lse, zs = rp.forward(*args, keep_z=True, **kw)
+    torch.cuda.synchronize(dev)
+    fwd = torch.cuda.max_memory_allocated(dev) - base
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    grads = rp.backward(*args, O, lse, t["do"], zs, **kw)
+    torch.cuda.synchronize(dev)
+    bwd = torch.cuda.max_memory_allocated(dev) - base
+    del O, lse, zs, grads
+    torch.cuda.empty_cache()
+    return {"fwd": int(fwd), "bwd": int(bwd)}
 
 
 def stage_list(B_, run, separate_passes=False):
@@ -229,12 +306,12 @@ def run_sweep(args):
         stage_ms, gpu_ms, _ = time_stages(torch, dev, stage_list(B_, run), args.warmup,
                                           args.steps)
         peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs
+        mem = measure_peak_memory(torch, dev, t, w, None)
         fwd_ms = stage_ms["project"] + stage_ms["attend"]
         bwd_ms = stage_ms["prepare"] + stage_ms["passes"] + stage_ms["contract"]
         kl = None if x["key_len"] is None else x["key_len"].numpy()
         pairs = live_pairs(w, kl) * w.H
         peak = PEAK_TFLOPS[w.dtype]
-        zbytes = run.zs.numel() if run.zs is not None else 0
         out = {"metric": metric, "config":
                describe(w), "dtype": w.dtype, "fwd_ms": round(fwd_ms, 4),
                "bwd_ms": round(bwd_ms, 4), "ms_per_step": round(gpu_ms, 4),
@@ -244,8 +321,7 @@ def run_sweep(args):
                                      2),
                "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
                "peak_extra_bytes": int(peak_extra),
-               "peak_extra_bytes_fwd": int(run.O.numel() * run.O.element_size()
-                                           + run.lse.numel() * 4 + zbytes + run.ws_f.numel()),
+               "peak_extra_bytes_fwd": mem["fwd"], "peak_extra_bytes_bwd": mem["bwd"],
                "steps": args.steps, "warmup": args.warmup}
         print(json.dumps(out), flush=True)
         del run, t, x
@@ -314,28 +390,47 @@ def main():
     bwd_ms = sum(stage_ms[n] for n in ("prepare", "passes", "query_pass", "key_pass", "contract")
                  if n in stage_ms)
 
+    mem = measure_peak_memory(torch, dev, t, w, drop)
     kl = None if x["key_len"] is None else x["key_len"].numpy()
     pairs = live_pairs(w, kl) * w.H
     d = w.d
     useful = 14.0 * d * pairs
     value = useful / (gpu_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    # MFMA work per launch: forward 2 products, query pass 3 (S, dP, dQ), key
-    # pass 4 (S, dP, dV, dK), 2*d flops per live pair each
-    kern_flops = {"attend": 4.0 * d * pairs, "passes": 14.0 * d * pairs,
-                  "query_pass": 6.0 * d * pairs, "key_pass": 8.0 * d * pairs}
+    # Useful work per launch (FlashAttention convention, the same count the
+    # pages' equal-useful-work comparison implies): forward 4 d flops per live
+    # pair (S and P V), backward 10 d (S recomputed once, dP, dV, dQ, dK).
+    # The two-pass backward executes 14 d (the key pass recomputes S and dP),
+    # reported separately as executed work.
+    kern_flops = {"attend": 4.0 * d * pairs, "passes": 10.0 * d * pairs}
+    kern_exec = {"attend": 4.0 * d * pairs, "passes": 14.0 * d * pairs,
+                 "query_pass": 6.0 * d * pairs, "key_pass": 8.0 * d * pairs}
     kern_name = {"attend": "fwd_kernel", "passes": "bwd_kernel", "query_pass": "bwd_kernel",
                  "key_pass": "bwd_kernel"}
-    dom = max((n for n in kern_flops if n in stage_ms), key=lambda n: stage_ms[n])
+    if "passes" not in stage_ms:
+        # --separate-passes: the two launches together are the backward
+        stage_ms["passes"] = stage_ms["query_pass"] + stage_ms["key_pass"]
+        kern_exec["passes"] = kern_exec["query_pass"] + kern_exec["key_pass"]
+    dom = max(("attend", "passes"), key=lambda n: stage_ms[n])
     achieved = kern_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
 
-    # projection pass: algorithmic bytes = fp32 window written + Q and table read
+    # projection pass: algorithmic bytes = the fp32 window entries written
+    # (live columns only, not the row padding of the buffer) + X and the
+    # table read once
     zbytes = run.zs.numel() if run.zs is not None else 0
     proj = None
     if zbytes:
-        rd = t["q"].numel() * t["q"].element_size() * (1 + int(w.has_ak))
-        proj = {"GB/s": round((zbytes + rd) / (stage_ms["project"] * 1e-3) / 1e9, 1),
-                "bytes": int(zbytes + rd), "ms": round(stage_ms["project"], 4)}
+        nt = int(w.has_aq) + int(w.has_ak)
+        zlive = 4 * w.B * w.H * (window_columns(w) * int(w.has_aq)
+                                 + window_columns(w, key_side=True) * int(w.has_ak))
+        R = B_.phi_info(w.phi, w.N)[0]
+        tab = (1 if w.shared_tables else w.H) * R * d * t["q"].element_size() * nt
+        rd = t["q"].numel() * t["q"].element_size() * nt + tab
+        proj = {"GB/s": round((zlive + rd) / (stage_ms["project"] * 1e-3) / 1e9, 1),
+                "frac_hbm": round((zlive + rd) / (stage_ms["project"] * 1e-3) / 1e9
+                                  / HBM_PEAK_GBS, 4),
+                "bytes": int(zlive + rd), "z_bytes": int(zlive),
+                "ms": round(stage_ms["project"], 4)}
 
     out = {
         "metric": METRIC,
@@ -358,12 +453,18 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "projection": proj,
         "peak_extra_bytes": int(peak_extra),
-        "peak_extra_bytes_fwd": int(run.O.numel() * run.O.element_size() + run.lse.numel() * 4
-                                    + zbytes + run.ws_f.numel()),
+        "peak_extra_bytes_fwd": mem["fwd"],
+        "peak_extra_bytes_bwd": mem["bwd"],
+        "fwd_pct_peak": round(100.0 * kern_flops["attend"] / (fwd_ms * 1e-3) / 1e12 / peak, 2),
+        "attend_pct_peak": round(100.0 * kern_flops["attend"] / (stage_ms["attend"] * 1e-3)
+                                 / 1e12 / peak, 2),
         "roofline": {"bound": "mfma", "kernel": kern_name[dom], "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(kern_name[dom], w.name),
                      "flops_per_launch": kern_flops[dom],
+                     "flops_executed_per_launch": kern_exec[dom],
+                     "frac_executed": round(kern_exec[dom] / (stage_ms[dom] * 1e-3) / 1e12
+                                            / peak, 4),
                      "ms_per_launch": round(stage_ms[dom], 4)},
         "cpu_baseline": None,
     }

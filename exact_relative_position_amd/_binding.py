@@ -137,6 +137,85 @@ def _table_hs(t, vec):
     return 0 if shared else t.stride(0)
 
 
+def _same(t, q, name, shape=None):
+    """``t`` on q's device with q's dtype and ``shape`` (q's shape by default)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != q.device:
+        raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if t.dtype != q.dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, q has {q.dtype} (tables and tensors "
+                         "share one element type)")
+    want = tuple(q.shape) if shape is None else tuple(shape)
+    if tuple(t.shape) != want:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+
+
+def check_inputs(q, k, v, aq, ak, b, *, phi, key_len=None, tensors=(), device_type="cuda"):
+    """Validate every tensor argument before anything reaches the library.
+
+    q, k, v (and the extra [B, H, N, d] ``tensors``, as (name, tensor) pairs)
+    must share q's device, dtype and shape; q must be on a ``device_type``
+    device with a dtype the library knows.  A vector table is [H, R, d] or,
+    shared by all heads, [R, d]; the bias is [H, R] or [R]; R is the row count
+    of ``phi`` at this N.  ``key_len`` is an int32 [B] tensor on q's device.
+    Raises TypeError / ValueError naming the offending argument."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B, H, N, d] tensor")
+    if q.device.type != device_type:
+        raise ValueError(f"q is on {q.device}; the library needs {device_type} tensors")
+    if q.dtype not in DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype} (float32, float16 or bfloat16)")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v)) + tuple(tensors):
+        _same(t, q, name)
+    R = phi_info(phi, N)[0] if N > 0 else None
+    for name, t, vec in (("aq", aq, True), ("ak", ak, True), ("b", b, False)):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a tensor or None")
+        full, shared = (3, 2) if vec else (2, 1)
+        if t.dim() not in (full, shared) or (vec and t.shape[-1] != d) or \
+                (t.dim() == full and t.shape[0] != H):
+            raise ValueError(f"{name} must be [H, R{', d' if vec else ''}] or "
+                             f"[R{', d' if vec else ''}] with H = {H}, d = {d}; "
+                             f"got {tuple(t.shape)}")
+        _same(t, q, name, t.shape)
+        rows = t.shape[-2] if vec else t.shape[-1]
+        if R is not None and rows != R:
+            raise ValueError(f"{name} has {rows} rows; the map {phi.get('kind')} has R = {R} "
+                             f"at N = {N}")
+    if key_len is not None:
+        if not isinstance(key_len, torch.Tensor):
+            raise TypeError("key_len must be a tensor or None")
+        if key_len.device != q.device:
+            raise ValueError(f"key_len is on {key_len.device}, q on {q.device}")
+        if key_len.dtype != torch.int32:
+            raise ValueError(f"key_len must be int32, got {key_len.dtype}")
+        if tuple(key_len.shape) != (B,) or not key_len.is_contiguous():
+            raise ValueError(f"key_len must be a contiguous [B] = [{B}] tensor, "
+                             f"got {tuple(key_len.shape)}")
+
+
+def _check_lse(lse, q):
+    B, H, N, _ = q.shape
+    if not isinstance(lse, torch.Tensor) or lse.device != q.device or \
+            lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or \
+            not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 [B, H, N] = [{B}, {H}, {N}] tensor "
+                         f"on {q.device}")
+
+
+def _check_zsave(zsave, q, nbytes):
+    if zsave is None:
+        return
+    if not isinstance(zsave, torch.Tensor) or zsave.device != q.device or \
+            not zsave.is_contiguous() or zsave.numel() * zsave.element_size() < nbytes:
+        raise ValueError(f"zsave must be a contiguous tensor on {q.device} of at least "
+                         f"{nbytes} bytes (the forward's saved projections)")
+
+
 def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None):
     """Problem descriptor; ``tensors`` maps a role index to its [B,H,N,d] tensor;
     ``dropout`` = (p, seed, offset) or None."""
@@ -216,6 +295,8 @@ def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_le
             keep_z=True, out=None, dropout=None):
     """O, LSE (and the saved projections, or None) of the relative-position
     attention; ``dropout`` = (p, seed, offset) or None."""
+    check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len,
+                 tensors=(() if out is None else (("out", out),)))
     dev = q.device
     O = torch.empty_like(q) if out is None else out
     B, H, N, _ = q.shape
@@ -238,6 +319,8 @@ def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_le
 def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=False,
              key_len=None, dropout=None):
     """dQ, dK, dV (input dtype) and daQ, daK, db (fp32, shape of their table, or None)."""
+    check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("o", o), ("do", do)))
+    _check_lse(lse, q)
     dev = q.device
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     daq = None if aq is None else torch.empty(aq.shape, dtype=torch.float32, device=dev)
@@ -248,6 +331,7 @@ def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=Fal
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     terms = _terms(aq, ak, b)
+    _check_zsave(zsave, q, zsave_size(prob, phi_s, terms))
     ws = _workspace(workspace_size(prob, phi_s, mask_s, terms, PASS_BWD, zsave is not None), dev)
     _check(lib().relpos_attn_bwd(ctypes.byref(prob), ctypes.byref(phi_s), ctypes.byref(mask_s),
                                  _ptr(q), _ptr(k), _ptr(v), _ptr(aq), _ptr(ak), _ptr(b),
@@ -264,6 +348,7 @@ class Prepared:
 
     def __init__(self, q, k, v, aq, ak, b, do, *, phi, tau, causal=False, key_len=None,
                  keep_z=True, dropout=None):
+        check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("do", do),))
         dev = q.device
         self.dev = dev
         self.q, self.k, self.v, self.aq, self.ak, self.b, self.do = q, k, v, aq, ak, b, do

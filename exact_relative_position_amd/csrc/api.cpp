@@ -12,6 +12,8 @@
 //   fold of copied bucket columns.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -89,8 +91,11 @@ int first_true(int lo, int hi, P pred) {
   return lo;
 }
 
-// Unfolded thresholds of a map: the first offsets on each side beyond which
-// the row no longer changes.
+// Unfolded thresholds of a map.  Truncated: its own thresholds.  Bucketed:
+// the first offsets on each side beyond which the row no longer changes,
+// clipped to the offsets that exist at this length, +-(N - 1), so that the
+// unfolded tables and the contraction grow with N and not with max_distance
+// (bucket rows no offset reaches get no unfolded row and a zero gradient).
 relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& lo, int64_t& hi) {
   switch (p.kind) {
     case RELPOS_PHI_TRUNCATED:
@@ -124,8 +129,8 @@ relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& 
                nb - 1;
       });
       R = p.num_buckets;
-      lo = -nsat;
-      hi = p.bidirectional ? nsat : 0;
+      lo = std::max<int64_t>(-nsat, -(N - 1));
+      hi = std::min<int64_t>(p.bidirectional ? nsat : 0, N - 1);
       return RELPOS_OK;
     }
     case RELPOS_PHI_BUCKET_LOG: {
@@ -139,8 +144,8 @@ relpos_status unfold_range(const relpos_phi& p, int64_t N, int64_t& R, int64_t& 
       const int nhi = first_true(0, m - 1, [&](int n) { return log_bucket_dev(n, k, m) == 2 * k - 1; });
       const int nlo = first_true(0, m, [&](int n) { return log_bucket_dev(-n, k, m) == 0; });
       R = 2 * k;
-      lo = -nlo;
-      hi = nhi;
+      lo = std::max<int64_t>(-nlo, -(N - 1));
+      hi = std::min<int64_t>(nhi, N - 1);
       return RELPOS_OK;
     }
     default:
@@ -173,6 +178,9 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   pl.drop_t = (int)std::nearbyint(prob->dropout_p * 256.f);
   if (pl.drop_t > 255)
     return fail(RELPOS_ERR_INVALID_ARG, "dropout_p rounds to 1 (t = 256 of 256)");
+  if (pl.drop_t == 0 && prob->dropout_p > 0.f)
+    return fail(RELPOS_ERR_INVALID_ARG,
+                "dropout_p rounds to 0 (below 1/512): it would silently turn dropout off");
   if (pl.drop_t > 0 && elem_size(prob->dtype) != 2)
     return fail(RELPOS_ERR_UNSUPPORTED, "dropout is implemented for fp16 and bf16 inputs");
   pl.dtype = prob->dtype;
@@ -456,19 +464,21 @@ relpos_status project(const Plan& pl, const relpos_problem* prob, const void* Q,
   return RELPOS_OK;
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device, queried once per device.  The cache
+// is the library's only shared state: each entry is written with the same
+// value by whichever thread queries it first, through an atomic store.
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask* mask,

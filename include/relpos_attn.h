@@ -25,9 +25,13 @@
  *  - Every argument is validated before anything is launched; on an error
  *    nothing is written and the status says why (see relpos_last_error()).
  *  - Outputs are overwritten, never accumulated into.
- *  - Results are bitwise reproducible run to run: no atomics, fixed
- *    summation orders.
- *  - Thread-safe; no global state except the thread-local error message.
+ *  - Results are bitwise reproducible run to run on one device model: no
+ *    atomics, fixed summation orders.  Some launch shapes depend on the
+ *    device's compute-unit count, so devices with different counts may
+ *    differ in the last bits (always within the same error bounds).
+ *  - Thread-safe.  The only shared state is a per-device cache of the
+ *    compute-unit count (written once, atomically) and the thread-local
+ *    error message.
  */
 #ifndef RELPOS_ATTN_H
 #define RELPOS_ATTN_H
@@ -105,9 +109,10 @@ enum {
  *  - Attention dropout (the digest page's section on reproduction asks for
  *    dropout whose random numbers the backward recomputes): the weights P of
  *    O = P V are replaced by P * K / (1 - p), with drop probability
- *    p = t / 256, t = dropout_p * 256 rounded to the nearest integer (it must
- *    be <= 255; dropout_p = 0 turns dropout off).  K_ij = 1 iff the random
- *    byte u_ij >= t, where u_ij is byte j % 4 of word i % 4 of Philox4x32-10
+ *    p = t / 256, t = dropout_p * 256 rounded to the nearest integer, which
+ *    must be in [1, 255]: a dropout_p that rounds to t = 0 or to t = 256 is
+ *    RELPOS_ERR_INVALID_ARG, and dropout_p = 0 exactly turns dropout off.
+ *    K_ij = 1 iff the random byte u_ij >= t, where u_ij is byte j % 4 of word i % 4 of Philox4x32-10
  *    (Salmon et al., SC 2011) at counter (j / 4, i / 4, batch * H + head,
  *    dropout_offset) under the key dropout_seed (low word first).  The LSE
  *    output is that of the undropped softmax.  The backward must be given
@@ -243,7 +248,10 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
 /* Host-side facts about a map at length N: R (rows of the caller's tables),
  * and the truncated map the library unfolds it into, [lo_unf, hi_unf]
  * (R_unf = hi_unf - lo_unf + 1 rows).  For the bucketed maps the unfolded
- * thresholds are the first offsets beyond which the row no longer changes. */
+ * thresholds are the first offsets beyond which the row no longer changes,
+ * clipped to the offsets that exist at length N, [-(N - 1), N - 1]; bucket
+ * rows that no offset reaches then have no unfolded row (their gradients
+ * are zero), and every buffer grows with N, not with max_distance. */
 relpos_status relpos_phi_info(const relpos_phi* phi, int64_t N, int64_t* R, int64_t* lo_unf,
                               int64_t* hi_unf);
 

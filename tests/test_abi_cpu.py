@@ -113,6 +113,41 @@ def test_zsave_size_closed_form(L):
     assert n.value == 0
 
 
+@pytest.mark.parametrize("phi,N,want", [
+    # T5 saturates at |o| = 91: below N = 92 the unfolded map is every offset
+    ({"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": True}, 50,
+     (32, -49, 49)),
+    ({"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": True}, 92,
+     (32, -91, 91)),
+    ({"kind": "t5", "num_buckets": 32, "max_distance": 1 << 24, "bidirectional": True}, 512,
+     (32, -511, 511)),
+    ({"kind": "t5", "num_buckets": 32, "max_distance": 128, "bidirectional": False}, 10,
+     (32, -9, 0)),
+    ({"kind": "log", "num_buckets": 256, "max_distance": 1 << 20}, 512, (512, -511, 511)),
+    ({"kind": "log", "num_buckets": 256, "max_distance": 512}, 1, (512, 0, 0)),
+])
+def test_bucketed_unfold_is_clipped_to_reachable_offsets(phi, N, want):
+    assert b.phi_info(phi, N) == want
+
+
+def test_bucketed_workspace_grows_with_n_not_max_distance(L):
+    """The unfolded tables, dZ and the contraction partials of a bucketed map
+    are sized by the offsets that exist at this N: a huge max_distance costs
+    nothing at N = 512."""
+    p = _prob(B=1, H=12, N=512)
+    sizes = []
+    for m in (600, 1 << 20, 1 << 24):
+        phi = b.phi_struct({"kind": "log", "num_buckets": 256, "max_distance": m})
+        st, n = _ws(L, p, phi, terms=7, pass_=1)
+        assert st == 0
+        sizes.append(n)
+    assert sizes[0] == sizes[1] == sizes[2]
+    phi = b.phi_struct({"kind": "t5", "num_buckets": 32, "max_distance": 1 << 24,
+                        "bidirectional": True})
+    st, n = _ws(L, p, phi, terms=4, pass_=1)
+    assert st == 0 and n < 64 << 20
+
+
 def test_workspace_is_linear_in_n(L):
     phi = b.phi_struct({"kind": "truncated", "lo": -128, "hi": 128})
     sizes = []
@@ -141,7 +176,10 @@ def test_bad_problem(L, field, value, code):
     (1, -0.1, -1), (1, 1.0, -1), (2, float("nan"), -1),
     (1, 0.999, -1),      # rounds to t = 256 of 256
     (0, 0.1, -2),        # dropout is implemented for 16-bit inputs only
-    (0, 0.001, 0),       # rounds to t = 0: no dropout, fine for fp32
+    (1, 0.001, -1),      # rounds to t = 0: refused rather than silently no dropout
+    (0, 1 / 512 - 1e-6, -1),
+    (1, 1 / 512 + 1e-6, 0),  # rounds to t = 1
+    (0, 0.0, 0),         # exactly 0: no dropout, fine for fp32
     (2, 0.1, 0), (1, 255 / 256, 0),
 ])
 def test_dropout_probability(L, dtype, p, code):
@@ -261,3 +299,93 @@ def test_python_descriptor_marshalling():
     aq = torch.empty(3, 9, 64, dtype=torch.float16)
     assert b._table_hs(aq, True) == 9 * 64
     assert b._table_hs(aq[0], True) == 0
+
+
+# Python-side validation: every tensor argument is checked before anything
+# reaches the library (so a wrong dtype, shape or device can never hand the
+# kernels a pointer they would misread).  CPU tensors with device_type="cpu"
+# stand in for device tensors here.
+
+def _inputs(B=2, H=3, N=40, dtype=None, phi=None):
+    import torch
+    dtype = dtype or torch.float16
+    phi = phi or {"kind": "truncated", "lo": -4, "hi": 4}
+    R = b.phi_info(phi, N)[0]
+    t = lambda *s: torch.zeros(*s, dtype=dtype)  # noqa: E731
+    return dict(q=t(B, H, N, 64), k=t(B, H, N, 64), v=t(B, H, N, 64), aq=t(H, R, 64),
+                ak=t(R, 64), b=t(H, R), phi=phi, key_len=torch.full((B,), N, dtype=torch.int32))
+
+
+def _check(x, **kw):
+    b.check_inputs(x["q"], x["k"], x["v"], x["aq"], x["ak"], x["b"], phi=x["phi"],
+                   key_len=x["key_len"], device_type="cpu", **kw)
+
+
+def test_check_inputs_accepts_a_consistent_problem():
+    _check(_inputs())
+    x = _inputs(phi={"kind": "identity"})
+    _check(x)
+    x = _inputs(phi={"kind": "t5", "num_buckets": 32, "max_distance": 128,
+                     "bidirectional": True})
+    assert x["aq"].shape[1] == 32
+    _check(x)
+
+
+@pytest.mark.parametrize("mutate,match", [
+    (lambda x, T: x.update(aq=x["aq"].float()), "aq has dtype"),        # fp32 table, fp16 q
+    (lambda x, T: x.update(b=x["b"].to(T.bfloat16)), "b has dtype"),
+    (lambda x, T: x.update(k=x["k"][:, :, :-1]), "k has shape"),
+    (lambda x, T: x.update(v=x["v"].float()), "v has dtype"),
+    (lambda x, T: x.update(aq=x["aq"][:, :-1]), "aq has 8 rows"),        # too few rows
+    (lambda x, T: x.update(ak=T.zeros(17, 64, dtype=T.float16)), "ak has 17 rows"),
+    (lambda x, T: x.update(aq=T.zeros(2, 9, 64, dtype=T.float16)), "aq must be"),  # H mismatch
+    (lambda x, T: x.update(aq=T.zeros(3, 9, 32, dtype=T.float16)), "aq must be"),  # d mismatch
+    (lambda x, T: x.update(b=T.zeros(3, 9, 1, dtype=T.float16)), "b must be"),
+    (lambda x, T: x.update(key_len=x["key_len"].long()), "int32"),
+    (lambda x, T: x.update(key_len=x["key_len"][:1]), "key_len must be a contiguous"),
+    (lambda x, T: x.update(q=x["q"][0]), r"q must be a \[B, H, N, d\]"),
+    (lambda x, T: x.update(q=x["q"].double(), k=x["k"].double(), v=x["v"].double()),
+     "unsupported dtype"),
+])
+def test_check_inputs_rejects(mutate, match):
+    import torch
+    x = _inputs()
+    mutate(x, torch)
+    with pytest.raises((ValueError, TypeError), match=match):
+        _check(x)
+
+
+def test_identity_table_for_another_n_is_rejected():
+    # an identity-map table built for N = 40 (79 rows) used at N = 41
+    import torch
+    x = _inputs(phi={"kind": "identity"})
+    x["q"] = x["k"] = x["v"] = torch.zeros(2, 3, 41, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="aq has 79 rows"):
+        _check(x)
+
+
+def test_host_tensors_are_rejected_before_the_library():
+    """The public entry points refuse host tensors: a host pointer handed to a
+    kernel would fault the GPU."""
+    import torch
+    x = _inputs()
+    with pytest.raises(ValueError, match="needs cuda tensors"):
+        b.forward(x["q"], x["k"], x["v"], x["aq"], None, None, phi=x["phi"], tau=0.125)
+    o = torch.zeros_like(x["q"])
+    lse = torch.zeros(2, 3, 40)
+    with pytest.raises(ValueError, match="needs cuda tensors"):
+        b.backward(x["q"], x["k"], x["v"], None, None, None, o, lse, o, phi=x["phi"], tau=0.125)
+
+
+def test_backward_checks_lse_and_saved_projections():
+    import torch
+    x = _inputs()
+    lse = torch.zeros(2, 3, 40)
+    with pytest.raises(ValueError, match="lse must be"):
+        b._check_lse(lse.double(), x["q"])
+    with pytest.raises(ValueError, match="lse must be"):
+        b._check_lse(lse[:, :, :-1], x["q"])
+    b._check_lse(lse, x["q"])
+    with pytest.raises(ValueError, match="zsave must be"):
+        b._check_zsave(torch.zeros(10, dtype=torch.uint8), x["q"], 11)
+    b._check_zsave(torch.zeros(11, dtype=torch.uint8), x["q"], 11)

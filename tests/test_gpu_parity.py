@@ -92,6 +92,17 @@ SMALL = [
              has_b=True, shared_tables=True, dropout=(13, 99, 1)),
     Workload("dropout_nearly_all_n5_f16", 1, 1, 5, 64, "f16", SHAW16, 1 / 8, has_aq=True,
              has_ak=True, has_b=True, dropout=(255, 3, 0)),
+    # bucketed maps shorter than their saturation offset: the unfolded map is
+    # clipped to the offsets that exist (+-(N - 1)), and bucket rows no
+    # offset reaches get zero gradients
+    Workload("t5_shorter_than_saturation_f16", 2, 2, 50, 64, "f16", T5_32_128, 1 / 8,
+             has_aq=True, has_ak=True, has_b=True, key_padding=True, pad_frac=0.3),
+    Workload("log_huge_max_distance_bf16", 1, 2, 300, 64, "bf16",
+             {"kind": "log", "num_buckets": 256, "max_distance": 1 << 20}, 1 / 8, has_aq=True,
+             has_ak=True, has_b=True, causal=True),
+    Workload("t5_huge_max_distance_f32", 1, 2, 200, 64, "f32",
+             {"kind": "t5", "num_buckets": 32, "max_distance": 1 << 24, "bidirectional": True},
+             1.0, has_b=True),
 ]
 
 
@@ -108,7 +119,7 @@ def test_small_parity(w):
     got = gpu_run(w, x, dev)
     ref = oracle_run(w, x)
     to, tg = tolerances(w.dtype)
-    rep = compare(got, ref, ALL, tol_o=to, tol_g=tg, label=w.name)
+    rep = compare(got, ref, ALL, tol_o=to, tol_g=tg, label=w.name, dtype=w.dtype)
     _say(f"  {w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in rep.items()))
 
 
@@ -160,6 +171,34 @@ def _random_workloads(n, seed=7):
 def test_random_small_parity(w):
     """Seeded random configurations, every output against the oracle."""
     test_small_parity(w)
+
+
+@pytest.mark.parametrize("table", ["aq", "ak", "b"])
+def test_present_all_zero_table(table):
+    """A table passed as all zeros is not the same call as an absent one (the
+    kernels add its lookups and return its gradient), but it must give the
+    absent case's O and dQ/dK/dV, and a gradient equal to the oracle's, which
+    is non-zero: daQ = (dZ^Q)^T Q, daK = (dZ^K)^T K, db = column sums of dZ^Q."""
+    dev = require_gpu()
+    w = Workload(f"zero_{table}_f16", 1, 2, 333, 64, "f16",
+                 {"kind": "truncated", "lo": -40, "hi": 31}, 1 / 8,
+                 **{"has_" + table: True})
+    x = make_inputs(w)
+    x[table] = torch.zeros_like(x[table])
+    _say(f"[gpu] present all-zero table {table}")
+    got = gpu_run(w, x, dev)
+    ref = oracle_run(w, x)
+    to, tg = tolerances(w.dtype)
+    compare(got, ref, ALL, tol_o=to, tol_g=tg, label=w.name, dtype=w.dtype)
+    g = {"aq": "daq", "ak": "dak", "b": "db"}[table]
+    assert np.abs(ref[g]).max() > 1e-3 and np.abs(got[g]).max() > 1e-3, g
+    absent = w.with_(has_aq=False, has_ak=False, has_b=False, name=f"absent_{table}")
+    y = dict(x)
+    y[table] = None
+    got0 = gpu_run(absent, y, dev)
+    compare({k: got[k] for k in ("O", "lse", "dq", "dk", "dv")},
+            {k: got0[k] for k in ("O", "lse", "dq", "dk", "dv")},
+            ("O", "lse", "dq", "dk", "dv"), tol_o=to, tol_g=tg, label=f"zero vs absent {table}")
 
 
 def test_fully_masked_batch():
@@ -364,37 +403,48 @@ def test_sweep_parity(name):
     _full_parity(sweep_workloads()[name], n_others=2)
 
 
+def full_heads(H):
+    """Heads whose every output is checked at full size: the first, a middle
+    and the last.  Equal-work launches place one head's blocks on one XCD
+    (head mod 8) and causal launches deal blocks rank by rank over all
+    heads, so these three reach different XCDs, the start, middle and end of
+    the dispatch order, and both ends of the causal interleave."""
+    return sorted({0, H // 2, H - 1})
+
+
 def _full_parity(w, n_others=6):
     dev = require_gpu()
     name = w.name
     x = make_inputs(w)
     _say(f"[gpu] full-shape parity {name} B{w.B} H{w.H} N{w.N} {w.dtype}")
     got = gpu_run(w, x, dev)
-    pairs = [(b, 0) for b in range(w.B)]
-    ref = oracle_run(w, x, bh=pairs)
-    sel = (slice(None), 0)
     to, tg = tolerances(w.dtype)
-    rep = compare(got, {k: v for k, v in ref.items() if k in ("O", "lse", "dq", "dk", "dv")},
-                  ("O", "lse", "dq", "dk", "dv"), sel=sel, tol_o=to, tol_g=tg, label=name)
-    # table gradients of head 0 (per-head tables: sum over the batch of head 0 only)
-    for n in ("daq", "dak", "db"):
-        if ref[n] is None:
-            continue
-        r = ref[n][0]
-        g = got[n][0]
-        err = rel_err(g, r)
-        rep[n] = err
-        assert err <= tg, f"{name} {n}: {err:.3e}"
+    heads = full_heads(w.H)
+    rep = {}
+    for h in heads:
+        # every output of head h over the whole batch, table gradients
+        # included (per-head tables: the sum over the batch of head h only)
+        pairs = [(b, h) for b in range(w.B)]
+        ref = oracle_run(w, x, bh=pairs)
+        r = compare(got, {k: v for k, v in ref.items() if k in ("O", "lse", "dq", "dk", "dv")},
+                    ("O", "lse", "dq", "dk", "dv"), sel=(slice(None), h), tol_o=to, tol_g=tg,
+                    label=f"{name} h{h}", dtype=w.dtype)
+        tabs = {n: ref[n][h] for n in ("daq", "dak", "db") if ref[n] is not None}
+        r.update(compare({n: got[n][h] for n in tabs}, tabs, tuple(tabs), tol_o=to, tol_g=tg,
+                         label=f"{name} h{h} tables"))
+        for k, v in r.items():
+            rep[k] = max(rep.get(k, 0.0), v)
     rng = np.random.default_rng(1)
     rows = np.sort(rng.choice(w.N, size=min(w.N, 48), replace=False))
-    others = [(b, h) for b in range(w.B) for h in range(1, w.H)][:n_others]
+    others = [(b, h) for b in range(w.B) for h in range(w.H) if h not in heads][:n_others]
     if others:
         refo = oracle_run(w, x, bh=others, query_rows=rows, backward=False)
         for (b, h) in others:
             compare({"O": got["O"][b, h, rows], "lse": got["lse"][b, h, rows]},
                     {"O": refo["O"][b, h, rows], "lse": refo["lse"][b, h, rows]},
-                    ("O", "lse"), tol_o=to, tol_g=tg, label=f"{name} b{b} h{h}")
-    _say(f"  {name}: " + " ".join(f"{k}={v:.2e}" for k, v in rep.items()))
+                    ("O", "lse"), tol_o=to, tol_g=tg, label=f"{name} b{b} h{h}",
+                    dtype=w.dtype)
+    _say(f"  {name} heads {heads}: " + " ".join(f"{k}={v:.2e}" for k, v in rep.items()))
 
 
 def test_phi_tables_bit_exact():
