@@ -26,7 +26,9 @@ T_Q, T_K, T_V, T_O, T_DO, T_DQ, T_DK, T_DV = range(8)
 
 EXPORTS = ("relpos_attn_workspace_size", "relpos_attn_zsave_size", "relpos_attn_fwd",
            "relpos_attn_bwd", "relpos_attn_fwd_stages", "relpos_attn_bwd_stages",
-           "relpos_phi_info", "relpos_phi_rows", "relpos_status_string", "relpos_last_error")
+           "relpos_attn_fwd_noalloc", "relpos_phi_info", "relpos_phi_rows",
+           "relpos_status_string", "relpos_last_error")
+NOALLOC_SCRATCH_BYTES = 128 << 20
 FWD_PROJECT, FWD_ATTEND, FWD_ALL = 1, 2, 3
 BWD_PREPARE, BWD_QUERY_PASS, BWD_KEY_PASS, BWD_CONTRACT, BWD_ALL = 1, 2, 4, 8, 15
 
@@ -78,12 +80,13 @@ def lib():
                                       P, P, P, P, P, P, P, SZ, V]
         L.relpos_attn_fwd_stages.argtypes = L.relpos_attn_fwd.argtypes + [I32]
         L.relpos_attn_bwd_stages.argtypes = L.relpos_attn_bwd.argtypes + [I32]
+        L.relpos_attn_fwd_noalloc.argtypes = [pp, pphi, pm, P, P, P, P, P, P, P, P, P, V]
         L.relpos_phi_info.argtypes = [pphi, I64, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                       ctypes.POINTER(I64)]
         L.relpos_phi_rows.argtypes = [pphi, I64, P, P, V]
         for fn in ("relpos_attn_workspace_size", "relpos_attn_zsave_size", "relpos_attn_fwd",
                    "relpos_attn_bwd", "relpos_attn_fwd_stages", "relpos_attn_bwd_stages",
-                   "relpos_phi_info", "relpos_phi_rows"):
+                   "relpos_attn_fwd_noalloc", "relpos_phi_info", "relpos_phi_rows"):
             getattr(L, fn).restype = I32
         L.relpos_status_string.argtypes = [I32]
         L.relpos_status_string.restype = ctypes.c_char_p
@@ -314,6 +317,23 @@ def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_le
                                  _ptr(O), _ptr(lse), _ptr(zs), _ptr(ws), ws.numel(),
                                  _stream(dev)))
     return O, lse, zs
+
+
+def forward_noalloc(q, k, v, aq=None, ak=None, b=None, *, phi, tau, O, lse, zsave=None,
+                    causal=False, key_len=None, dropout=None):
+    """relpos_attn_fwd_noalloc: the forward into caller-given O and LSE (and
+    zsave, or None), with the library's static scratch instead of a
+    workspace; allocates nothing."""
+    check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("O", O),))
+    _check_lse(lse, q)
+    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout)
+    phi_s = phi_struct(phi)
+    mask_s = mask_struct(causal, key_len)
+    _check_zsave(zsave, q, zsave_size(prob, phi_s, _terms(aq, ak, b)))
+    _check(lib().relpos_attn_fwd_noalloc(ctypes.byref(prob), ctypes.byref(phi_s),
+                                         ctypes.byref(mask_s), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(aq), _ptr(ak), _ptr(b), _ptr(O), _ptr(lse),
+                                         _ptr(zsave), _stream(q.device)))
 
 
 def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=False,

@@ -16,6 +16,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "geometry.hpp"
@@ -531,6 +532,94 @@ relpos_status check_tables(const Plan& pl, const void* aQ, const void* aK, const
   return RELPOS_OK;
 }
 
+// Allocation-free forward: the scratch the forward needs (fold table,
+// unfolded bias, the projections when no zsave buffer is given) lives in one
+// file-scope device array instead of a caller workspace.  Each device that
+// runs the library holds its own copy until the process ends; its address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever handed to kernels.  Calls on one
+// device share the array, so calls that overlap on one device race.
+constexpr size_t kScratchBytes = RELPOS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+relpos_status scratch_address(void** out) {
+  int dev = 0;
+  relpos_status s = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (s != RELPOS_OK) return s;
+  if (dev < 0 || dev >= kMaxDevices) return fail(RELPOS_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    s = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address");
+    if (s != RELPOS_OK) return s;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RELPOS_OK;
+}
+
+// The forward: validation of every argument, then the stages asked for.
+// With use_scratch the workspace is the library's static scratch (its
+// address is looked up only once everything else has been validated).
+relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const relpos_mask* mask,
+                      const void* Q, const void* K, const void* V, const void* aQ,
+                      const void* aK, const void* b, void* O, float* lse, void* zsave,
+                      void* workspace, size_t workspace_bytes, void* stream, int32_t stages,
+                      bool use_scratch) {
+  g_err.clear();
+  if (stages & ~RELPOS_FWD_ALL) return fail(RELPOS_ERR_INVALID_ARG, "unknown forward stage bits");
+  Plan pl;
+  relpos_status s = make_plan(prob, phi, mask, terms_of(aQ, aK, b), pl);
+  if (s != RELPOS_OK) return s;
+  if (pl.B * pl.H * pl.N == 0) return RELPOS_OK;
+  if ((s = check_tensor(pl, prob, RELPOS_T_Q, Q, "Q")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_K, K, "K")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_V, V, "V")) != RELPOS_OK) return s;
+  if ((s = check_tensor(pl, prob, RELPOS_T_O, O, "O")) != RELPOS_OK) return s;
+  if ((s = check_tables(pl, aQ, aK, b)) != RELPOS_OK) return s;
+  if (!lse || !aligned16(lse)) return fail(RELPOS_ERR_INVALID_ARG, "lse null or misaligned");
+  if (zsave && !aligned16(zsave)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: zsave");
+  WsFwd w;
+  const size_t need = carve_fwd(pl, zsave != nullptr, nullptr, w);
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(RELPOS_ERR_WORKSPACE,
+                  "this forward needs " + std::to_string(need) +
+                      " bytes of scratch, above the allocation-free limit of " +
+                      std::to_string(kScratchBytes) +
+                      " (pass a zsave buffer to hold the projections, or call relpos_attn_fwd)");
+    if ((s = scratch_address(&workspace)) != RELPOS_OK) return s;
+    workspace_bytes = kScratchBytes;
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(RELPOS_ERR_WORKSPACE, "workspace smaller than relpos_attn_workspace_size()");
+  if (workspace && !aligned16(workspace))
+    return fail(RELPOS_ERR_INVALID_ARG, "misaligned: workspace");
+  carve_fwd(pl, zsave != nullptr, workspace, w);
+  if (zsave) {
+    Carve c(zsave);
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (stages & RELPOS_FWD_PROJECT) {
+    if ((s = prepare_tables(pl, b, w.fold, nullptr, nullptr, w.bunf, st)) != RELPOS_OK) return s;
+    if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st)) != RELPOS_OK) return s;
+  }
+  if (!(stages & RELPOS_FWD_ATTEND)) return RELPOS_OK;
+  AttnArgs a = attn_args(pl, prob, mask, Q, K, V);
+  a.o_out = O;
+  a.lse = lse;
+  a.zq = w.zq;
+  a.zk = w.zk;
+  a.bunf = w.bunf;
+  return hip_check(launch_fwd(pl.dtype, a, st), "forward");
+}
+
 }  // namespace
 
 extern "C" {
@@ -624,44 +713,8 @@ relpos_status relpos_attn_fwd_stages(const relpos_problem* prob, const relpos_ph
                                      const void* V, const void* aQ, const void* aK, const void* b,
                                      void* O, float* lse, void* zsave, void* workspace,
                                      size_t workspace_bytes, void* stream, int32_t stages) {
-  g_err.clear();
-  if (stages & ~RELPOS_FWD_ALL) return fail(RELPOS_ERR_INVALID_ARG, "unknown forward stage bits");
-  Plan pl;
-  relpos_status s = make_plan(prob, phi, mask, terms_of(aQ, aK, b), pl);
-  if (s != RELPOS_OK) return s;
-  if (pl.B * pl.H * pl.N == 0) return RELPOS_OK;
-  if ((s = check_tensor(pl, prob, RELPOS_T_Q, Q, "Q")) != RELPOS_OK) return s;
-  if ((s = check_tensor(pl, prob, RELPOS_T_K, K, "K")) != RELPOS_OK) return s;
-  if ((s = check_tensor(pl, prob, RELPOS_T_V, V, "V")) != RELPOS_OK) return s;
-  if ((s = check_tensor(pl, prob, RELPOS_T_O, O, "O")) != RELPOS_OK) return s;
-  if ((s = check_tables(pl, aQ, aK, b)) != RELPOS_OK) return s;
-  if (!lse || !aligned16(lse)) return fail(RELPOS_ERR_INVALID_ARG, "lse null or misaligned");
-  if (zsave && !aligned16(zsave)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: zsave");
-  WsFwd w;
-  const size_t need = carve_fwd(pl, zsave != nullptr, nullptr, w);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(RELPOS_ERR_WORKSPACE, "workspace smaller than relpos_attn_workspace_size()");
-  if (workspace && !aligned16(workspace))
-    return fail(RELPOS_ERR_INVALID_ARG, "misaligned: workspace");
-  carve_fwd(pl, zsave != nullptr, workspace, w);
-  if (zsave) {
-    Carve c(zsave);
-    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
-    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
-  }
-  hipStream_t st = (hipStream_t)stream;
-  if (stages & RELPOS_FWD_PROJECT) {
-    if ((s = prepare_tables(pl, b, w.fold, nullptr, nullptr, w.bunf, st)) != RELPOS_OK) return s;
-    if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st)) != RELPOS_OK) return s;
-  }
-  if (!(stages & RELPOS_FWD_ATTEND)) return RELPOS_OK;
-  AttnArgs a = attn_args(pl, prob, mask, Q, K, V);
-  a.o_out = O;
-  a.lse = lse;
-  a.zq = w.zq;
-  a.zk = w.zk;
-  a.bunf = w.bunf;
-  return hip_check(launch_fwd(pl.dtype, a, st), "forward");
+  return fwd_run(prob, phi, mask, Q, K, V, aQ, aK, b, O, lse, zsave, workspace, workspace_bytes,
+                 stream, stages, false);
 }
 
 relpos_status relpos_attn_fwd(const relpos_problem* prob, const relpos_phi* phi,
@@ -670,6 +723,15 @@ relpos_status relpos_attn_fwd(const relpos_problem* prob, const relpos_phi* phi,
                               void* zsave, void* workspace, size_t workspace_bytes, void* stream) {
   return relpos_attn_fwd_stages(prob, phi, mask, Q, K, V, aQ, aK, b, O, lse, zsave, workspace,
                                 workspace_bytes, stream, RELPOS_FWD_ALL);
+}
+
+relpos_status relpos_attn_fwd_noalloc(const relpos_problem* prob, const relpos_phi* phi,
+                                      const relpos_mask* mask, const void* Q, const void* K,
+                                      const void* V, const void* aQ, const void* aK,
+                                      const void* b, void* O, float* lse, void* zsave,
+                                      void* stream) {
+  return fwd_run(prob, phi, mask, Q, K, V, aQ, aK, b, O, lse, zsave, nullptr, 0, stream,
+                 RELPOS_FWD_ALL, true);
 }
 
 relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_phi* phi,

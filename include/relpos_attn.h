@@ -196,6 +196,26 @@ relpos_status relpos_attn_bwd(const relpos_problem* prob, const relpos_phi* phi,
                               float* daQ, float* daK, float* db,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments and results as relpos_attn_fwd, without the
+ * workspace: the forward's scratch (the bucket fold table, the unfolded
+ * bias and, when zsave is NULL, the projections Z^Q, Z^K) lives in a static
+ * device buffer of RELPOS_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * device, held until the process ends.  A problem whose forward workspace
+ * (relpos_attn_workspace_size, pass FWD, with the same zsave_given) exceeds
+ * that size returns RELPOS_ERR_WORKSPACE before anything is launched; passing
+ * a zsave buffer moves the projections out of the scratch.  Nothing in the
+ * scratch needs to start at any value.  Every call on one device shares its
+ * buffer, so calls that overlap on one device (concurrent streams or host
+ * threads) race: the caller must order them.  Calls no allocating routine. */
+#define RELPOS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+relpos_status relpos_attn_fwd_noalloc(const relpos_problem* prob, const relpos_phi* phi,
+                                      const relpos_mask* mask,
+                                      const void* Q, const void* K, const void* V,
+                                      const void* aQ, const void* aK, const void* b,
+                                      void* O, float* lse, void* zsave, void* stream);
+
 /* Stages of the two passes, for callers that schedule them separately (for
  * example to overlap the key-parallel pass with other work, or to time each
  * kernel).  The pipeline section of the page orders the forward as relation

@@ -389,3 +389,29 @@ def test_backward_checks_lse_and_saved_projections():
     with pytest.raises(ValueError, match="zsave must be"):
         b._check_zsave(torch.zeros(10, dtype=torch.uint8), x["q"], 11)
     b._check_zsave(torch.zeros(11, dtype=torch.uint8), x["q"], 11)
+
+
+def test_noalloc_forward_validates_before_touching_the_device(L):
+    """The allocation-free forward checks every argument, and that the
+    forward fits its static scratch, before it looks up the scratch or
+    launches anything (so these calls need no GPU)."""
+    phi = b.phi_struct({"kind": "truncated", "lo": -128, "hi": 128})
+    m = b.Mask()
+    P = ctypes.c_void_p
+
+    def call(p, q=FAKE, zs=None):
+        return L.relpos_attn_fwd_noalloc(ctypes.byref(p), ctypes.byref(phi), ctypes.byref(m),
+                                         P(q) if q else None, P(FAKE), P(FAKE), P(FAKE), None,
+                                         None, P(FAKE), P(FAKE), P(zs) if zs else None, None)
+    assert call(_prob(), q=None) == -1
+    assert call(_prob(), q=FAKE + 4) == -1
+    # 12 x 16384 rows of a 288-float window: 226 MB of projections, above the
+    # 128 MiB scratch unless a zsave buffer takes them
+    big = _prob(B=1, H=12, N=16384)
+    assert call(big) == -3
+    err = L.relpos_last_error().decode()
+    assert "allocation-free limit" in err and str(b.NOALLOC_SCRATCH_BYTES) in err
+    ws = ctypes.c_size_t()
+    assert L.relpos_attn_workspace_size(ctypes.byref(big), ctypes.byref(phi), ctypes.byref(m), 1,
+                                        0, 0, ctypes.byref(ws)) == 0
+    assert ws.value > b.NOALLOC_SCRATCH_BYTES
