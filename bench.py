@@ -74,6 +74,8 @@ def describe(w):
            "terms": terms or "none", "mask": mask or "none", "tau": round(w.tau, 6)}
     if w.dropout is not None:
         out["dropout_p"] = w.dropout[0] / 256.0
+    if w.zchunk:
+        out["zchunk"] = w.zchunk
     return out
 
 
@@ -217,7 +219,8 @@ def measure_peak_memory(torch, dev, t, w, drop):
     and its workspace.  Run outside the timed region."""
     import exact_relative_position_amd as rp
     args = (t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"])
-    kw = dict(phi=w.phi, tau=w.tau, causal=w.causal, key_len=t["key_len"], dropout=drop)
+    kw = dict(phi=w.phi, tau=w.tau, causal=w.causal, key_len=t["key_len"], dropout=drop,
+              zchunk=w.zchunk)
     torch.cuda.synchronize(dev)
     base = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
@@ -288,8 +291,9 @@ def run_sweep(args):
     dev = torch.device("cuda:0")
     if args.memory_scaling:
         from relpos_synth import memory_scaling_workloads
-        todo = memory_scaling_workloads()
-        metric = "memory scaling in N (Shaw, 1x12xN fp16): fwd and bwd ms, extra memory"
+        todo = memory_scaling_workloads(args.memory_scaling)
+        metric = (f"memory scaling in N ({args.memory_scaling}, 1x12xN fp16): fwd and bwd ms, "
+                  "extra memory")
     else:
         mechs = None if args.sweep == "all" else set(args.sweep.split(","))
         todo = {n: w for n, w in sweep_workloads().items()
@@ -302,7 +306,8 @@ def run_sweep(args):
         mem_inputs = torch.cuda.memory_allocated(dev)
         torch.cuda.reset_peak_memory_stats(dev)
         run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
-                          tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True)
+                          tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True,
+                          zchunk=w.zchunk)
         stage_ms, gpu_ms, _ = time_stages(torch, dev, stage_list(B_, run), args.warmup,
                                           args.steps)
         peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs
@@ -341,10 +346,16 @@ def main():
                     help="instead of the one-line step benchmark, run the layer sweep "
                          "(N = 128 .. 8192 at 16384 tokens) for 'all' or a comma list of "
                          "shaw, txl, deberta, t5; one JSON line per point")
-    ap.add_argument("--memory-scaling", action="store_true",
+    ap.add_argument("--memory-scaling", nargs="?", const="shaw", default=None,
+                    metavar="MECH",
                     help="instead of the one-line step benchmark, run the Shaw workload "
-                         "(1x12xN fp16) at N = 1K .. 16K; one JSON line per N with the "
-                         "memory allocated beyond the inputs")
+                         "(1x12xN fp16; or 'txl': the Transformer-XL identity map at that "
+                         "shape with its projection computed 1024 queries at a time) at "
+                         "N = 1K .. 16K; one JSON line per N with the memory allocated "
+                         "beyond the inputs")
+    ap.add_argument("--zchunk", type=int, default=0,
+                    help="compute the query-side projection this many queries at a time "
+                         "(a multiple of 128; 0 = the whole sequence)")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="attention dropout probability (fp16/bf16; rounded to a multiple "
                          "of 1/256; generator seed 2024, offset 0)")
@@ -366,6 +377,8 @@ def main():
     from relpos_synth import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.zchunk:
+        w = w.with_(name=f"{w.name}_chunk{args.zchunk}", zchunk=args.zchunk)
     t_drop = int(round(args.dropout * 256))
     if t_drop > 0:
         w = w.with_(name=f"{w.name}_dropout{t_drop}", dropout=(t_drop, 2024, 0))
@@ -381,7 +394,7 @@ def main():
     drop = None if w.dropout is None else (w.dropout[0] / 256.0, w.dropout[1], w.dropout[2])
     run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
                       tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True,
-                      dropout=drop)
+                      dropout=drop, zchunk=w.zchunk)
     stages = stage_list(B_, run, args.separate_passes)
     stage_ms, gpu_ms, wall = time_stages(torch, dev, stages, args.warmup, args.steps)
     peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs

@@ -49,7 +49,7 @@ class Problem(ctypes.Structure):
                 ("strides", (ctypes.c_int64 * 3) * 8), ("aq_head_stride", ctypes.c_int64),
                 ("ak_head_stride", ctypes.c_int64), ("b_head_stride", ctypes.c_int64),
                 ("dropout_p", ctypes.c_float), ("dropout_offset", ctypes.c_uint32),
-                ("dropout_seed", ctypes.c_uint64)]
+                ("dropout_seed", ctypes.c_uint64), ("zchunk", ctypes.c_int64)]
 
 
 class RelposError(RuntimeError):
@@ -219,9 +219,10 @@ def _check_zsave(zsave, q, nbytes):
                          f"{nbytes} bytes (the forward's saved projections)")
 
 
-def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None):
+def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None, zchunk=0):
     """Problem descriptor; ``tensors`` maps a role index to its [B,H,N,d] tensor;
-    ``dropout`` = (p, seed, offset) or None."""
+    ``dropout`` = (p, seed, offset) or None; ``zchunk`` = query rows per chunk
+    of the projection (0: the whole sequence)."""
     B, H, N, d = q.shape
     p = Problem()
     p.B, p.H, p.N, p.d = B, H, N, d
@@ -237,6 +238,7 @@ def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None):
         p.dropout_p = float(dropout[0])
         p.dropout_seed = int(dropout[1]) & 0xFFFFFFFFFFFFFFFF
         p.dropout_offset = int(dropout[2]) & 0xFFFFFFFF
+    p.zchunk = int(zchunk)
     return p
 
 
@@ -295,22 +297,24 @@ def phi_rows(phi, N, device="cuda"):
 
 
 def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_len=None,
-            keep_z=True, out=None, dropout=None):
+            keep_z=True, out=None, dropout=None, zchunk=0):
     """O, LSE (and the saved projections, or None) of the relative-position
-    attention; ``dropout`` = (p, seed, offset) or None."""
+    attention; ``dropout`` = (p, seed, offset) or None; ``zchunk`` > 0 computes
+    the projection one chunk of queries at a time (nothing is kept)."""
     check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len,
                  tensors=(() if out is None else (("out", out),)))
     dev = q.device
     O = torch.empty_like(q) if out is None else out
     B, H, N, _ = q.shape
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout)
+    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout, zchunk)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     terms = _terms(aq, ak, b)
     zs = None
     if keep_z and (aq is not None or ak is not None):
-        zs = _workspace(zsave_size(prob, phi_s, terms), dev)
+        nz = zsave_size(prob, phi_s, terms)
+        zs = _workspace(nz, dev) if nz > 0 else None
     ws = _workspace(workspace_size(prob, phi_s, mask_s, terms, PASS_FWD, zs is not None), dev)
     _check(lib().relpos_attn_fwd(ctypes.byref(prob), ctypes.byref(phi_s), ctypes.byref(mask_s),
                                  _ptr(q), _ptr(k), _ptr(v), _ptr(aq), _ptr(ak), _ptr(b),
@@ -320,13 +324,13 @@ def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_le
 
 
 def forward_noalloc(q, k, v, aq=None, ak=None, b=None, *, phi, tau, O, lse, zsave=None,
-                    causal=False, key_len=None, dropout=None):
+                    causal=False, key_len=None, dropout=None, zchunk=0):
     """relpos_attn_fwd_noalloc: the forward into caller-given O and LSE (and
     zsave, or None), with the library's static scratch instead of a
     workspace; allocates nothing."""
     check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("O", O),))
     _check_lse(lse, q)
-    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout)
+    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout, zchunk)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     _check_zsave(zsave, q, zsave_size(prob, phi_s, _terms(aq, ak, b)))
@@ -337,7 +341,7 @@ def forward_noalloc(q, k, v, aq=None, ak=None, b=None, *, phi, tau, O, lse, zsav
 
 
 def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=False,
-             key_len=None, dropout=None):
+             key_len=None, dropout=None, zchunk=0):
     """dQ, dK, dV (input dtype) and daQ, daK, db (fp32, shape of their table, or None)."""
     check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("o", o), ("do", do)))
     _check_lse(lse, q)
@@ -347,7 +351,7 @@ def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=Fal
     dak = None if ak is None else torch.empty(ak.shape, dtype=torch.float32, device=dev)
     db = None if b is None else torch.empty(b.shape, dtype=torch.float32, device=dev)
     prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: o, T_DO: do, T_DQ: dq, T_DK: dk,
-                            T_DV: dv}, aq, ak, b, dropout)
+                            T_DV: dv}, aq, ak, b, dropout, zchunk)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     terms = _terms(aq, ak, b)
@@ -367,7 +371,7 @@ class Prepared:
     library calls (nothing is allocated in between)."""
 
     def __init__(self, q, k, v, aq, ak, b, do, *, phi, tau, causal=False, key_len=None,
-                 keep_z=True, dropout=None):
+                 keep_z=True, dropout=None, zchunk=0):
         check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("do", do),))
         dev = q.device
         self.dev = dev
@@ -382,13 +386,14 @@ class Prepared:
         self.dak = None if ak is None else torch.empty(ak.shape, **f32)
         self.db = None if b is None else torch.empty(b.shape, **f32)
         self.prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: self.O, T_DO: do, T_DQ: self.dq,
-                                     T_DK: self.dk, T_DV: self.dv}, aq, ak, b, dropout)
+                                     T_DK: self.dk, T_DV: self.dv}, aq, ak, b, dropout, zchunk)
         self.phi_s = phi_struct(phi)
         self.mask_s = mask_struct(causal, key_len)
         terms = _terms(aq, ak, b)
         self.zs = None
         if keep_z and (aq is not None or ak is not None):
-            self.zs = _workspace(zsave_size(self.prob, self.phi_s, terms), dev)
+            nz = zsave_size(self.prob, self.phi_s, terms)
+            self.zs = _workspace(nz, dev) if nz > 0 else None
         zg = self.zs is not None
         self.ws_f = _workspace(workspace_size(self.prob, self.phi_s, self.mask_s, terms,
                                               PASS_FWD, zg), dev)

@@ -75,7 +75,10 @@ struct Plan {
   int64_t aq_hs = 0, ak_hs = 0, b_hs = 0;
   int nblk = 0;        // 128-row blocks per (b, h)
   int ncol_q = 0, ncol_k = 0;
-  size_t z_elems = 0;  // one projection buffer, elements
+  int zr = 0;          // query rows per chunk of the query-side projection
+  int nchunk = 1;      // chunks of queries (1: the whole sequence at once)
+  size_t zq_elems = 0; // query-side projection buffer (Z^Q, dZ^Q), elements
+  size_t zk_elems = 0; // key-side projection buffer (Z^K, dZ^K), elements
   int rtiles = 0, Rpad = 0;
   int split_q = 1, split_k = 1, split_b = 1;
   int ho_aq = 1, ho_ak = 1, ho_b = 1;
@@ -232,7 +235,20 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   pl.ho_ak = pl.ak_hs == 0 ? 1 : pl.H;
   pl.ho_b = pl.b_hs == 0 ? 1 : pl.H;
   pl.nblk = (pl.N + kBlockRows - 1) / kBlockRows;
-  pl.z_elems = (size_t)pl.B * pl.H * pl.N * pl.geo.Wp;
+  if (prob->zchunk < 0 || prob->zchunk % kBlockRows)
+    return fail(RELPOS_ERR_INVALID_ARG, "zchunk must be a non-negative multiple of 128");
+  pl.zr = pl.N;
+  if (prob->zchunk > 0 && prob->zchunk < pl.N) {
+    pl.zr = (int)prob->zchunk;
+    pl.nchunk = (pl.N + pl.zr - 1) / pl.zr;
+    if (pl.has_ak)
+      return fail(RELPOS_ERR_UNSUPPORTED,
+                  "a chunked projection covers the query-side terms only (aK must be absent)");
+  }
+  pl.geo.zr = pl.zr;
+  pl.geo.z0 = 0;
+  pl.zq_elems = (size_t)pl.B * pl.H * pl.zr * pl.geo.Wp;
+  pl.zk_elems = (size_t)pl.B * pl.H * pl.N * pl.geo.Wp;
   // column tiles of the projection (max over groups)
   for (int grp = 0; grp < pl.nblk; ++grp) {
     int cb, ce;
@@ -325,6 +341,8 @@ struct WsBwd {
   float* part_q = nullptr;
   float* part_qb = nullptr;
   float* part_k = nullptr;
+  float* dk_acc = nullptr;
+  float* dv_acc = nullptr;
 };
 
 bool need_bunf(const Plan& pl) { return pl.has_b && !pl.has_aq; }
@@ -334,8 +352,8 @@ size_t carve_fwd(const Plan& pl, bool zsave_given, void* base, WsFwd& w) {
   if (pl.bucketed) w.fold = c.take<int32_t>(sizeof(int32_t) * pl.Runf);
   if (need_bunf(pl)) w.bunf = c.take<float>(sizeof(float) * pl.Runf * pl.ho_b);
   if (!zsave_given) {
-    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
-    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.zq_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.zk_elems);
   }
   return c.off;
 }
@@ -350,8 +368,8 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
   }
   if (need_bunf(pl)) w.bunf = c.take<float>(sizeof(float) * pl.Runf * pl.ho_b);
   if (!zsave_given) {
-    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
-    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.zq_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.zk_elems);
   }
   const size_t bhnp = (size_t)pl.B * pl.H * pl.Np;
   w.L2 = c.take<float>(sizeof(float) * bhnp);
@@ -373,8 +391,13 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
   }
   if (pl.has_aq) w.dq_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
   if (pl.has_ak) w.dk_part = c.take<float>(sizeof(float) * bhn * kHeadDim);
-  if (pl.has_aq || pl.has_b) w.dzq = c.take<float>(sizeof(float) * pl.z_elems);
-  if (pl.has_ak) w.dzk = c.take<float>(sizeof(float) * pl.z_elems);
+  if (pl.has_aq || pl.has_b) w.dzq = c.take<float>(sizeof(float) * pl.zq_elems);
+  if (pl.has_ak) w.dzk = c.take<float>(sizeof(float) * pl.zk_elems);
+  if (pl.nchunk > 1) {
+    // dK, dV summed over the chunks (fp32)
+    w.dk_acc = c.take<float>(sizeof(float) * bhn * kHeadDim);
+    w.dv_acc = c.take<float>(sizeof(float) * bhn * kHeadDim);
+  }
   if (pl.has_aq)
     w.part_q = c.take<float>(sizeof(float) * pl.split_q * pl.ho_aq * pl.Rpad * kHeadDim);
   if (pl.has_b) w.part_qb = c.take<float>(sizeof(float) * pl.split_b * pl.ho_b * pl.Rpad);
@@ -384,9 +407,10 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
 }
 
 size_t zsave_bytes(const Plan& pl) {
+  if (pl.nchunk > 1) return 0;  // a chunked projection is never kept
   size_t n = 0;
-  if (pl.has_aq) n += align256(sizeof(float) * pl.z_elems);
-  if (pl.has_ak) n += align256(sizeof(float) * pl.z_elems);
+  if (pl.has_aq) n += align256(sizeof(float) * pl.zq_elems);
+  if (pl.has_ak) n += align256(sizeof(float) * pl.zk_elems);
   return n;
 }
 
@@ -422,9 +446,12 @@ relpos_status prepare_tables(const Plan& pl, const void* b, int32_t* fold, int32
   return RELPOS_OK;
 }
 
+// Z^Q (query groups [g0, g0 + ngroups), into the query-side buffer laid out
+// by geo) and Z^K (every key group).
 relpos_status project(const Plan& pl, const relpos_problem* prob, const void* Q, const void* K,
                       const void* aQ, const void* aK, const void* b, const int32_t* fold,
-                      float* zq, float* zk, hipStream_t st) {
+                      float* zq, float* zk, hipStream_t st, const Geo& geo, int g0,
+                      int ngroups) {
   if (pl.has_aq) {
     ProjArgs pa{};
     pa.x = Q;
@@ -437,10 +464,11 @@ relpos_status project(const Plan& pl, const relpos_problem* prob, const void* Q,
     pa.z = zq;
     pa.B = pl.B;
     pa.H = pl.H;
-    pa.geo = pl.geo;
+    pa.geo = geo;
     pa.key_side = 0;
     pa.ncol_tiles = pl.ncol_q;
-    pa.ngroups = pl.nblk;
+    pa.ngroups = ngroups;
+    pa.g0 = g0;
     relpos_status s = hip_check(launch_proj(pl.dtype, pa, st), "projection Q");
     if (s != RELPOS_OK) return s;
   }
@@ -482,6 +510,14 @@ int device_cus() {
   return n;
 }
 
+// Causal 16-bit launches whose blocks all fit on the device at once (two
+// per CU) split each block's tiles between two wave groups: the longest
+// block then bounds the pass, and splitting halves it.  With more blocks the
+// longest-first order already balances the CUs.
+int split_blocks(const Plan& pl, int64_t blocks) {
+  return pl.geo.causal && pl.esz == 2 && blocks <= 2 * (int64_t)device_cus();
+}
+
 AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask* mask,
                    const void* Q, const void* K, const void* V) {
   AttnArgs a{};
@@ -515,12 +551,12 @@ AttnArgs attn_args(const Plan& pl, const relpos_problem* prob, const relpos_mask
   a.bunf_hs = pl.b_hs == 0 ? 0 : pl.Runf;
   a.nblk = pl.nblk;
   a.Np = pl.Np;
-  // Causal 16-bit launches whose blocks all fit on the device at once (two
-  // per CU) split each block's tiles between two wave groups: the longest
-  // block then bounds the pass, and splitting halves it.  With more blocks
-  // the longest-first order already balances the CUs.
-  a.split = pl.geo.causal && pl.esz == 2 &&
-            (int64_t)pl.B * pl.H * pl.nblk <= 2 * (int64_t)device_cus();
+  a.qb0 = 0;
+  a.nqb = pl.nblk;
+  a.qt0 = 0;
+  a.qt1 = (pl.N + 63) / 64;  // every 64-row query tile
+  a.kacc = 0;
+  a.split = split_blocks(pl, (int64_t)pl.B * pl.H * pl.nblk);
   return a;
 }
 
@@ -583,6 +619,8 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
   if ((s = check_tables(pl, aQ, aK, b)) != RELPOS_OK) return s;
   if (!lse || !aligned16(lse)) return fail(RELPOS_ERR_INVALID_ARG, "lse null or misaligned");
   if (zsave && !aligned16(zsave)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: zsave");
+  if (zsave && pl.nchunk > 1)
+    return fail(RELPOS_ERR_INVALID_ARG, "zsave must be NULL when the projection is chunked");
   WsFwd w;
   const size_t need = carve_fwd(pl, zsave != nullptr, nullptr, w);
   if (use_scratch) {
@@ -602,13 +640,16 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
   carve_fwd(pl, zsave != nullptr, workspace, w);
   if (zsave) {
     Carve c(zsave);
-    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
-    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.zq_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.zk_elems);
   }
   hipStream_t st = (hipStream_t)stream;
   if (stages & RELPOS_FWD_PROJECT) {
     if ((s = prepare_tables(pl, b, w.fold, nullptr, nullptr, w.bunf, st)) != RELPOS_OK) return s;
-    if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st)) != RELPOS_OK) return s;
+    if (pl.nchunk == 1 &&
+        (s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st, pl.geo, 0, pl.nblk)) !=
+            RELPOS_OK)
+      return s;
   }
   if (!(stages & RELPOS_FWD_ATTEND)) return RELPOS_OK;
   AttnArgs a = attn_args(pl, prob, mask, Q, K, V);
@@ -617,7 +658,144 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
   a.zq = w.zq;
   a.zk = w.zk;
   a.bunf = w.bunf;
-  return hip_check(launch_fwd(pl.dtype, a, st), "forward");
+  if (pl.nchunk == 1) return hip_check(launch_fwd(pl.dtype, a, st), "forward");
+  // chunked projection: Z^Q of one chunk of queries, then their attention
+  for (int c = 0; c < pl.nchunk; ++c) {
+    Geo gc = pl.geo;
+    gc.z0 = c * pl.zr;
+    const int nb = (std::min(pl.zr, pl.N - gc.z0) + kBlockRows - 1) / kBlockRows;
+    if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st, gc, gc.z0 / kBlockRows,
+                     nb)) != RELPOS_OK)
+      return s;
+    a.geo = gc;
+    a.qb0 = gc.z0 / kBlockRows;
+    a.nqb = nb;
+    a.split = split_blocks(pl, (int64_t)pl.B * pl.H * nb);
+    if ((s = hip_check(launch_fwd(pl.dtype, a, st), "forward")) != RELPOS_OK) return s;
+  }
+  return RELPOS_OK;
+}
+
+// Backward with a chunked projection (the query-side terms only).  The map
+// tables come with BWD_PREPARE; the passes (both bits) run, per chunk of zr
+// queries in order: Z^Q of the chunk, the chunk's row terms, the query pass
+// over its query blocks, the key pass over its query tiles (dK, dV summed in
+// fp32 over the chunks, the last chunk writing the outputs), then the
+// chunk's share of the contraction (dQ rows; daQ, db summed over the chunks).
+relpos_status bwd_chunks(const Plan& pl, const relpos_problem* prob, int32_t stages,
+                         const void* Q, const void* K, const void* aQ, const void* b,
+                         const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                         void* dV, float* daQ, float* db, const WsBwd& w, AttnArgs a,
+                         hipStream_t st) {
+  (void)K;
+  (void)dK;
+  (void)dV;
+  relpos_status s;
+  if (stages & RELPOS_BWD_PREPARE) {
+    if ((s = prepare_tables(pl, b, w.fold, w.ub, w.ue, w.bunf, st)) != RELPOS_OK) return s;
+  }
+  if (!(stages & RELPOS_BWD_QUERY_PASS)) return RELPOS_OK;
+  const int64_t tu_hs = (int64_t)(pl.Runf + 32) * kHeadDim;
+  void* tunf_lo = nullptr;
+  if (pl.has_aq) {
+    tunf_lo = pl.dtype == 1 ? (void*)((uint16_t*)w.tunf_q + (size_t)pl.ho_aq * tu_hs) : nullptr;
+    TabUnfoldArgs t{aQ, pl.aq_hs, pl.bucketed ? w.fold : nullptr, w.tunf_q, tunf_lo, pl.ho_aq,
+                    pl.Runf};
+    if ((s = hip_check(launch_tab_unfold(pl.dtype, t, st), "table unfold aQ")) != RELPOS_OK)
+      return s;
+    if (pl.dtype == 1) {
+      SplitArgs x{Q, str_of(prob, RELPOS_T_Q), w.xq_h, w.xq_l, pl.B, pl.H, pl.N};
+      if ((s = hip_check(launch_xsplit(x, st), "split Q")) != RELPOS_OK) return s;
+    }
+  }
+  const float dseed_scale = pl.drop_t > 0 ? (float)(256 - pl.drop_t) / 256.f : 1.f;
+  const int32_t* ub = pl.bucketed ? w.ub : nullptr;
+  const int32_t* ue = pl.bucketed ? w.ue : nullptr;
+  const bool joint_b = pl.has_aq && pl.has_b && pl.ho_aq == pl.ho_b && pl.split_q == pl.split_b;
+  a.dk_acc = w.dk_acc;
+  a.dv_acc = w.dv_acc;
+  for (int c = 0; c < pl.nchunk; ++c) {
+    Geo gc = pl.geo;
+    gc.z0 = c * pl.zr;
+    const int rows = std::min(pl.zr, pl.N - gc.z0);
+    const int nb = (rows + kBlockRows - 1) / kBlockRows;
+    const int rb0 = gc.z0 / kBlockRows;
+    if (pl.has_aq &&
+        (s = project(pl, prob, Q, K, aQ, nullptr, b, w.fold, w.zq, nullptr, st, gc, rb0, nb)) !=
+            RELPOS_OK)
+      return s;
+    RowTermArgs r{O,    dO,   str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), lse,
+                  w.L2, w.D,  w.kseed, dseed_scale, w.zq, gc,
+                  prob->tau * 1.4426950408889634f, pl.B, pl.H, pl.N, pl.Np,
+                  gc.z0, std::min(gc.z0 + pl.zr, pl.Np)};
+    if ((s = hip_check(launch_rowterm(pl.dtype, r, st), "backward (row terms)")) != RELPOS_OK)
+      return s;
+    a.geo = gc;
+    a.qb0 = rb0;
+    a.nqb = nb;
+    a.split = split_blocks(pl, (int64_t)pl.B * pl.H * nb);
+    auto launch_passes = [&](bool q, bool k) {
+      return pl.dtype == 0   ? launch_bwd_f32(a, q, k, st)
+             : pl.dtype == 1 ? launch_bwd_f16(a, q, k, st)
+                             : launch_bwd_bf16(a, q, k, st);
+    };
+    if ((s = hip_check(launch_passes(true, false), "backward (query pass)")) != RELPOS_OK)
+      return s;
+    a.qt0 = gc.z0 / 64;
+    a.qt1 = (gc.z0 + rows + 63) / 64;
+    a.kacc = (c > 0 ? 1 : 0) | (c + 1 < pl.nchunk ? 2 : 0);
+    a.split = split_blocks(pl, (int64_t)pl.B * pl.H * pl.nblk);
+    if ((s = hip_check(launch_passes(false, true), "backward (key pass)")) != RELPOS_OK) return s;
+    // this chunk's contraction: dQ rows, then its share of daQ and db
+    if (pl.has_aq) {
+      RowsArgs ra{w.dq_part, w.dzq, w.tunf_q, tunf_lo, pl.aq_hs == 0 ? 0 : tu_hs, dQ,
+                  str_of(prob, RELPOS_T_DQ), pl.B, pl.H, gc, 0, nb, rb0};
+      if ((s = hip_check(launch_rows(pl.dtype, ra, st), "contraction dQ")) != RELPOS_OK) return s;
+      ColsArgs cq{};
+      cq.dz = w.dzq;
+      cq.x = Q;
+      cq.xh = w.xq_h;
+      cq.xl = w.xq_l;
+      cq.sx = str_of(prob, RELPOS_T_Q);
+      cq.part = w.part_q;
+      cq.partb = joint_b ? w.part_qb : nullptr;
+      cq.B = pl.B;
+      cq.H = pl.H;
+      cq.geo = gc;
+      cq.key_side = 0;
+      cq.shared = pl.aq_hs == 0;
+      cq.splits = pl.split_q;
+      cq.rtiles = pl.rtiles;
+      cq.Rpad = pl.Rpad;
+      cq.want_x = 1;
+      if ((s = hip_check(cols(pl, cq, pl.ho_aq, st), "contraction daQ")) != RELPOS_OK) return s;
+      FoldArgs f{w.part_q, joint_b ? w.part_qb : nullptr, ub, ue, daQ, joint_b ? db : nullptr,
+                 pl.ho_aq, pl.R, pl.Rpad, pl.split_q, c > 0 ? 1 : 0};
+      if ((s = hip_check(launch_fold(f, st), "fold daQ")) != RELPOS_OK) return s;
+    }
+    if (pl.has_b && !joint_b) {
+      ColsArgs cb{};
+      cb.dz = w.dzq;
+      cb.x = Q;
+      cb.sx = str_of(prob, RELPOS_T_Q);
+      cb.part = nullptr;
+      cb.partb = w.part_qb;
+      cb.B = pl.B;
+      cb.H = pl.H;
+      cb.geo = gc;
+      cb.key_side = 0;
+      cb.shared = pl.b_hs == 0;
+      cb.splits = pl.split_b;
+      cb.rtiles = pl.rtiles;
+      cb.Rpad = pl.Rpad;
+      cb.want_x = 0;
+      if ((s = hip_check(cols(pl, cb, pl.ho_b, st), "contraction db")) != RELPOS_OK) return s;
+      FoldArgs f{nullptr, w.part_qb, ub, ue, nullptr, db, pl.ho_b, pl.R, pl.Rpad, pl.split_b,
+                 c > 0 ? 1 : 0};
+      if ((s = hip_check(launch_fold(f, st), "fold db")) != RELPOS_OK) return s;
+    }
+  }
+  return RELPOS_OK;
 }
 
 }  // namespace
@@ -787,17 +965,25 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
     return fail(RELPOS_ERR_WORKSPACE, "workspace smaller than relpos_attn_workspace_size()");
   if (!aligned16(workspace)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: workspace");
   if (zsave && !aligned16(zsave)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: zsave");
+  if (zsave && pl.nchunk > 1)
+    return fail(RELPOS_ERR_INVALID_ARG, "zsave must be NULL when the projection is chunked");
+  if (pl.nchunk > 1 && (stages & (RELPOS_BWD_QUERY_PASS | RELPOS_BWD_KEY_PASS)) &&
+      (stages & (RELPOS_BWD_QUERY_PASS | RELPOS_BWD_KEY_PASS)) !=
+          (RELPOS_BWD_QUERY_PASS | RELPOS_BWD_KEY_PASS))
+    return fail(RELPOS_ERR_INVALID_ARG, "a chunked backward runs both passes together");
   carve_bwd(pl, zsave != nullptr, workspace, w);
   if (zsave) {
     Carve c(const_cast<void*>(zsave));
-    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.z_elems);
-    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.z_elems);
+    if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.zq_elems);
+    if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.zk_elems);
   }
 
   if (stages & RELPOS_BWD_PREPARE) {
     if ((s = prepare_tables(pl, b, w.fold, w.ub, w.ue, w.bunf, st)) != RELPOS_OK) return s;
-    if (!zsave) {
-      if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st)) != RELPOS_OK) return s;
+    if (!zsave && pl.nchunk == 1) {
+      if ((s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st, pl.geo, 0, pl.nblk)) !=
+        RELPOS_OK)
+      return s;
     }
   }
 
@@ -816,11 +1002,13 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
   a.dv = dV;
   a.dzq = w.dzq;
   a.dzk = w.dzk;
+  if (pl.nchunk > 1)
+    return bwd_chunks(pl, prob, stages, Q, K, aQ, b, O, lse, dO, dQ, dK, dV, daQ, db, w, a, st);
   if (stages & RELPOS_BWD_PREPARE) {
     const float dseed_scale = pl.drop_t > 0 ? (float)(256 - pl.drop_t) / 256.f : 1.f;
     RowTermArgs r{O,      dO,    str_of(prob, RELPOS_T_O), str_of(prob, RELPOS_T_DO), lse,
                   w.L2,   w.D,   w.kseed, dseed_scale, w.zq, pl.geo,
-                  prob->tau * 1.4426950408889634f, pl.B, pl.H, pl.N, pl.Np};
+                  prob->tau * 1.4426950408889634f, pl.B, pl.H, pl.N, pl.Np, 0, pl.Np};
     if ((s = hip_check(launch_rowterm(pl.dtype, r, st), "backward (row terms)")) != RELPOS_OK)
       return s;
   }

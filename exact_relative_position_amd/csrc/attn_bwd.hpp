@@ -93,15 +93,15 @@ static void launch_bwd_z(const AttnArgs& a, bool zk, bool sq, bool sk, int grid,
   }
 }
 
-// Launch the query pass (want_q), the key pass (want_k) or both over the
-// B*H*nblk blocks of each.
+// Launch the query pass (want_q: the B*H*nqb blocks of its query range),
+// the key pass (want_k: B*H*nblk blocks) or both.
 template <typename T>
 hipError_t launch_bwd_t(const AttnArgs& a, bool want_q, bool want_k, hipStream_t st) {
   static_assert(kStageMinW >= kStageMinWK, "staging of the query pass implies the key pass's");
-  const int total = a.B * a.H * a.nblk;
-  const int kblocks = want_k ? total : 0, grid = kblocks + (want_q ? total : 0);
+  const int kblocks = want_k ? a.B * a.H * a.nblk : 0;
+  const int grid = kblocks + (want_q ? a.B * a.H * a.nqb : 0);
   if (grid == 0) return hipSuccess;
-  const int weave = want_q && want_k && a.geo.causal;
+  const int weave = want_q && want_k && a.geo.causal && a.nqb == a.nblk;
   const bool zq = a.flags & F_ZQ, zk = a.flags & F_ZK;
   const bool sq = a.geo.W >= kStageMinW, sk = zk && a.geo.W >= kStageMinWK;
   if constexpr (sizeof(T) == 2) {

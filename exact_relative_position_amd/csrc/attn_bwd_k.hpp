@@ -141,9 +141,10 @@ struct BwdK {
   __device__ __forceinline__ void band_rel(int ib, int wq, float (&v)[16]) const {
     const int Wm = g.W - 1;
     if (has_zq) {
+      const int ilast = zq_last(g);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int i = imin(ib + kap0<T>(e), N - 1);
+        const int i = imin(ib + kap0<T>(e), ilast);
         v[e] += zq_bh[(int64_t)i * g.Wp + imin(imax(jk - i - g.lo - wq, 0), Wm)];
       }
     }
@@ -397,11 +398,12 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
   int kv_end = N;
   if (a.flags & F_KEYPAD) kv_end = imax(0, imin(N, a.key_len[bb]));
   k.kv_end = kv_end;
-  const int qt_begin = g.causal ? j0b / kTile : 0;
-  const int ntq = (N + kTile - 1) / kTile;
+  // query tiles of this launch: [qt0, qt1), from the causal diagonal on
+  const int qt_begin = imax(g.causal ? j0b / kTile : 0, a.qt0);
+  const int ntq = imin((N + kTile - 1) / kTile, a.qt1);
   k.ntq = ntq;
   // Whole block padded away: nothing to recompute, every output is zero.
-  const int t_begin = (j0b >= kv_end) ? ntq : qt_begin;
+  const int t_begin = (j0b >= kv_end) ? ntq : imin(qt_begin, ntq);
 
   k.Qb = (const T*)a.q + bb * a.sq.b + hh * a.sq.h;
   k.Ob = (const T*)a.dO + bb * a.sdo.b + hh * a.sdo.h;
@@ -419,7 +421,7 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
   }
   k.seed_stride = (int64_t)a.B * a.H * a.Np;
   k.seeds = a.kseed + (int64_t)bh * a.Np;
-  k.zq_bh = k.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr;
+  k.zq_bh = k.has_zq ? a.zq + zq_off(g, bh, 0) : nullptr;
   k.bun = k.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   k.wsk = win_k(g, kb);
   k.zk_row = k.has_zk ? a.zk + ((int64_t)bh * N + imin(jk, N - 1)) * g.Wp : nullptr;
@@ -520,7 +522,39 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
     k.acc_lo = 0.f;
     k.acc_hi = 0.f;
   }
-  if (jk < N) {
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) k.dk[dt][e] *= a.tau;
+  if (jk < N && a.kacc) {
+    // one of several launches over disjoint query ranges: the fp32 sums of
+    // the earlier ones are added in launch order, and all but the last
+    // launch hand theirs on instead of writing the outputs
+    float* av = a.dv_acc + ((int64_t)bh * N + jk) * kHeadDim;
+    float* ak = a.dk_acc + ((int64_t)bh * N + jk) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = 32 * dt + 8 * e4 + 4 * hl;
+        if (a.kacc & 1) {
+          const f32x4 pv = *reinterpret_cast<const f32x4*>(av + d);
+          const f32x4 pk = *reinterpret_cast<const f32x4*>(ak + d);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            k.dv[dt][4 * e4 + t] = pv[t] + k.dv[dt][4 * e4 + t];
+            k.dk[dt][4 * e4 + t] = pk[t] + k.dk[dt][4 * e4 + t];
+          }
+        }
+        if (a.kacc & 2) {
+          store4<float>(av + d, k.dv[dt][4 * e4], k.dv[dt][4 * e4 + 1], k.dv[dt][4 * e4 + 2],
+                        k.dv[dt][4 * e4 + 3]);
+          store4<float>(ak + d, k.dk[dt][4 * e4], k.dk[dt][4 * e4 + 1], k.dk[dt][4 * e4 + 2],
+                        k.dk[dt][4 * e4 + 3]);
+        }
+      }
+  }
+  if (jk < N && !(a.kacc & 2)) {
     T* vrow = (T*)a.dv + bb * a.sdv.b + hh * a.sdv.h + (int64_t)jk * a.sdv.n;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -537,8 +571,8 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int d = 32 * dt + 8 * e4 + 4 * hl;
-          store4<float>(prow + d, a.tau * k.dk[dt][4 * e4], a.tau * k.dk[dt][4 * e4 + 1],
-                        a.tau * k.dk[dt][4 * e4 + 2], a.tau * k.dk[dt][4 * e4 + 3]);
+          store4<float>(prow + d, k.dk[dt][4 * e4], k.dk[dt][4 * e4 + 1], k.dk[dt][4 * e4 + 2],
+                        k.dk[dt][4 * e4 + 3]);
         }
     } else {
       T* krow = (T*)a.dk + bb * a.sdk.b + hh * a.sdk.h + (int64_t)jk * a.sdk.n;
@@ -547,8 +581,8 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int d = 32 * dt + 8 * e4 + 4 * hl;
-          store4<T>(krow + d, a.tau * k.dk[dt][4 * e4], a.tau * k.dk[dt][4 * e4 + 1],
-                    a.tau * k.dk[dt][4 * e4 + 2], a.tau * k.dk[dt][4 * e4 + 3]);
+          store4<T>(krow + d, k.dk[dt][4 * e4], k.dk[dt][4 * e4 + 1], k.dk[dt][4 * e4 + 2],
+                    k.dk[dt][4 * e4 + 3]);
         }
     }
   }

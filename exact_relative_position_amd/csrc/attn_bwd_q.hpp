@@ -328,10 +328,12 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
   q.lane = lane;
   q.hl = hl;
   q.l32 = l32;
-  const int total = a.B * a.H * a.nblk;
+  // the pass covers the query blocks [qb0, qb0 + nqb) of every (b, h)
+  const int total = a.B * a.H * a.nqb;
   int bh, qb;
-  block_of(bid, total, a.nblk, g.causal, bh, qb);
-  if (g.causal) qb = a.nblk - 1 - qb;  // longest rows first
+  block_of(bid, total, a.nqb, g.causal, bh, qb);
+  if (g.causal) qb = a.nqb - 1 - qb;  // longest rows first
+  qb += a.qb0;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
   q.i0 = i0;
@@ -369,7 +371,7 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
   c.has_zk = ZK;
   c.has_b = a.flags & F_B;
   c.wsq = win_q(g, qb);
-  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.Wp : nullptr;
+  c.zq_row = c.has_zq ? a.zq + zq_off(g, bh, imin(iq, zq_last(g))) : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   q.need_dz = a.flags & F_ZQ_NEEDED;
@@ -392,11 +394,11 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
 #pragma unroll
     for (int e = 0; e < 16; ++e) q.dseed[e] = -q.Dl;
   }
-  q.dz_row = q.need_dz ? a.dzq + ((int64_t)bh * N + iq) * g.Wp : nullptr;
-  q.dz_w = q.need_dz ? a.dzq + ((int64_t)bh * N + iw0) * g.Wp : nullptr;
+  q.dz_row = q.need_dz ? a.dzq + zq_off(g, bh, iq) : nullptr;
+  q.dz_w = q.need_dz ? a.dzq + zq_off(g, bh, iw0) : nullptr;
   q.zs.buf[0] = STAGE ? sSt0 + wall * kStageFloats : sSt0;
   q.zs.buf[1] = STAGE ? sSt1 + wall * kStageFloats : sSt1;
-  q.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, -1, lane);
+  q.zs.init(g, c.has_zq ? a.zq + zq_off(g, bh, 0) : nullptr, -1, lane);
   q.dq[0] = zero16();
   q.dq[1] = zero16();
   q.acc_lo = 0.f;

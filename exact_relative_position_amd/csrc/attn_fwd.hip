@@ -333,10 +333,12 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   f.lane = lane;
   f.hl = hl;
   f.l32 = l32;
-  const int total = a.B * a.H * a.nblk;
+  // this launch covers the query blocks [qb0, qb0 + nqb) of every (b, h)
+  const int total = a.B * a.H * a.nqb;
   int bh, qb;
-  block_of(blockIdx.x, total, a.nblk, g.causal, bh, qb);
-  if (g.causal) qb = a.nblk - 1 - qb;  // longest rows first
+  block_of(blockIdx.x, total, a.nqb, g.causal, bh, qb);
+  if (g.causal) qb = a.nqb - 1 - qb;  // longest rows first
+  qb += a.qb0;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int i0 = qb * kBlockRows, iw0 = i0 + 32 * w, iq = iw0 + l32;
   f.i0 = i0;
@@ -373,13 +375,13 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   c.has_zk = ZK;
   c.has_b = a.flags & F_B;
   c.wsq = win_q(g, qb);
-  c.zq_row = c.has_zq ? a.zq + ((int64_t)bh * N + imin(iq, N - 1)) * g.Wp : nullptr;
+  c.zq_row = c.has_zq ? a.zq + zq_off(g, bh, imin(iq, zq_last(g))) : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
   qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
   f.zs.buf[0] = ZQS ? sZQ0 + wall * RowStage::kFloats : sZQ0;
   f.zs.buf[1] = ZQS ? sZQ1 + wall * RowStage::kFloats : sZQ1;
-  f.zs.init(g, c.has_zq ? a.zq + (int64_t)bh * N * g.Wp : nullptr, -1, lane);
+  f.zs.init(g, c.has_zq ? a.zq + zq_off(g, bh, 0) : nullptr, -1, lane);
   f.sc2 = a.scale2;
   if constexpr (DROP) f.dr = drop_ctx(a, bh, lane);
 
@@ -454,7 +456,7 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
 
 template <typename T, bool GRP, bool DROP>
 static hipError_t launch_fwd_g(const AttnArgs& a, hipStream_t st) {
-  const int total = a.B * a.H * a.nblk;
+  const int total = a.B * a.H * a.nqb;
   const bool zk = a.flags & F_ZK, zqs = (a.flags & F_ZQ) && a.geo.W >= kStageMinW;
   const int nt = fwd_threads<T, GRP>();
   if (zk && zqs)

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   const int N = g.N;
   const int total = a.B * a.H * a.nblk;
   const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / a.nblk, rb = lid - bh * a.nblk;
+  const int bh = lid / a.nblk, rb = a.rb0 + lid - bh * a.nblk;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int tid = threadIdx.x;
   RowsK<T> k;
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
     cols_q(g, rb, k.cb, k.ce);
     k.ws = win_q(g, rb);
   }
-  k.dzb = a.dz + (int64_t)bh * N * g.Wp;
+  // rows addressed by token (key side: every key; query side: the held rows)
+  k.dzb = a.key_side ? a.dz + (int64_t)bh * N * g.Wp : a.dz + zq_off(g, bh, 0);
   k.tub = (const float*)a.tunf + hh * a.tunf_hs;
   const int w = k.w, hl = k.hl, l32 = k.l32;
 
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void rows2_kernel(RowsArgs a) {
   const int N = g.N;
   const int total = a.B * a.H * a.nblk;
   const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / a.nblk, rb = lid - bh * a.nblk;
+  const int bh = lid / a.nblk, rb = a.rb0 + lid - bh * a.nblk;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int tid = threadIdx.x;
   Rows2K<T> k;
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void rows2_kernel(RowsArgs a) {
     cols_q(g, rb, k.cb, k.ce);
     k.ws = win_q(g, rb);
   }
-  k.dzb = a.dz + (int64_t)bh * N * g.Wp;
+  k.dzb = a.key_side ? a.dz + (int64_t)bh * N * g.Wp : a.dz + zq_off(g, bh, 0);
   k.thb = (const __bf16*)a.tunf + hh * a.tunf_hs;
   k.tlb = a.tunf_lo ? (const __bf16*)a.tunf_lo + hh * a.tunf_hs : nullptr;
   k.tr.init(k.lane);
@@ -356,6 +357,7 @@ struct ColsK {
   Str sx;            // strides of x (a split X is [B*H][N][64])
   Geo g;
   int N, Wp, H, ho, u0, w, lane, hl, l32, key_side;
+  int rlo, rhi;  // rows of each segment taken: every key, or the held query rows
   bool shared, grp_on;
   RowPos end;  // end of this split's row range
   int cb0, ce0, ws0;  // the single window (ungrouped)
@@ -379,8 +381,8 @@ struct ColsK {
   __device__ __forceinline__ int group_of(RowPos p) const { return grp_on ? p.i / kGroup : 0; }
   // end of the run of rows that shares p's segment and window
   __device__ __forceinline__ RowPos run_end(RowPos p) const {
-    RowPos e = grp_on ? RowPos{p.seg, imin(N, (p.i / kGroup + 1) * kGroup)} : RowPos{p.seg, N};
-    if (e.i >= N) e = RowPos{p.seg + 1, 0};
+    RowPos e = grp_on ? RowPos{p.seg, imin(rhi, (p.i / kGroup + 1) * kGroup)} : RowPos{p.seg, rhi};
+    if (e.i >= rhi) e = RowPos{p.seg + 1, rlo};
     return before(end, e) ? end : e;
   }
   // first row at or after p (end if none) whose window's live columns meet
@@ -397,12 +399,12 @@ struct ColsK {
   // rows of the chunk starting at p: up to 64, inside one run
   __device__ __forceinline__ int chunk_rows(RowPos p) const {
     const RowPos e = run_end(p);
-    const int n = e.seg == p.seg ? e.i - p.i : N - p.i;
+    const int n = e.seg == p.seg ? e.i - p.i : rhi - p.i;
     return n < 64 ? n : 64;
   }
   __device__ __forceinline__ RowPos advance(RowPos p, int n) const {
     p.i += n;
-    if (p.i >= N) p = RowPos{p.seg + 1, 0};
+    if (p.i >= rhi) p = RowPos{p.seg + 1, rlo};
     return p;
   }
 
@@ -415,7 +417,8 @@ struct ColsK {
     const int seg = p.seg, i = p.i;
     const int b_ = shared ? seg / H : seg;
     const int h_ = shared ? seg % H : ho;
-    const float* dzs = dz + (int64_t)(b_ * H + h_) * N * Wp;
+    const float* dzs =
+        key_side ? dz + (int64_t)(b_ * H + h_) * N * Wp : dz + zq_off(g, b_ * H + h_, 0);
     int cb, ce, ws;
     window(group_of(p), cb, ce, ws);
     const int colb = u0 - ws;  // stored column of the block's first unfolded row
@@ -550,13 +553,17 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   const int dh = w >> 1;  // d half of this wave's tile
   const int d = 32 * dh + l32;
 
-  // this split's range of the flattened rows (segment-major)
+  // this split's range of the flattened rows (segment-major, rows [rlo, rhi)
+  // of each segment)
+  k.rlo = a.key_side ? 0 : g.z0;
+  k.rhi = a.key_side ? N : zq_last(g) + 1;
+  const int nr = k.rhi - k.rlo;
   const int nseg = a.shared ? a.B * a.H : a.B;
-  const int64_t nrows = (int64_t)nseg * N;
+  const int64_t nrows = (int64_t)nseg * nr;
   const int64_t per = (nrows + a.splits - 1) / a.splits;
   const int64_t f0 = (int64_t)sp * per;
   const int64_t f1 = f0 + per < nrows ? f0 + per : nrows;
-  k.end = RowPos{(int)(f1 / N), (int)(f1 % N)};
+  k.end = RowPos{(int)(f1 / nr), k.rlo + (int)(f1 % nr)};
   k.grp_on = grouped(g);
   if (a.key_side) cols_k(g, 0, k.cb0, k.ce0); else cols_q(g, 0, k.cb0, k.ce0);
   k.ws0 = 0;
@@ -564,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   f32x16 acc = zero16();
   float csum = 0.f;
   // live chunk n (rows [p.i, p.i + nrow) of segment p.seg) sits in buffer n & 1
-  RowPos p = k.next_live(RowPos{(int)(f0 / N), (int)(f0 % N)});
+  RowPos p = k.next_live(RowPos{(int)(f0 / nr), k.rlo + (int)(f0 % nr)});
   int nrow = before(p, k.end) ? k.chunk_rows(p) : 0;
   if (nrow > 0) k.template issue<WANT_X>(sZ0, sX0, sL0, p, nrow);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -669,8 +676,11 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
   const int rt = lid % gridDim.x, sp = (lid / gridDim.x) % gridDim.y, ho = lid / (gridDim.x * gridDim.y);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int u = 32 * rt + l32;  // unfolded row of this lane (operand A row)
+  // rows [rlo, rlo + nr) of each segment: every key, or the held query rows
+  const int rlo = a.key_side ? 0 : g.z0;
+  const int nr = (a.key_side ? N : zq_last(g) + 1) - rlo;
   const int nseg = a.shared ? a.B * a.H : a.B;
-  const int64_t nrows = (int64_t)nseg * N;
+  const int64_t nrows = (int64_t)nseg * nr;
   const int64_t per = (nrows + a.splits - 1) / a.splits;
   const int64_t f0 = (int64_t)sp * per;
   const int64_t f1 = f0 + per < nrows ? f0 + per : nrows;
@@ -682,11 +692,11 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
 
   int64_t f = f0;
   while (f < f1) {
-    const int seg = (int)(f / N);
-    const int i_start = (int)(f - (int64_t)seg * N);
+    const int seg = (int)(f / nr);
+    const int i_start = rlo + (int)(f - (int64_t)seg * nr);
     const int grp = grouped(g) ? i_start / kGroup : 0;
-    const int i_gend = grouped(g) ? imin(N, (grp + 1) * kGroup) : N;
-    const int64_t fend0 = (int64_t)seg * N + i_gend;
+    const int i_gend = grouped(g) ? imin(rlo + nr, (grp + 1) * kGroup) : rlo + nr;
+    const int64_t fend0 = (int64_t)seg * nr + (i_gend - rlo);
     const int64_t fend = fend0 < f1 ? fend0 : f1;
     int cb, ce, ws;
     if (a.key_side) {
@@ -701,11 +711,11 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
       const int b_ = a.shared ? seg / a.H : seg;
       const int h_ = a.shared ? seg % a.H : ho;
       const int bh = b_ * a.H + h_;
-      const float* dzb = a.dz + (int64_t)bh * N * g.Wp;
+      const float* dzb = a.key_side ? a.dz + (int64_t)bh * N * g.Wp : a.dz + zq_off(g, bh, 0);
       const T* xb = (const T*)a.x + b_ * a.sx.b + h_ * a.sx.h;
       const int col = u - ws;
       const bool colv = col >= cb && col < ce;
-      const int i_end = (int)(fend - (int64_t)seg * N);
+      const int i_end = rlo + (int)(fend - (int64_t)seg * nr);
       // each wave takes 16 consecutive rows (8 MFMA k-steps) per round, loads first
       for (int ib = i_start + 16 * w; ib < i_end; ib += 64) {
         float av[8], bv[8][2];
@@ -771,7 +781,8 @@ __device__ __forceinline__ float sum_splits(float s, const float* p, int64_t str
   return s;
 }
 
-// out[ho][k][d] = sum_{u in [ub[k], ue[k])} sum_s part[s][ho][u][d], u ascending.
+// out[ho][k][d] = sum_{u in [ub[k], ue[k])} sum_s part[s][ho][u][d], u ascending
+// (added to out when accumulate is set: one call per chunk of rows, in order).
 // Block (k4, ho): table rows k = 4 k4 .. 4 k4 + 3 of head ho, one thread per
 // (row, d); lane d = 0 also sums the bias column.  Fixed order: u ascending,
 // then the splits.
@@ -789,13 +800,15 @@ __global__ __launch_bounds__(256) void fold_kernel(FoldArgs a) {
     float s = 0.f;
     for (int u = b; u < e; ++u)
       s = sum_splits<BATCH>(s, p + (int64_t)u * 64, sstride * 64, a.splits);
-    a.out[((int64_t)ho * a.R + k) * 64 + d] = s;
+    float* o = a.out + ((int64_t)ho * a.R + k) * 64 + d;
+    *o = a.accumulate ? *o + s : s;
   }
   if (a.outb && d == 0) {
     const float* p = a.partb + (int64_t)ho * a.Rpad;
     float s = 0.f;
     for (int u = b; u < e; ++u) s = sum_splits<BATCH>(s, p + u, sstride, a.splits);
-    a.outb[(int64_t)ho * a.R + k] = s;
+    float* o = a.outb + (int64_t)ho * a.R + k;
+    *o = a.accumulate ? *o + s : s;
   }
 }
 

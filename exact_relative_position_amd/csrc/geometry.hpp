@@ -34,6 +34,11 @@ struct Geo {
   int W;       // projection window width (= R for a single group, else N + G - 1)
   int Wp;      // row stride of the Z / dZ buffers: W rounded up to 32 floats (128 B)
   int causal;  // 1 if j > i is masked
+  // The query-side buffers Z^Q and dZ^Q hold the query rows [z0, z0 + zr)
+  // of each (b, h), zr rows per (b, h): the whole sequence (z0 = 0, zr = N)
+  // unless the projection is computed one chunk of queries at a time.  The
+  // key-side buffers always hold every key row.
+  int zr, z0;
 };
 
 RP_HD int imin(int a, int b) { return a < b ? a : b; }
@@ -43,6 +48,14 @@ RP_HD int imax(int a, int b) { return a > b ? a : b; }
 RP_HD int rrow(const Geo& g, int o) { return imin(imax(o, g.lo), g.hi) - g.lo; }
 
 RP_HD bool grouped(const Geo& g) { return g.W < g.R; }
+
+// Float offset of query row i of (b, h) in the query-side Z / dZ buffers
+// (rows outside [z0, z0 + zr) are not held).
+RP_HD int64_t zq_off(const Geo& g, int64_t bh, int i) {
+  return (bh * g.zr + (i - g.z0)) * (int64_t)g.Wp;
+}
+// Last query row the query-side buffers hold (the clamp of rows beyond N).
+RP_HD int zq_last(const Geo& g) { return imin(g.N, g.z0 + g.zr) - 1; }
 
 // First unfolded row stored for query group `grp` (window [ws, ws + W)).
 RP_HD int win_q(const Geo& g, int grp) {
@@ -109,7 +122,8 @@ struct ProjArgs {
   Geo geo;
   int key_side;        // 0: query windows, 1: key windows
   int ncol_tiles;      // 64-column tiles per group launched
-  int ngroups;         // groups per (b, h)
+  int ngroups;         // groups per (b, h) launched
+  int g0;              // first group launched
 };
 
 // Attention kernels -----------------------------------------------------------
@@ -147,6 +161,15 @@ struct AttnArgs {
   // (drop probability t / 256) and 1 / (1 - p)
   uint32_t seed_lo, seed_hi, drop_off, drop_t;
   float drop_scale;
+  // Launch ranges: the forward and the query pass take the query blocks
+  // [qb0, qb0 + nqb) of every (b, h); the key pass takes the query tiles
+  // [qt0, qt1) (64 rows each).  The key pass accumulates across launches
+  // when kacc is set: bit 0 adds the fp32 sums in dk_acc / dv_acc ([B*H][N][64],
+  // dK carrying its tau) before writing, bit 1 writes those sums instead of
+  // the outputs.
+  int qb0, nqb, qt0, qt1, kacc;
+  float* dk_acc;
+  float* dv_acc;
 };
 
 struct RowTermArgs {     // padded backward row terms
@@ -163,15 +186,16 @@ struct RowTermArgs {     // padded backward row terms
   //  3:     -D (-D (1 - p) under attention dropout)
   float* kseed;
   float dseed_scale;     // multiplies -D in seed 3 (1 - p under dropout, else 1)
-  const float* zq;       // [B*H][N][W] or null
+  const float* zq;       // query-side Z buffer (rows of geo) or null
   Geo geo;
   float scale2;          // tau * log2(e)
   int B, H, N, Np;
+  int r0, r1;            // rows [r0, r1) of each (b, h) are prepared
 };
 
 struct RowsArgs {       // dX = part + dZ . table   (per row)
   const float* part;    // [B*H][N][64] fp32
-  const float* dz;      // [B*H][N][Wp]
+  const float* dz;      // [B*H][N][Wp] (query side: the rows of geo)
   const void* tunf;     // [Ho][Runf + 32][64] unfolded table: fp32 for fp32 inputs,
                         // else its bf16 high part
   const void* tunf_lo;  // bf16 low part (fp16 tables), or null
@@ -181,7 +205,8 @@ struct RowsArgs {       // dX = part + dZ . table   (per row)
   int B, H;
   Geo geo;
   int key_side;
-  int nblk;             // 128-row blocks per (b, h)
+  int nblk;             // 128-row blocks per (b, h) launched
+  int rb0;              // first 128-row block launched
 };
 
 struct TabUnfoldArgs {  // out[ho][u][:] = tab[ho][fold(u)][:], 32 zero rows after Runf
@@ -227,6 +252,7 @@ struct FoldArgs {       // out[ho][k][:] = sum_s sum_{u in fold range of k} part
   float* out;           // [Ho][R][64] or null
   float* outb;          // [Ho][R] or null
   int Ho, R, Rpad, splits;
+  int accumulate;       // 1: out += the sums (in call order), 0: out = the sums
 };
 
 struct BiasArgs {       // bunf[h][u] = b[h][fold[u]]

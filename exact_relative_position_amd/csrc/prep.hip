@@ -15,31 +15,34 @@
 
 namespace relpos {
 
-// 8 lanes per row; rows over B*H*Np.
+// 8 lanes per row; rows [r0, r1) of each of the B*H sequences (padded to Np).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rowterm_kernel(RowTermArgs a) {
   constexpr float kLog2e = 1.4426950408889634f;
-  const int64_t rows = (int64_t)a.B * a.H * a.Np;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
+  const int nr = a.r1 - a.r0;
+  const int64_t rows = (int64_t)a.B * a.H * a.Np;  // stride between the seed vectors
+  const int64_t todo = (int64_t)a.B * a.H * nr;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
   float acc = 0.f;
   int i = 0;
-  int64_t bh = 0;
-  if (row < rows) {
-    i = (int)(row % a.Np);
-    bh = row / a.Np;
+  int64_t bh = 0, row = 0;
+  if (t < todo) {
+    bh = t / nr;
+    i = a.r0 + (int)(t - bh * nr);
+    row = bh * a.Np + i;
     if (i < a.N) {
       const int b = (int)(bh / a.H), h = (int)(bh % a.H);
       const T* o = (const T*)a.o + b * a.so.b + h * a.so.h + (int64_t)i * a.so.n + 8 * part;
       const T* d = (const T*)a.dO + b * a.sdo.b + h * a.sdo.h + (int64_t)i * a.sdo.n + 8 * part;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc = fmaf(MT<T>::to_f(o[t]), MT<T>::to_f(d[t]), acc);
+      for (int u = 0; u < 8; ++u) acc = fmaf(MT<T>::to_f(o[u]), MT<T>::to_f(d[u]), acc);
     }
   }
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
-  if (row < rows && part == 0) {
+  if (t < todo && part == 0) {
     a.D[row] = acc;
     float l2 = INFINITY;
     if (i < a.N) {
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void rowterm_kernel(RowTermArgs a) {
     const float base = -(l2 / a.scale2);
     float zlo = 0.f, zhi = 0.f;
     if (a.zq) {
-      const float* zqb = a.zq + bh * (int64_t)a.N * a.geo.Wp;
+      const float* zqb = a.zq + zq_off(a.geo, bh, 0);
       const float* p0 = qside_sat_ptr(a.geo, zqb, i, 0);
       const float* p1 = qside_sat_ptr(a.geo, zqb, i, 1);
       if (p0) zlo = *p0;
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void rowterm_kernel(RowTermArgs a) {
 }
 
 hipError_t launch_rowterm(int dtype, const RowTermArgs& a, hipStream_t st) {
-  const int64_t rows = (int64_t)a.B * a.H * a.Np;
+  const int64_t rows = (int64_t)a.B * a.H * (a.r1 - a.r0);
   const int blocks = (int)((rows + kThreads / 8 - 1) / (kThreads / 8));
   if (blocks <= 0) return hipSuccess;
   switch (dtype) {

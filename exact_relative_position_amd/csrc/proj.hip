@@ -78,7 +78,7 @@ __global__ void bias_unfold_kernel(BiasArgs a) {
 }
 
 // Z[bh][i][c] = x_i . tab[fold(ws + c)] (+ bias[fold(ws + c)]) for c in the
-// group's live columns [cb, ce).  Block: 128 rows x proj_cols() columns (256
+// group's live columns [cb, ce), for the groups [g0, g0 + ngroups).  Block: 128 rows x proj_cols() columns (256
 // for windows of 2048 columns and more, else 128); wave w
 // owns rows 32w..32w+31, keeps their X fragments in registers and walks the
 // block's 32-column MFMA tiles, loading the next tile's table fragments
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   const int lid = xcd_remap(blockIdx.x, total);
   const int bh = lid / per_bh;
   const int rem = lid - bh * per_bh;
-  const int grp = rem / nch, ch = rem - grp * nch;
+  const int grp = a.g0 + rem / nch, ch = rem - (rem / nch) * nch;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   int cb, ce, ws;
   if (a.key_side) {
@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   for (int ks = 0; ks < NSD; ++ks) xf[ks] = i < N ? frag_g<T>(xrow, KS * ks + E * hl) : M::zero();
 
   const T* tab = (const T*)a.tab + hh * a.tab_hs;
-  float* zb = a.z + (int64_t)bh * N * g.Wp;
+  // rows addressed by token: every key row (key side), the held query rows
+  float* zb = a.key_side ? a.z + (int64_t)bh * N * g.Wp : a.z + zq_off(g, bh, 0);
   // table fragments (operand B: lane's column) and bias of tile n
   auto load_tile = [&](int n, frag (&tf)[NSD], float& badd, bool& cv, int& col) {
     col = c0 + 32 * n + l32;

@@ -42,7 +42,7 @@ struct QCtx {
   int sig;               // sigma(l % 32)
   int kv_end;            // keys >= kv_end are masked
   int wsq;               // first unfolded row of this group's Z^Q window
-  const float* zq_row;   // Z^Q row of min(iq, N - 1) (when has_zq)
+  const float* zq_row;   // Z^Q row of min(iq, last row held) (when has_zq)
   const float* zkb;      // Z^K of this (b, h)
   const float* bun;      // unfolded b of this head
   bool has_zq, has_zk, has_b;
@@ -172,14 +172,16 @@ struct RowStage {
   static constexpr int kPitch = 68;             // floats per row pair
   static constexpr int kFloats = 16 * kPitch;   // one wave, one subtile
   float* buf[2];     // this wave's buffers of subtile 0 / 1
-  const float* z;    // Z of this (b, h), row stride Wp
+  const float* z;    // Z of this (b, h), row stride Wp, addressed by query row
   int dc;            // column step per row
   int lane_off;      // (lane & 31) + (lane >> 5) * (Wp + dc)
+  int rlast;         // last row the buffer holds (rows beyond are clamped to it)
 
   __device__ __forceinline__ void init(const Geo& g, const float* z_bh, int dc_, int lane) {
     z = z_bh;
     dc = dc_;
     lane_off = (lane & 31) + (lane >> 5) * (g.Wp + dc);
+    rlast = zq_last(g);
   }
   // staged row m, position 0 (row pairs at kPitch, odd rows 32 floats in)
   __device__ __forceinline__ const float* row(int st, int m) const {
@@ -190,12 +192,13 @@ struct RowStage {
   // clamped into [0, W - 1] exactly as the per-score lookup clamps them: for
   // a saturated entry of a band tile the clamp is the truncation of the map
   // (first / last row); rows beyond N read row N - 1 (their results are
-  // discarded).  A subtile that needs no clamp takes the fast path.
+  // discarded; rows beyond the buffer's last row read that row).  A subtile
+  // that needs no clamp takes the fast path.
   template <int ST>
   __device__ __forceinline__ void issue(const Geo& g, int row0, int c0, int lane) const {
     float* dst = buf[ST];
     const int cmin = c0 + (dc < 0 ? 31 * dc : 0), cmax = c0 + 31 + (dc > 0 ? 31 * dc : 0);
-    if (row0 + 31 < g.N && cmin >= 0 && cmax < g.W) {
+    if (row0 + 31 <= rlast && cmin >= 0 && cmax < g.W) {
       // wave-uniform row-pair address plus a fixed 32-bit lane offset
       const char* base = reinterpret_cast<const char*>(z + (int64_t)row0 * g.Wp + c0);
       const int64_t step = (int64_t)8 * (g.Wp + dc);  // bytes between row pairs
@@ -212,7 +215,7 @@ struct RowStage {
 #pragma unroll 1
       for (int p = 0; p < 16; ++p) {
         const int m = 2 * p + h;
-        const int r = imin(row0 + m, g.N - 1);
+        const int r = imin(row0 + m, rlast);
         const int col = imin(imax(c0 + dc * m + k, 0), g.W - 1);
         __builtin_amdgcn_global_load_lds((glb_void_t*)(z + (int64_t)r * g.Wp + col),
                                          (lds_void_t*)(dst + p * kPitch), 4, 0, 0);
@@ -262,10 +265,11 @@ __device__ __forceinline__ const float* kside_sat_ptr(const Geo& g, const float*
   if (col < cb || col >= ce) return nullptr;
   return zkb + (int64_t)j * g.Wp + col;
 }
-// Same for the query side: Z^Q[i, first / last row] of query i.
+// Same for the query side: Z^Q[i, first / last row] of query i (zqb
+// addressed by query row; null for a row the buffer does not hold).
 __device__ __forceinline__ const float* qside_sat_ptr(const Geo& g, const float* zqb, int i,
                                                       int side) {
-  if (i >= g.N) return nullptr;
+  if (i >= g.N || i < g.z0 || i > zq_last(g)) return nullptr;
   const int grp = i / kGroup;
   const int wq = win_q(g, grp);
   int cb, ce;

@@ -125,7 +125,24 @@ enum {
  *    their head strides are given in elements and may be 0 (one table shared
  *    by all heads; its gradient is then summed over heads).
  *  - tau > 0 (the softmax scale of Eq. (1)).
- *  - d must be 64 (ERR_UNSUPPORTED otherwise); any N >= 0 (N = 0 is a no-op). */
+ *  - d must be 64 (ERR_UNSUPPORTED otherwise); any N >= 0 (N = 0 is a no-op).
+ *  - zchunk (a multiple of 128, or 0): linear-memory mode for wide relation
+ *    windows (the identity map's is N + 127 columns per query).  When
+ *    0 < zchunk < N the query-side projection Z^Q and its gradient dZ^Q are
+ *    never held for the whole sequence: the forward and the backward each
+ *    recompute them one chunk of zchunk queries at a time inside the
+ *    workspace (the digest's section on limitations: recomputing the
+ *    projection instead of storing it makes the memory linear), so the
+ *    workspace is O(B H zchunk W) plus O(B H N d) for the chunk-summed dK
+ *    and dV, and nothing is kept between the passes (zsave must be NULL,
+ *    relpos_attn_zsave_size returns 0).  The key-side term must be absent
+ *    (ERR_UNSUPPORTED).  Under this mode the stage calls run whole chunks:
+ *    FWD_PROJECT and BWD_PREPARE only build the map tables, FWD_ATTEND runs
+ *    every chunk's projection and attention, BWD_QUERY_PASS | BWD_KEY_PASS
+ *    (both together) every chunk's row terms, passes and contraction, and
+ *    BWD_CONTRACT alone does nothing.  Each chunk's results are summed into
+ *    dK, dV, daQ and db in chunk order, so the outputs are deterministic;
+ *    they may differ from the unchunked ones in the last bits. */
 typedef struct relpos_problem {
   int64_t B, H, N, d;
   int32_t dtype;            /* relpos_dtype */
@@ -137,6 +154,7 @@ typedef struct relpos_problem {
   float dropout_p;          /* in [0, 1); 0 = no dropout */
   uint32_t dropout_offset;  /* counter word 3 of the generator */
   uint64_t dropout_seed;    /* generator key */
+  int64_t zchunk;           /* query rows per projection chunk; 0 = whole sequence */
 } relpos_problem;
 
 /* Which relation terms are present (a "= 0" table is simply absent). */

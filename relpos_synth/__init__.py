@@ -54,6 +54,9 @@ class Workload:
     # attention dropout: (t, generator seed, generator offset), drop
     # probability t / 256; None = no dropout
     dropout: Optional[tuple] = None
+    # query rows per chunk of the query-side projection (0: the whole
+    # sequence); a run setting, not an input
+    zchunk: int = 0
 
     def with_(self, **kw):
         return dataclasses.replace(self, **kw)
@@ -138,8 +141,14 @@ def sweep_workloads():
 MEMORY_NS = (1024, 2048, 4096, 8192, 16384)
 
 
-def memory_scaling_workloads():
-    """Name -> Workload of the Shaw workload at each N of MEMORY_NS."""
+def memory_scaling_workloads(mechanism="shaw"):
+    """Name -> Workload at each N of MEMORY_NS: the Shaw workload (1 x 12 x N,
+    fp16), or the Transformer-XL identity map at the same shape (fp16,
+    causal, aQ + b) with its projection computed 1024 queries at a time."""
+    if mechanism == "txl":
+        base = WORKLOADS["txl_n8192_f16"].with_(zchunk=1024)
+        return {f"txl_n{N}_f16_chunk1024": base.with_(name=f"txl_n{N}_f16_chunk1024", N=N)
+                for N in MEMORY_NS}
     base = WORKLOADS["shaw_n8192_f16"]
     return {f"shaw_n{N}_f16": base.with_(name=f"shaw_n{N}_f16", N=N) for N in MEMORY_NS}
 

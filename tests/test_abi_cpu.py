@@ -196,7 +196,8 @@ def test_problem_struct_layout():
     assert b.Problem.dropout_p.offset == b.Problem.b_head_stride.offset + 8
     assert b.Problem.dropout_offset.offset == b.Problem.dropout_p.offset + 4
     assert b.Problem.dropout_seed.offset == b.Problem.dropout_offset.offset + 4
-    assert ctypes.sizeof(b.Problem) == b.Problem.dropout_seed.offset + 8
+    assert b.Problem.zchunk.offset == b.Problem.dropout_seed.offset + 8
+    assert ctypes.sizeof(b.Problem) == b.Problem.zchunk.offset + 8
 
 
 @pytest.mark.parametrize("phi", [
@@ -415,3 +416,50 @@ def test_noalloc_forward_validates_before_touching_the_device(L):
     assert L.relpos_attn_workspace_size(ctypes.byref(big), ctypes.byref(phi), ctypes.byref(m), 1,
                                         0, 0, ctypes.byref(ws)) == 0
     assert ws.value > b.NOALLOC_SCRATCH_BYTES
+
+
+# Chunked query-side projection (zchunk): validation and the memory model.
+
+@pytest.mark.parametrize("zchunk,terms,code", [
+    (100, 1, -1), (-128, 1, -1), (128, 3, -2),   # aK cannot be chunked
+    (128, 1, 0), (128, 5, 0), (4096, 3, 0),       # zchunk >= N: no chunking, aK fine
+])
+def test_zchunk_validation(L, zchunk, terms, code):
+    p = _prob(N=1000)
+    p.zchunk = zchunk
+    phi = b.phi_struct({"kind": "identity"})
+    assert _ws(L, p, phi, terms=terms, pass_=1)[0] == code
+
+
+def test_chunked_projection_is_never_kept(L):
+    p = _prob(N=1000)
+    p.zchunk = 256
+    phi = b.phi_struct({"kind": "identity"})
+    n = ctypes.c_size_t()
+    assert L.relpos_attn_zsave_size(ctypes.byref(p), ctypes.byref(phi), 1, ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_chunked_identity_workspace_is_linear_in_n(L):
+    """With the identity map the projection window is N + 127 columns per
+    query: unchunked, the backward workspace grows about 4x per doubling of
+    N; with 1024-query chunks about 2x (the chunk's Z^Q and dZ^Q grow with
+    the window only, the rest with N)."""
+    phi = b.phi_struct({"kind": "identity"})
+    sizes = {0: [], 1024: []}
+    for zc in sizes:
+        for N in (2048, 4096, 8192, 16384):
+            p = _prob(H=12, N=N)
+            p.zchunk = zc
+            st, n = _ws(L, p, phi, terms=5, pass_=1)
+            assert st == 0
+            sizes[zc].append(n)
+    for a, c in zip(sizes[0], sizes[0][1:]):
+        assert 3.5 < c / a < 4.5
+    for a, c in zip(sizes[1024], sizes[1024][1:]):
+        assert 1.8 < c / a < 2.2
+    # forward: only the chunk's Z^Q
+    p = _prob(H=12, N=16384)
+    p.zchunk = 1024
+    st, n = _ws(L, p, phi, terms=5, pass_=0)
+    assert st == 0 and n < 12 * 1024 * (16384 + 128) * 4 + (1 << 20)
