@@ -41,6 +41,20 @@ FLAGS = [
 ]
 
 
+# Sources compiled without the VGPR-form option: with it, the fp32 backward
+# kernels make this compiler crash (in its pass that rewrites AGPR copies of
+# MFMA results); they keep the default AGPR accumulators, which changes
+# register use only, not results.
+AGPR_FORM = {"attn_bwd_f32.hip"}
+
+
+def flags_for(src):
+    if src in AGPR_FORM:
+        i = FLAGS.index("-amdgpu-mfma-vgpr-form")
+        return FLAGS[:i - 1] + FLAGS[i + 1:]
+    return FLAGS
+
+
 def hipcc():
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -50,7 +64,7 @@ def hipcc():
 
 def _compile(src):
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(SRC, src), "-o", out]
+    cmd = [hipcc(), *flags_for(src), "-c", os.path.join(SRC, src), "-o", out]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)

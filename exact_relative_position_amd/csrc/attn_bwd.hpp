@@ -66,9 +66,9 @@ __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, 
     if (!key) bid -= kblocks;
   }
   if (key)
-    bwd_k_block<T, ZQ, SK, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0);
+    bwd_k_block<T, ZQ, ZK, SK, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0);
   else
-    bwd_q_block<T, ZK, SQ, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0, st1);
+    bwd_q_block<T, ZQ, ZK, SQ, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0, st1);
 }
 
 template <typename T, bool GRP, bool DROP, bool ZQ, bool ZK, bool SQ, bool SK>

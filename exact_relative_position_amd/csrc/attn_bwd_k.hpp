@@ -192,6 +192,27 @@ struct BwdK {
     }
   }
 
+  // Whether every entry of the 32 x 32 subtile (this wave's keys, queries
+  // [qb, qb + 32)) is live and strictly inside the band (wave-uniform).
+  __device__ __forceinline__ bool band_interior(int qb) const {
+    return jw0 - qb - 31 > g.lo && jw0 + 31 - qb < g.hi && qb + 31 < N &&
+           jw0 + 31 < imin(N, kv_end) && !(g.causal && jw0 + 31 > qb);
+  }
+
+  // Band stores of an interior subtile (16-bit operands): a lane's elements
+  // e = 0..7 and 8..15 are eight consecutive queries each (kappa), hence
+  // eight consecutive offsets of its key's dZ^K row in descending order,
+  // written as four 16-byte stores.
+  __device__ __forceinline__ void band_store_row(const float (&ds)[16], int qb) {
+    float* p = dz_row + (jk - qb - E * hl - g.lo - wsk);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e0 = 4 * u;
+      store_f32x4_a4(p - (u < 2 ? 4 * u + 3 : 16 + 4 * (u - 2) + 3),
+                     f32x4{tau * ds[e0 + 3], tau * ds[e0 + 2], tau * ds[e0 + 1], tau * ds[e0]});
+    }
+  }
+
   // One 64-query tile from LDS buffer BUF.  BAND: the wave's tile crosses
   // the band or holds masked entries (each wave refines the kind for its
   // own keys); otherwise the whole tile is saturated on side `sat`.
@@ -278,6 +299,8 @@ struct BwdK {
 #pragma unroll
           for (int e = 0; e < 16; ++e) tsum += ds[e];
           if (kind == KIND_LO) acc_lo += tsum; else acc_hi += tsum;
+        } else if (kHalf && band_interior(qt0 + 32 * st)) {
+          band_store_row(ds, qt0 + 32 * st);
         } else {
           // saturated entries of a band tile go to the two accumulators
           // (masked entries have ds = 0); interior live entries are stored
@@ -346,13 +369,15 @@ struct BwdK {
   }
 };
 
-// ZQ: whether the query-side relation term is present (compile-time switch);
-// STAGE: band dZ^K stores staged through LDS; GRP: grouped workgroup.
+// ZQ / ZK: whether the query-side / key-side relation term is present
+// (compile-time switches: code for an absent term is not generated, which
+// keeps its registers out of the allocation); STAGE: band dZ^K stores staged
+// through LDS; GRP: grouped workgroup.
 // One key block of the pass: block number bid of a launch over B*H*nblk
 // blocks.  LDS (sizes for G = key_groups groups): sQ0..sO1 G*DTile bytes
 // each, sR0/sR1 G*4*kTile floats, sSt (STAGE only) 4*G*32*kStagePitchK
 // floats.
-template <typename T, bool ZQ, bool STAGE, bool GRP, bool DROP>
+template <typename T, bool ZQ, bool ZK, bool STAGE, bool GRP, bool DROP>
 __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ0, char* sQ1,
                                             char* sO0, char* sO1, float* sR0, float* sR1,
                                             float* sSt) {
@@ -392,7 +417,7 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
   k.jk = jk;
   k.sig = sigma<T>(l32);
   k.has_zq = ZQ;
-  k.has_zk = a.flags & F_ZK;
+  k.has_zk = ZK && (a.flags & F_ZK);
   k.has_b = a.flags & F_B;
 
   int kv_end = N;

@@ -145,6 +145,27 @@ struct BwdQ {
     }
   }
 
+  // Whether every entry of the 32 x 32 subtile (this wave's queries, keys
+  // [jb, jb + 32)) is live and strictly inside the band (wave-uniform).
+  __device__ __forceinline__ bool band_interior(int jb) const {
+    return jb - iw0 - 31 > g.lo && jb + 31 - iw0 < g.hi && iw0 + 31 < N && jb + 31 < c.kv_end &&
+           !(g.causal && jb + 31 > iw0);
+  }
+
+  // Band stores of an interior subtile (16-bit operands): a lane's elements
+  // e = 0..7 and 8..15 are eight consecutive keys each (kappa), hence eight
+  // consecutive offsets of its query's dZ^Q row, written as four 16-byte
+  // stores.
+  __device__ __forceinline__ void band_store_row(const float (&ds)[16], int jb) {
+    float* p = dz_row + (jb + E * hl - c.iq - g.lo - c.wsq);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e0 = 4 * u;
+      store_f32x4_a4(p + (u < 2 ? 4 * u : 16 + 4 * (u - 2)),
+                     f32x4{tau * ds[e0], tau * ds[e0 + 1], tau * ds[e0 + 2], tau * ds[e0 + 3]});
+    }
+  }
+
   // One 64-key tile from LDS buffer BUF; BAND: the wave's tile crosses the
   // band, otherwise it is saturated on side `sat`.
   // stage_next: the Z^Q rows of tile t + 1 are staged from this tile's band
@@ -202,6 +223,8 @@ struct BwdQ {
 #pragma unroll
           for (int e = 0; e < 16; ++e) tsum += ds[e];
           if (kind == KIND_LO) acc_lo += tsum; else acc_hi += tsum;
+        } else if (kHalf && band_interior(j0 + 32 * st)) {
+          band_store_row(ds, j0 + 32 * st);
         } else {
           // saturated entries go to the two per-query accumulators (masked
           // entries have ds = 0).  With a wide band (most tiles inside it)
@@ -292,13 +315,15 @@ struct BwdQ {
   }
 };
 
-// ZK: whether the key-side relation term is present (compile-time switch);
-// STAGE: band stores staged through LDS; GRP: grouped workgroup.
+// ZQ / ZK: whether the query-side / key-side relation term is present
+// (compile-time switches: code for an absent term is not generated, which
+// keeps its registers out of the allocation); STAGE: band stores staged
+// through LDS; GRP: grouped workgroup.
 // One query block of the pass: block number bid of a launch over
 // B*H*nblk blocks.  LDS (sizes for G = query_groups groups): sK0..sV1
 // G*DTile bytes each, sZK0/sZK1 G*2*kTile floats, sSt0/sSt1 (STAGE only)
 // 4*G*kStageFloats floats.
-template <typename T, bool ZK, bool STAGE, bool GRP, bool DROP>
+template <typename T, bool ZQ, bool ZK, bool STAGE, bool GRP, bool DROP>
 __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK0, char* sK1,
                                             char* sV0, char* sV1, float* sZK0, float* sZK1,
                                             float* sSt0, float* sSt1) {
@@ -367,7 +392,7 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
   c.hl = hl;
   c.sig = sigma<T>(l32);
   c.kv_end = kv_end;
-  c.has_zq = a.flags & F_ZQ;
+  c.has_zq = ZQ && (a.flags & F_ZQ);
   c.has_zk = ZK;
   c.has_b = a.flags & F_B;
   c.wsq = win_q(g, qb);

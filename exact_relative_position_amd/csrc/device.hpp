@@ -176,6 +176,14 @@ __device__ inline float sum_xor32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 16-byte store to an address that is only 4-byte aligned (global memory
+// accepts unaligned vector accesses; the type's alignment tells the compiler
+// so, which keeps it one dwordx4 store).
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ void store_f32x4_a4(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4_a4*>(p) = v;
+}
+
 // s_waitcnt immediate for "vmcnt(0)" with the other counters left alone
 // (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
 constexpr int kWaitVmcnt0 = 0x0F70;
