@@ -376,7 +376,14 @@ def main():
     import exact_relative_position_amd._binding as B_
     from relpos_synth import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
+    if args.workload in WORKLOADS:
+        w = WORKLOADS[args.workload]
+    else:
+        from relpos_synth import sweep_workloads
+        sweep = sweep_workloads()
+        if args.workload not in sweep:
+            sys.exit(f"unknown workload {args.workload!r}")
+        w = sweep[args.workload]
     if args.zchunk:
         w = w.with_(name=f"{w.name}_chunk{args.zchunk}", zchunk=args.zchunk)
     t_drop = int(round(args.dropout * 256))

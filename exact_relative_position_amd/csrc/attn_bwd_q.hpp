@@ -166,6 +166,28 @@ struct BwdQ {
     }
   }
 
+  // Band stores of an interior subtile through the LDS area `stage`
+  // (registers -> [query][key] as in band_store); then each lane takes four
+  // consecutive keys of one query row, so that eight lanes write one 128-byte
+  // run and one store instruction covers eight rows.
+  __device__ __forceinline__ void band_store_runs(const float (&ds)[16], int jb, float* stage) {
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int k0 = kappa<T>(hl, 4 * e4);
+      *reinterpret_cast<f32x4*>(stage + l32 * kStagePitch + k0) = f32x4{
+          tau * ds[4 * e4], tau * ds[4 * e4 + 1], tau * ds[4 * e4 + 2], tau * ds[4 * e4 + 3]};
+    }
+    const int qr = lane >> 3, kc = 4 * (lane & 7);
+    // row iw0 + q, key jb + kc: offset jb + kc - iw0 - q
+    float* base = dz_w + (jb + kc - iw0 - g.lo - c.wsq);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = 8 * r + qr;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + q * kStagePitch + kc);
+      store_f32x4_a4(base + (int64_t)q * (g.Wp - 1), v);
+    }
+  }
+
   // One 64-key tile from LDS buffer BUF; BAND: the wave's tile crosses the
   // band, otherwise it is saturated on side `sat`.
   // stage_next: the Z^Q rows of tile t + 1 are staged from this tile's band
@@ -224,7 +246,8 @@ struct BwdQ {
           for (int e = 0; e < 16; ++e) tsum += ds[e];
           if (kind == KIND_LO) acc_lo += tsum; else acc_hi += tsum;
         } else if (kHalf && band_interior(j0 + 32 * st)) {
-          band_store_row(ds, j0 + 32 * st);
+          if constexpr (STAGE) band_store_runs(ds, j0 + 32 * st, zs.buf[st]);
+          else band_store_row(ds, j0 + 32 * st);
         } else {
           // saturated entries go to the two per-query accumulators (masked
           // entries have ds = 0).  With a wide band (most tiles inside it)
