@@ -78,15 +78,27 @@ __global__ void bias_unfold_kernel(BiasArgs a) {
 }
 
 // Z[bh][i][c] = x_i . tab[fold(ws + c)] (+ bias[fold(ws + c)]) for c in the
-// group's live columns [cb, ce), for the groups [g0, g0 + ngroups).  Block: 128 rows x proj_cols() columns (256
-// for windows of 2048 columns and more, else 128); wave w
-// owns rows 32w..32w+31, keeps their X fragments in registers and walks the
-// block's 32-column MFMA tiles, loading the next tile's table fragments
-// before it computes and stores the current one, so that the loads overlap
-// the stores (each store instruction writes 128-byte runs of two rows).
+// group's live columns [cb, ce), for the groups [g0, g0 + ngroups).  Block:
+// 128 rows x proj_cols() columns (256 for windows of 2048 columns and more,
+// else 128); wave w owns rows 32w..32w+31, keeps their X fragments in
+// registers and walks the block's 32-column MFMA tiles, loading the next
+// tile's table fragments before it computes and stores the current one, so
+// that the loads overlap the stores (each store instruction writes 128-byte
+// runs of two rows).
+//
+// Every iteration issues the same memory instructions whatever its lanes
+// hold: lanes past the window's end load table row 0, and the stores are
+// buffer stores whose out-of-range lanes (rows beyond N, columns beyond the
+// window) carry an offset past the buffer's end, which the hardware drops.
+// With fixed counts the compiler's wait for the prefetched fragments leaves
+// the previous tile's stores in flight.  (Conditional loads or stores would
+// make it wait for every outstanding access.)  BUF: the (b, h) slab of Z is
+// below 2 GiB, as 32-bit buffer offsets need; otherwise plain stores.
 __host__ __device__ inline int proj_cols(const ProjArgs& a) { return a.ncol_tiles >= 32 ? 256 : 128; }
 
-template <typename T>
+// FOLD: bucketed map (table rows through the fold table); BIAS: b is folded
+// into the projection.
+template <typename T, bool FOLD, bool BIAS, bool BUF>
 __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
   using M = MT<T>;
   using frag = typename M::frag;
@@ -121,48 +133,93 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs a) {
 #pragma unroll
   for (int ks = 0; ks < NSD; ++ks) xf[ks] = i < N ? frag_g<T>(xrow, KS * ks + E * hl) : M::zero();
 
+  // the fold rows of the block's columns, looked up once (a lookup inside
+  // the loop would be a dependent global load)
+  __shared__ int sfold[FOLD ? 256 : 1];
+  if constexpr (FOLD) {
+    for (int c = tid; c < pc; c += kThreads) {
+      const int cc = c0 + c;
+      sfold[c] = cc < ce ? a.fold[ws + cc] : 0;
+    }
+    __syncthreads();
+  }
+
   const T* tab = (const T*)a.tab + hh * a.tab_hs;
+  const T* bias = BIAS ? (const T*)a.bias + hh * a.bias_hs : nullptr;
   // rows addressed by token: every key row (key side), the held query rows
-  float* zb = a.key_side ? a.z + (int64_t)bh * N * g.Wp : a.z + zq_off(g, bh, 0);
-  // table fragments (operand B: lane's column) and bias of tile n
-  auto load_tile = [&](int n, frag (&tf)[NSD], float& badd, bool& cv, int& col) {
+  // [first, first + nrows)
+  const int first = a.key_side ? 0 : g.z0;
+  const int nrows = a.key_side ? N : zq_last(g) + 1 - g.z0;
+  float* zb = a.key_side ? a.z + (int64_t)bh * N * g.Wp : a.z + zq_off(g, bh, g.z0);
+  const int row0 = grp * kBlockRows + 32 * w - first;  // this wave's first row in the slab
+  const int rlim = imin(N - first, nrows);             // rows of the slab that exist
+  __amdgpu_buffer_rsrc_t zr;
+  if constexpr (BUF) zr = __builtin_amdgcn_make_buffer_rsrc(zb, 0, nrows * g.Wp * 4, 0x00020000);
+
+  // table fragments (operand B: the lane's column) and bias of tile n; the
+  // bias stays in the input type until it is used
+  auto load_tile = [&](int n, frag (&tf)[NSD], T& braw, int& col) {
     col = c0 + 32 * n + l32;
-    cv = col < ce;
-    const int u = ws + col;
-    const int r = cv ? (a.fold ? a.fold[u] : u) : 0;
+    // (n < nsub keeps the fold lookup inside the block's own columns: the
+    // window can go on beyond them, into the next block's chunk)
+    const bool cv = n < nsub && col < ce;
+    const int r = cv ? (FOLD ? sfold[col - c0] : ws + col) : 0;
     const T* trow = tab + (int64_t)r * kHeadDim;
 #pragma unroll
-    for (int ks = 0; ks < NSD; ++ks) tf[ks] = cv ? frag_g<T>(trow, KS * ks + E * hl) : M::zero();
-    badd = (a.bias && cv) ? MT<T>::to_f(((const T*)a.bias)[hh * a.bias_hs + r]) : 0.f;
+    for (int ks = 0; ks < NSD; ++ks) tf[ks] = frag_g<T>(trow, KS * ks + E * hl);
+    if constexpr (BIAS) braw = bias[r];
   };
   frag tf[NSD];
-  float badd;
-  bool cv;
+  T braw = MT<T>::from_f(0.f);
   int col;
-  load_tile(0, tf, badd, cv, col);
+  load_tile(0, tf, braw, col);
 #pragma unroll 1
   for (int n = 0; n < nsub; ++n) {
+    // (past the last tile this loads row 0 again: a fixed count per iteration)
     frag tn[NSD];
-    float bn = 0.f;
-    bool cvn = false;
-    int coln = 0;
-    if (n + 1 < nsub) load_tile(n + 1, tn, bn, cvn, coln);
+    T bn = MT<T>::from_f(0.f);
+    int coln;
+    load_tile(n + 1, tn, bn, coln);
     f32x16 acc = zero16();
 #pragma unroll
     for (int ks = 0; ks < NSD; ++ks) acc = M::mma(xf[ks], tf[ks], acc);
-    if (cv) {
+    const float badd = BIAS ? MT<T>::to_f(braw) : 0.f;
+    if constexpr (BUF) {
+      const bool cv = col < ce;  // (n < nsub here)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = row0 + res_row(hl, e);
+        const uint32_t off = (cv && row < rlim) ? (uint32_t)(row * g.Wp + col) * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[e] + badd), zr, off, 0, 0);
+      }
+    } else if (col < ce) {
       float* zc = zb + col;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = grp * kBlockRows + 32 * w + res_row(hl, e);
-        if (row < N) zc[(int64_t)row * g.Wp] = acc[e] + badd;
+        const int row = row0 + res_row(hl, e);
+        if (row < rlim) zc[(int64_t)row * g.Wp] = acc[e] + badd;
       }
     }
 #pragma unroll
     for (int ks = 0; ks < NSD; ++ks) tf[ks] = tn[ks];
-    badd = bn;
-    cv = cvn;
+    braw = bn;
     col = coln;
+  }
+}
+
+template <typename T, bool FOLD, bool BIAS>
+static void launch_proj_b(const ProjArgs& a, int total, bool buf, hipStream_t st) {
+  if (buf) hipLaunchKernelGGL((proj_kernel<T, FOLD, BIAS, true>), dim3(total), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((proj_kernel<T, FOLD, BIAS, false>), dim3(total), dim3(kThreads), 0, st, a);
+}
+template <typename T>
+static void launch_proj_t(const ProjArgs& a, int total, bool buf, hipStream_t st) {
+  if (a.fold) {
+    if (a.bias) launch_proj_b<T, true, true>(a, total, buf, st);
+    else launch_proj_b<T, true, false>(a, total, buf, st);
+  } else {
+    if (a.bias) launch_proj_b<T, false, true>(a, total, buf, st);
+    else launch_proj_b<T, false, false>(a, total, buf, st);
   }
 }
 
@@ -202,10 +259,13 @@ hipError_t launch_proj(int dtype, const ProjArgs& a, hipStream_t st) {
   const int nch = (a.ncol_tiles + pc / 64 - 1) / (pc / 64);
   const int total = a.B * a.H * a.ngroups * nch;
   if (total <= 0) return hipSuccess;
+  // the (b, h) slab of Z must be below 2 GiB for 32-bit buffer offsets
+  const int64_t slab_rows = a.key_side ? a.geo.N : a.geo.zr;
+  const bool buf = slab_rows * a.geo.Wp * 4 < ((int64_t)1 << 31);
   switch (dtype) {
-    case 0: hipLaunchKernelGGL(proj_kernel<float>, dim3(total), dim3(kThreads), 0, st, a); break;
-    case 1: hipLaunchKernelGGL(proj_kernel<_Float16>, dim3(total), dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL(proj_kernel<__bf16>, dim3(total), dim3(kThreads), 0, st, a); break;
+    case 0: launch_proj_t<float>(a, total, buf, st); break;
+    case 1: launch_proj_t<_Float16>(a, total, buf, st); break;
+    default: launch_proj_t<__bf16>(a, total, buf, st); break;
   }
   return hipGetLastError();
 }
