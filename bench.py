@@ -184,7 +184,7 @@ def measured_traffic(kernel, workload):
     rocprofv3 counter summary, or None when there is none or the kernel's
     source has changed since the counters were taken."""
     try:
-        with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")) as fh:
+        with open(os.path.join(ROOT, "profiles", f"counters_{workload}.md")) as fh:
             lines = fh.read().splitlines()
     except OSError:
         return None
