@@ -154,9 +154,12 @@ struct BwdK {
         v[e] += zk_row[imin(imax(jk - ib - kap0<T>(e) - g.lo - wsk, 0), Wm)];
     }
     if (has_b) {
+      // (all loads first, then the sums, so that they are in flight together)
+      float bv[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        v[e] += bun[imin(imax(jk - ib - kap0<T>(e) - g.lo, 0), g.R - 1)];
+      for (int e = 0; e < 16; ++e) bv[e] = bun[imin(imax(jk - ib - kap0<T>(e) - g.lo, 0), g.R - 1)];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] += bv[e];
     }
   }
 

@@ -81,6 +81,12 @@ __device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, i
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[e] = c.zq_row[imin(imax(base + kap0<T>(e), 0), Wm)];
     }
+  } else if (c.has_b) {
+    // b is looked up here only without a query-side table (with one it is
+    // folded into Z^Q): the loads go straight into v, all in flight at once
+    const int base = jb - c.iq - g.lo;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = c.bun[imin(imax(base + kap0<T>(e), 0), g.R - 1)];
   }
   if (c.has_zk) {
 #pragma unroll
@@ -89,11 +95,6 @@ __device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, i
       const int col = imin(imax(j - c.iq - g.lo - wk, 0), Wm);
       v[e] += c.zkb[(int64_t)j * g.Wp + col];
     }
-  }
-  if (c.has_b) {
-    const int base = jb - c.iq - g.lo;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] += c.bun[imin(imax(base + kap0<T>(e), 0), g.R - 1)];
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) s[e] = v[e];
