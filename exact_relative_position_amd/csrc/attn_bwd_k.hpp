@@ -242,6 +242,9 @@ struct BwdK {
     const float off = kind == KIND_LO ? off_lo : (kind == KIND_HI ? off_hi : 0.f);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
+      // scheduling strategy 0 of the compiler (interleave the LDS operand
+      // reads with the MFMAs): -1% to -2% on the passes, measured
+      __builtin_amdgcn_iglp_opt(0);
       f32x16 s;
       {
         float v[16];

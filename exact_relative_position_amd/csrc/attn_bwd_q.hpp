@@ -207,6 +207,9 @@ struct BwdQ {
     const float off = cst * sc2 - lse2;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
+      // scheduling strategy 0 of the compiler (interleave the LDS operand
+      // reads with the MFMAs), as in the key pass
+      __builtin_amdgcn_iglp_opt(0);
       frag kf[NSD];
 #pragma unroll
       for (int ks = 0; ks < NSD; ++ks) kf[ks] = kfrag<T>(tK, kofs, c, st, ks);
