@@ -178,13 +178,16 @@ struct BwdQ {
           tau * ds[4 * e4], tau * ds[4 * e4 + 1], tau * ds[4 * e4 + 2], tau * ds[4 * e4 + 3]};
     }
     const int qr = lane >> 3, kc = 4 * (lane & 7);
-    // row iw0 + q, key jb + kc: offset jb + kc - iw0 - q
+    // row iw0 + q, key jb + kc: offset jb + kc - iw0 - q; rows qr, qr + 8,
+    // qr + 16, qr + 24 of the area (8 rows = 8 * kStagePitch floats apart)
+    constexpr int RB = 8 * kStagePitch * 4;
+    f32x4 v[4];
+    lds_read4x16<0, RB, 2 * RB, 3 * RB>(stage + qr * kStagePitch + kc, v[0], v[1], v[2], v[3]);
     float* base = dz_w + (jb + kc - iw0 - g.lo - c.wsq);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int q = 8 * r + qr;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + q * kStagePitch + kc);
-      store_f32x4_a4(base + (int64_t)q * (g.Wp - 1), v);
+      store_f32x4_a4(base + (int64_t)q * (g.Wp - 1), v[r]);
     }
   }
 
@@ -215,7 +218,7 @@ struct BwdQ {
       for (int ks = 0; ks < NSD; ++ks) kf[ks] = kfrag<T>(tK, kofs, c, st, ks);
       f32x16 s;
       if (BAND && kind == KIND_BAND)
-        s = qside_scores<T>(g, c, kf, zk, qf, KIND_BAND, j0, st, needmask,
+        s = qside_scores<T, STAGE>(g, c, kf, zk, qf, KIND_BAND, j0, st, needmask,
                             STAGE ? zs.row(st, l32) + E * hl : nullptr);
       else
         s = qside_scores<T>(g, c, kf, zk, qf, kind == KIND_HI ? KIND_HI : KIND_LO, j0, st,
@@ -420,7 +423,9 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
   c.kv_end = kv_end;
   c.has_zq = ZQ && (a.flags & F_ZQ);
   c.has_zk = ZK;
-  c.has_b = a.flags & F_B;
+  // (with a query-side table b is folded into Z^Q: no lookup of its own,
+  // and no code for one)
+  c.has_b = !ZQ && (a.flags & F_B);
   c.wsq = win_q(g, qb);
   c.zq_row = c.has_zq ? a.zq + zq_off(g, bh, imin(iq, zq_last(g))) : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;

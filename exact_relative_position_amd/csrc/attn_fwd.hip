@@ -190,7 +190,7 @@ struct Fwd {
       }
       f32x16 s;
       if (BAND && kind == KIND_BAND) {
-        s = qside_scores<T>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask,
+        s = qside_scores<T, ZQS>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask,
                             ZQS ? zs.row(st, l32) + E * hl : nullptr);
         if (stage_next) {
           if (st == 0) stage<0>(t + kGroups); else stage<1>(t + kGroups);
@@ -373,7 +373,9 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   c.kv_end = kv_end;
   c.has_zq = a.flags & F_ZQ;
   c.has_zk = ZK;
-  c.has_b = a.flags & F_B;
+  // (a staged kernel has a query-side table, into which b is folded: no
+  // lookup of its own, and no code for one)
+  c.has_b = !ZQS && (a.flags & F_B);
   c.wsq = win_q(g, qb);
   c.zq_row = c.has_zq ? a.zq + zq_off(g, bh, imin(iq, zq_last(g))) : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;

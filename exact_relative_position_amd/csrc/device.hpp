@@ -184,6 +184,33 @@ __device__ __forceinline__ void store_f32x4_a4(float* p, f32x4 v) {
   *reinterpret_cast<f32x4_a4*>(p) = v;
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Four 16-byte LDS reads at byte offsets O0..O3 from p, issued in one asm
+// block that also waits for them (the results are early-clobber operands,
+// so that no read lands in the address register of a later one).  For LDS areas that the kernel fills with
+// direct-to-LDS loads and waits for itself (explicit vmcnt and a barrier):
+// the compiler cannot tell such an area from the ones whose loads are still
+// in flight and would otherwise wait for every outstanding global access
+// (the prefetch of the next tile, the stores of this one) before the read.
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void lds_read4x16(const float* p, f32x4& a, f32x4& b, f32x4& c,
+                                             f32x4& d) {
+  const uint32_t ad = lds_addr(p);
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"(ad), "i"(O0), "i"(O1), "i"(O2), "i"(O3)
+      : "memory");
+}
+
 // s_waitcnt immediate for "vmcnt(0)" with the other counters left alone
 // (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]).
 constexpr int kWaitVmcnt0 = 0x0F70;

@@ -63,9 +63,12 @@ __device__ constexpr int kap0(int e) {
 // afterwards or belong to a discarded row, so what such a clamped load
 // returns never reaches a result.  For a live entry the clamp is the
 // identity: its unfolded row lies inside the group's window.
-// zst: this lane's Z^Q row in the LDS stage of the subtile (RowStage, offset
-// by E * hl), which then replaces the Z^Q gather from global memory.
-template <typename T>
+// STAGED: zst is this lane's Z^Q row in the LDS stage of the subtile
+// (RowStage, offset by E * hl), which then replaces the Z^Q gather from
+// global memory (a compile-time switch, so that a staged kernel carries no
+// gather path: a load in flight on a path not taken still makes the compiler
+// wait for it before registers it shares with the taken path are written).
+template <typename T, bool STAGED>
 __device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, int wk,
                                           const float* zst, f32x16& s) {
   const int Wm = g.W - 1;
@@ -74,9 +77,22 @@ __device__ __forceinline__ void band_seed(const Geo& g, const QCtx& c, int jb, i
   for (int e = 0; e < 16; ++e) v[e] = 0.f;
   if (c.has_zq) {
     const int base = jb - c.iq - g.lo - c.wsq;
-    if (zst) {
+    if constexpr (STAGED) {
+      if constexpr (sizeof(T) == 2) {
+        // kap0(e): e = 0..7 at floats 0..7, e = 8..15 at floats 16..23
+        f32x4 a0, a1, b0, b1;
+        lds_read4x16<0, 16, 64, 80>(zst, a0, a1, b0, b1);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] = zst[kap0<T>(e)];
+        for (int t = 0; t < 4; ++t) {
+          v[t] = a0[t];
+          v[4 + t] = a1[t];
+          v[8 + t] = b0[t];
+          v[12 + t] = b1[t];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = zst[kap0<T>(e)];
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[e] = c.zq_row[imin(imax(base + kap0<T>(e), 0), Wm)];
@@ -119,8 +135,8 @@ __device__ __forceinline__ typename MT<T>::frag kfrag(const char* sK, const int*
 // The per-query constant of a saturated tile (Z^Q of the saturated row plus
 // b) is NOT included.
 // kf: the NSD K fragments of this subtile (kfrag), already read from LDS.
-// zst: the lane's staged Z^Q row of a band subtile (see band_seed), or null.
-template <typename T>
+// STAGED, zst: the lane's staged Z^Q row of a band subtile (see band_seed).
+template <typename T, bool STAGED = false>
 __device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c,
                                                const typename MT<T>::frag* kf, const float* sZK,
                                                const typename MT<T>::frag* qf, int kind,
@@ -141,7 +157,7 @@ __device__ __forceinline__ f32x16 qside_scores(const Geo& g, const QCtx& c,
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = v[e];
   } else {
-    band_seed<T>(g, c, j0 + 32 * st + MT<T>::E * c.hl, win_k(g, j0 / kGroup), zst, s);
+    band_seed<T, STAGED>(g, c, j0 + 32 * st + MT<T>::E * c.hl, win_k(g, j0 / kGroup), zst, s);
   }
 #pragma unroll
   for (int ks = 0; ks < NSD; ++ks) {

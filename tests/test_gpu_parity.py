@@ -64,6 +64,12 @@ SMALL = [
              has_b=True, causal=True, b_std=0.02),
     Workload("wide_band_all_terms_f16", 1, 1, 1100, 64, "f16", IDENTITY, 1 / 8, has_aq=True,
              has_ak=True, has_b=True, b_std=0.1),
+    # wide windows without a query-side table: the query pass stages its band
+    # stores but has no Z^Q rows to stage; b is looked up per band score
+    Workload("wide_band_key_and_bias_f16", 1, 2, 1100, 64, "f16", IDENTITY, 1 / 8, has_aq=False,
+             has_ak=True, has_b=True, b_std=0.1),
+    Workload("wide_band_bias_only_bf16", 1, 2, 1060, 64, "bf16", IDENTITY, 1 / 8, has_aq=False,
+             has_b=True, causal=True, b_std=0.1),
     Workload("wide_band_causal_keypad_f16", 2, 1, 1050, 64, "f16",
              {"kind": "truncated", "lo": -1040, "hi": 1030}, 1 / 8, has_aq=True, has_ak=True,
              causal=True, key_padding=True, pad_frac=0.2),
