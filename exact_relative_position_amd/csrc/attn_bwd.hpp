@@ -65,10 +65,16 @@ __global__ __launch_bounds__((query_threads<T, GRP>()), (query_blocks_per_cu<T, 
     key = bid < kblocks;
     if (!key) bid -= kblocks;
   }
+  // The compiler's scheduling strategy 0 (LDS reads interleaved with the
+  // MFMAs) gains 1-2% where it fits the registers; with dropout, or with a
+  // key-side term and staged query rows, it doubles the spills (measured),
+  // so those kernels keep the default schedule.
+  constexpr bool SCHED = !DROP && !(ZK && SQ);
   if (key)
-    bwd_k_block<T, ZQ, ZK, SK, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0);
+    bwd_k_block<T, ZQ, ZK, SK, GRP, DROP, SCHED>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0);
   else
-    bwd_q_block<T, ZQ, ZK, SQ, GRP, DROP>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0, st1);
+    bwd_q_block<T, ZQ, ZK, SQ, GRP, DROP, SCHED>(branch_args(), bid, s0, s1, s2, s3, r0, r1, st0,
+                                                 st1);
 }
 
 template <typename T, bool GRP, bool DROP, bool ZQ, bool ZK, bool SQ, bool SK>

@@ -56,7 +56,8 @@ constexpr int key_blocks_per_cu() {
 
 // STAGE: band dZ^K stores go through an LDS staging area; GRP: two groups
 // of waves split the query tiles; DROP: attention dropout.
-template <typename T, bool STAGE, bool GRP, bool DROP>
+// SCHED: use the compiler's scheduling strategy 0 in the subtile loop.
+template <typename T, bool STAGE, bool GRP, bool DROP, bool SCHED>
 struct BwdK {
   static constexpr int kGroups = key_groups<T, GRP>();
   using M = MT<T>;
@@ -244,7 +245,7 @@ struct BwdK {
     for (int st = 0; st < 2; ++st) {
       // scheduling strategy 0 of the compiler (interleave the LDS operand
       // reads with the MFMAs): -1% to -2% on the passes, measured
-      __builtin_amdgcn_iglp_opt(0);
+      if constexpr (SCHED) __builtin_amdgcn_iglp_opt(0);
       f32x16 s;
       {
         float v[16];
@@ -383,12 +384,12 @@ struct BwdK {
 // blocks.  LDS (sizes for G = key_groups groups): sQ0..sO1 G*DTile bytes
 // each, sR0/sR1 G*4*kTile floats, sSt (STAGE only) 4*G*32*kStagePitchK
 // floats.
-template <typename T, bool ZQ, bool ZK, bool STAGE, bool GRP, bool DROP>
+template <typename T, bool ZQ, bool ZK, bool STAGE, bool GRP, bool DROP, bool SCHED>
 __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ0, char* sQ1,
                                             char* sO0, char* sO1, float* sR0, float* sR1,
                                             float* sSt) {
   using M = MT<T>;
-  using K = BwdK<T, STAGE, GRP, DROP>;
+  using K = BwdK<T, STAGE, GRP, DROP, SCHED>;
   constexpr int TB = DTile<T>::BYTES;
   constexpr int G = K::kGroups;
 
@@ -424,7 +425,9 @@ __device__ __forceinline__ void bwd_k_block(const AttnArgs& a, int bid, char* sQ
   k.sig = sigma<T>(l32);
   k.has_zq = ZQ;
   k.has_zk = ZK && (a.flags & F_ZK);
-  k.has_b = a.flags & F_B;
+  // (with a query-side table b is folded into Z^Q: no lookup of its own,
+  // and no code for one)
+  k.has_b = !ZQ && (a.flags & F_B);
 
   int kv_end = N;
   if (a.flags & F_KEYPAD) kv_end = imax(0, imin(N, a.key_len[bb]));

@@ -49,7 +49,8 @@ constexpr int query_blocks_per_cu() {
 
 // STAGE: band stores go through an LDS staging area (chosen for wide bands);
 // GRP: two groups of waves split the key tiles; DROP: attention dropout.
-template <typename T, bool STAGE, bool GRP, bool DROP>
+// SCHED: use the compiler's scheduling strategy 0 in the subtile loop.
+template <typename T, bool STAGE, bool GRP, bool DROP, bool SCHED>
 struct BwdQ {
   static constexpr int kGroups = query_groups<T, GRP>();
   using M = MT<T>;
@@ -212,7 +213,7 @@ struct BwdQ {
     for (int st = 0; st < 2; ++st) {
       // scheduling strategy 0 of the compiler (interleave the LDS operand
       // reads with the MFMAs), as in the key pass
-      __builtin_amdgcn_iglp_opt(0);
+      if constexpr (SCHED) __builtin_amdgcn_iglp_opt(0);
       frag kf[NSD];
 #pragma unroll
       for (int ks = 0; ks < NSD; ++ks) kf[ks] = kfrag<T>(tK, kofs, c, st, ks);
@@ -352,12 +353,12 @@ struct BwdQ {
 // B*H*nblk blocks.  LDS (sizes for G = query_groups groups): sK0..sV1
 // G*DTile bytes each, sZK0/sZK1 G*2*kTile floats, sSt0/sSt1 (STAGE only)
 // 4*G*kStageFloats floats.
-template <typename T, bool ZQ, bool ZK, bool STAGE, bool GRP, bool DROP>
+template <typename T, bool ZQ, bool ZK, bool STAGE, bool GRP, bool DROP, bool SCHED>
 __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK0, char* sK1,
                                             char* sV0, char* sV1, float* sZK0, float* sZK1,
                                             float* sSt0, float* sSt1) {
   using M = MT<T>;
-  using B = BwdQ<T, STAGE, GRP, DROP>;
+  using B = BwdQ<T, STAGE, GRP, DROP, SCHED>;
   constexpr int TB = DTile<T>::BYTES;
   constexpr int G = B::kGroups;
 
