@@ -142,7 +142,7 @@ struct BwdQ {
       const int i = iw0 + q;
       const int o = j - i;
       if (o > g.lo && o < g.hi && i < N && j < N && !(g.causal && j > i))
-        dz_w[(int64_t)q * g.Wp + o - g.lo - c.wsq] = v;
+        dz_w[(int64_t)q * g.Wp + o - g.lo - c.wsq + ((i + g.lo + c.wsq) & g.dsm)] = v;
     }
   }
 
@@ -184,11 +184,14 @@ struct BwdQ {
     constexpr int RB = 8 * kStagePitch * 4;
     f32x4 v[4];
     lds_read4x16<0, RB, 2 * RB, 3 * RB>(stage + qr * kStagePitch + kc, v[0], v[1], v[2], v[3]);
+    // with the row shift (dz_shift, dsm = 31) every run starts on a 128-byte
+    // line
     float* base = dz_w + (jb + kc - iw0 - g.lo - c.wsq);
+    const int t = iw0 + g.lo + c.wsq;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int q = 8 * r + qr;
-      store_f32x4_a4(base + (int64_t)q * (g.Wp - 1), v[r]);
+      store_f32x4_a4(base + (int64_t)q * (g.Wp - 1) + ((t + q) & g.dsm), v[r]);
     }
   }
 
@@ -451,7 +454,8 @@ __device__ __forceinline__ void bwd_q_block(const AttnArgs& a, int bid, char* sK
 #pragma unroll
     for (int e = 0; e < 16; ++e) q.dseed[e] = -q.Dl;
   }
-  q.dz_row = q.need_dz ? a.dzq + zq_off(g, bh, iq) : nullptr;
+  // (dz_row at the row's column shift, dz_shift; dz_w at row iw0, unshifted)
+  q.dz_row = q.need_dz ? a.dzq + zq_off(g, bh, iq) + ((iq + g.lo + c.wsq) & g.dsm) : nullptr;
   q.dz_w = q.need_dz ? a.dzq + zq_off(g, bh, iw0) : nullptr;
   q.zs.buf[0] = STAGE ? sSt0 + wall * kStageFloats : sSt0;
   q.zs.buf[1] = STAGE ? sSt1 + wall * kStageFloats : sSt1;

@@ -49,11 +49,13 @@ __device__ __forceinline__ void split_bf16(const float (&z)[8], bf16x8& hi, bf16
 // read but replaced by zero before the MFMA.
 constexpr int kRC = 32;  // columns per chunk
 
-template <typename T>
+// SH: the rows are shifted query rows of dZ^Q (dz_shift with dsm = 31)
+template <typename T, bool SH>
 struct RowsK {
   const float* dzb;   // dZ of this (b, h), row stride Wp
   const float* tub;   // unfolded fp32 table of this head, [Runf + 32][64]
   int N, Wp, i0, ws, cb, ce, w, lane, hl, l32;
+  int shb = 0;  // (SH) column shift of row i: (i + shb) & 31 (dz_shift)
 
   __device__ static int zswz(int r) { return (r >> 1) & 7; }
 
@@ -67,7 +69,8 @@ struct RowsK {
       const int lc = (lane & 7) ^ zswz(r);
       float* dst = zb + 256 * j;
       if (i0 + r < N) {
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + c0 + 4 * lc),
+        const int sc = c0 + 4 * lc + (SH ? (i0 + r + shb) & 31 : 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + sc),
                                          (lds_void_t*)dst, 16, 0, 0);
       } else {
         *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
@@ -108,7 +111,7 @@ struct RowsK {
   }
 };
 
-template <typename T>
+template <typename T, bool SH>
 __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   __shared__ __align__(16) float sZ0[128 * kRC], sZ1[128 * kRC];
   __shared__ __align__(16) float sT0[kRC * kHeadDim], sT1[kRC * kHeadDim];
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   const int bh = lid / a.nblk, rb = a.rb0 + lid - bh * a.nblk;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int tid = threadIdx.x;
-  RowsK<T> k;
+  RowsK<T, SH> k;
   k.w = wave_id();
   k.lane = tid & 63;
   k.hl = k.lane >> 5;
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
   } else {
     cols_q(g, rb, k.cb, k.ce);
     k.ws = win_q(g, rb);
+    k.shb = g.lo + k.ws;  // (dz_shift)
   }
   // rows addressed by token (key side: every key; query side: the held rows)
   k.dzb = a.key_side ? a.dz + (int64_t)bh * N * g.Wp : a.dz + zq_off(g, bh, 0);
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowsArgs a) {
 // tables, low part) goes into LDS in the swizzled 16-bit tile layout and is
 // read as the MFMA B operand with transpose reads; each lane splits its 8 dZ
 // values of a k-step into bf16 parts.
-template <typename T>
+template <typename T, bool SH>
 struct Rows2K {
   using BF = MT<__bf16>;
   static constexpr bool kLo = std::is_same<T, _Float16>::value;  // table has a low part
@@ -192,6 +196,7 @@ struct Rows2K {
   const __bf16* thb;  // unfolded table of this head, high part, [Runf + 32][64]
   const __bf16* tlb;  // low part (fp16 tables)
   int N, Wp, i0, ws, cb, ce, w, lane, hl, l32;
+  int shb = 0;  // (SH) column shift of row i: (i + shb) & 31 (dz_shift)
   TrReader<__bf16> tr;
 
   __device__ __forceinline__ void issue(float* zb, char* th, char* tl, int c0) const {
@@ -199,10 +204,11 @@ struct Rows2K {
     for (int u = 0; u < 4; ++u) {
       const int j = 4 * w + u;  // 8 rows per instruction
       const int r = 8 * j + (lane >> 3);
-      const int lc = (lane & 7) ^ RowsK<T>::zswz(r);
+      const int lc = (lane & 7) ^ RowsK<T, SH>::zswz(r);
       float* dst = zb + 256 * j;
       if (i0 + r < N) {
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + c0 + 4 * lc),
+        const int sc = c0 + 4 * lc + (SH ? (i0 + r + shb) & 31 : 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + sc),
                                          (lds_void_t*)dst, 16, 0, 0);
       } else {
         *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
@@ -225,7 +231,7 @@ struct Rows2K {
                                             int c0, f32x16 (&acc)[2]) const {
     const int r = 32 * w + l32;
     const float* zr = zb + 32 * r;
-    const int sw = RowsK<T>::zswz(r);
+    const int sw = RowsK<T, SH>::zswz(r);
 #pragma unroll
     for (int ks = 0; ks < kRC / 16; ++ks) {
       const int c = 16 * ks + 8 * hl;  // first of the lane's 8 columns
@@ -256,11 +262,11 @@ struct Rows2K {
   }
 };
 
-template <typename T>
+template <typename T, bool SH>
 __global__ __launch_bounds__(kThreads) void rows2_kernel(RowsArgs a) {
   static_assert(sizeof(T) == 2, "16-bit inputs");
   constexpr int TT = kRC * kHeadDim * 2;  // bytes of one table part chunk
-  constexpr int TL = Rows2K<T>::kLo ? TT : 16;
+  constexpr int TL = Rows2K<T, SH>::kLo ? TT : 16;
   __shared__ __align__(16) float sZ0[128 * kRC], sZ1[128 * kRC];
   __shared__ __align__(16) char sH0[TT], sH1[TT], sL0[TL], sL1[TL];
   const Geo g = a.geo;
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void rows2_kernel(RowsArgs a) {
   const int bh = lid / a.nblk, rb = a.rb0 + lid - bh * a.nblk;
   const int bb = bh / a.H, hh = bh - bb * a.H;
   const int tid = threadIdx.x;
-  Rows2K<T> k;
+  Rows2K<T, SH> k;
   k.w = wave_id();
   k.lane = tid & 63;
   k.hl = k.lane >> 5;
@@ -284,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void rows2_kernel(RowsArgs a) {
   } else {
     cols_q(g, rb, k.cb, k.ce);
     k.ws = win_q(g, rb);
+    k.shb = g.lo + k.ws;  // (dz_shift)
   }
   k.dzb = a.key_side ? a.dz + (int64_t)bh * N * g.Wp : a.dz + zq_off(g, bh, 0);
   k.thb = (const __bf16*)a.tunf + hh * a.tunf_hs;
@@ -349,7 +356,7 @@ __device__ __forceinline__ bool before(RowPos a, RowPos b) {
   return a.seg < b.seg || (a.seg == b.seg && a.i < b.i);
 }
 
-template <typename T>
+template <typename T, bool SH>
 struct ColsK {
   const float* dz;
   const __bf16* x;   // X operand (bf16 inputs: X itself; fp16: its high part)
@@ -421,7 +428,11 @@ struct ColsK {
         key_side ? dz + (int64_t)(b_ * H + h_) * N * Wp : dz + zq_off(g, b_ * H + h_, 0);
     int cb, ce, ws;
     window(group_of(p), cb, ce, ws);
-    const int colb = u0 - ws;  // stored column of the block's first unfolded row
+    const int colb = u0 - ws;  // window column of the block's first unfolded row
+    // rows of dZ^Q may be stored shifted (dz_shift); columns below z_span
+    // stay inside the row after the shift
+    const int shb = i + g.lo + ws;
+    const int span = SH ? z_span(g) : Wp;
     if ((colb & 3) == 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -429,8 +440,9 @@ struct ColsK {
         const int r = 4 * j + (lane >> 4);
         const int col = colb + 4 * (lane & 15);
         float* dst = zb + 256 * j;
-        if (r < nrow && col >= 0 && col < Wp) {
-          __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + col),
+        if (r < nrow && col >= 0 && col < span) {
+          const int sc = col + (SH ? (r + shb) & 31 : 0);
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + sc),
                                            (lds_void_t*)dst, 16, 0, 0);
         } else {
           *reinterpret_cast<Chunk*>(dst + 4 * lane) = Chunk{{0u, 0u, 0u, 0u}};
@@ -444,9 +456,10 @@ struct ColsK {
       for (int u = 0; u < 16; ++u) {
         const int r = 16 * w + u;
         float* dst = zb + kCU * r;
-        if (r < nrow && col >= 0 && col < Wp) {
-          __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + col),
-                                           (lds_void_t*)dst, 4, 0, 0);
+        if (r < nrow && col >= 0 && col < span) {
+          __builtin_amdgcn_global_load_lds(
+              (glb_void_t*)(dzs + (int64_t)(i + r) * Wp + col + (SH ? (r + shb) & 31 : 0)),
+              (lds_void_t*)dst, 4, 0, 0);
         } else {
           dst[lane] = 0.f;
         }
@@ -513,7 +526,7 @@ struct ColsMma {
   }
 };
 
-template <typename T, bool WANT_X>
+template <typename T, bool WANT_X, bool SH>
 __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   static_assert(sizeof(T) == 2, "16-bit inputs");
   constexpr int XB = WANT_X ? DTile<__bf16>::BYTES : 16;
@@ -526,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void cols1_kernel(ColsArgs a) {
   const int lid = xcd_remap(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), nblk);
   const int ut = lid % gridDim.x, sp = (lid / gridDim.x) % gridDim.y;
   const int ho = lid / (gridDim.x * gridDim.y);
-  ColsK<T> k;
+  ColsK<T, SH> k;
   k.w = wave_id();
   k.lane = threadIdx.x & 63;
   k.hl = k.lane >> 5;
@@ -723,7 +736,8 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColsArgs a) {
         for (int s2 = 0; s2 < 8; ++s2) {
           const int i = ib + 2 * s2 + hl;
           const bool rv = i < i_end;
-          av[s2] = (rv && colv) ? dzb[(int64_t)i * g.Wp + col] : 0.f;
+          const int sc = col + (a.key_side ? 0 : ((i + g.lo + ws) & g.dsm));  // (dz_shift)
+          av[s2] = (rv && colv) ? dzb[(int64_t)i * g.Wp + sc] : 0.f;
           const T* xr = xb + (int64_t)i * a.sx.n;
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
@@ -812,13 +826,25 @@ __global__ __launch_bounds__(256) void fold_kernel(FoldArgs a) {
   }
 }
 
+template <typename T, bool SPLIT>
+static void launch_rows_t(const RowsArgs& a, int total, bool sh, hipStream_t st) {
+  if constexpr (SPLIT) {
+    if (sh) hipLaunchKernelGGL((rows2_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((rows2_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
+  } else {
+    if (sh) hipLaunchKernelGGL((rows_kernel<T, true>), dim3(total), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((rows_kernel<T, false>), dim3(total), dim3(kThreads), 0, st, a);
+  }
+}
+
 hipError_t launch_rows(int dtype, const RowsArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nblk;
   if (total <= 0) return hipSuccess;
+  const bool sh = !a.key_side && a.geo.dsm;  // shifted rows of dZ^Q
   switch (dtype) {
-    case 0: hipLaunchKernelGGL(rows_kernel<float>, dim3(total), dim3(kThreads), 0, st, a); break;
-    case 1: hipLaunchKernelGGL(rows2_kernel<_Float16>, dim3(total), dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL(rows2_kernel<__bf16>, dim3(total), dim3(kThreads), 0, st, a); break;
+    case 0: launch_rows_t<float, false>(a, total, sh, st); break;
+    case 1: launch_rows_t<_Float16, true>(a, total, sh, st); break;
+    default: launch_rows_t<__bf16, true>(a, total, sh, st); break;
   }
   return hipGetLastError();
 }
@@ -843,14 +869,21 @@ hipError_t launch_tab_unfold(int dtype, const TabUnfoldArgs& a, hipStream_t st) 
   return hipGetLastError();
 }
 
+template <typename T, bool SH>
+static void launch_cols1_t(const ColsArgs& a, dim3 grid, hipStream_t st) {
+  if (a.want_x) hipLaunchKernelGGL((cols1_kernel<T, true, SH>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((cols1_kernel<T, false, SH>), grid, dim3(kThreads), 0, st, a);
+}
+
 hipError_t launch_cols1(int dtype, const ColsArgs& a, int Ho, hipStream_t st) {
   dim3 grid((a.Rpad + kCU - 1) / kCU, a.splits, Ho);
+  const bool sh = !a.key_side && a.geo.dsm;  // shifted rows of dZ^Q
   if (dtype == 1) {
-    if (a.want_x) hipLaunchKernelGGL((cols1_kernel<_Float16, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((cols1_kernel<_Float16, false>), grid, dim3(kThreads), 0, st, a);
+    if (sh) launch_cols1_t<_Float16, true>(a, grid, st);
+    else launch_cols1_t<_Float16, false>(a, grid, st);
   } else {
-    if (a.want_x) hipLaunchKernelGGL((cols1_kernel<__bf16, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((cols1_kernel<__bf16, false>), grid, dim3(kThreads), 0, st, a);
+    if (sh) launch_cols1_t<__bf16, true>(a, grid, st);
+    else launch_cols1_t<__bf16, false>(a, grid, st);
   }
   return hipGetLastError();
 }

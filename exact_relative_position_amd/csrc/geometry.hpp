@@ -26,6 +26,9 @@ namespace relpos {
 constexpr int kGroup = 128;   // G: query/key group = largest block
 constexpr int kHeadDim = 64;  // d
 constexpr int kBlockRows = kGroup;  // rows owned by a workgroup (4 waves x 32)
+// Window width from which the rows of dZ^Q are stored shifted (dz_shift):
+// every key tile of such a row is a band tile.
+constexpr int kShiftMinW = 1024;
 
 struct Geo {
   int N;       // sequence length
@@ -39,6 +42,9 @@ struct Geo {
   // unless the projection is computed one chunk of queries at a time.  The
   // key-side buffers always hold every key row.
   int zr, z0;
+  // Column shift mask of the rows of dZ^Q (see dz_shift): 31 (rows shifted)
+  // or 0 (unshifted).
+  int dsm;
 };
 
 RP_HD int imin(int a, int b) { return a < b ? a : b; }
@@ -57,12 +63,34 @@ RP_HD int64_t zq_off(const Geo& g, int64_t bh, int i) {
 // Last query row the query-side buffers hold (the clamp of rows beyond N).
 RP_HD int zq_last(const Geo& g) { return imin(g.N, g.z0 + g.zr) - 1; }
 
+// Row pitch of the Z / dZ buffers for a window of w columns: w rounded up to
+// 32 floats (128 bytes), plus 32 floats of slack when the rows of dZ^Q are
+// shifted (see dz_shift).
+RP_HD int z_pitch(int w, bool shifted) { return (w + 31) / 32 * 32 + (shifted ? 32 : 0); }
+// Columns of a row below which every access, shifted, stays inside the row.
+RP_HD int z_span(const Geo& g) { return g.dsm ? g.Wp - 32 : g.Wp; }
+
 // First unfolded row stored for query group `grp` (window [ws, ws + W)).
 RP_HD int win_q(const Geo& g, int grp) {
   if (!grouped(g)) return 0;
   int s = rrow(g, -(grp * kGroup + kGroup - 1));
   return imin(s, g.R - g.W);
 }
+// Column shift of query row i in the storage of dZ^Q: window column c of the
+// row sits at storage column c + dz_shift(g, i).  The band run of row i
+// against the 32 keys [jb, jb + 32) starts at window column jb - i - lo - ws
+// (ws the row group's window start); adding (i + lo + ws) mod 32 turns that
+// into jb minus a multiple of 32, so with jb a multiple of 32 every such run
+// fills whole 128-byte lines, and the query pass writes whole lines
+// (unshifted, the runs of most rows straddle two lines and their halves are
+// written at different times).  Z^Q and the key-side buffers are not
+// shifted: their band runs are read, and a read of two half lines costs
+// less than the projection would pay to write shifted rows.
+RP_HD int dz_shift(const Geo& g, int i) {
+  const int ws = grouped(g) ? win_q(g, i / kGroup) : 0;
+  return (i + g.lo + ws) & g.dsm;
+}
+
 // First unfolded row stored for key group `grp`.
 RP_HD int win_k(const Geo& g, int grp) {
   if (!grouped(g)) return 0;
