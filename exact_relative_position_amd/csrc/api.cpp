@@ -211,9 +211,9 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   pl.geo.W = (int)std::min<int64_t>(pl.Runf, (int64_t)pl.N + kGroup - 1);
   pl.geo.causal = (mask->flags & RELPOS_MASK_CAUSAL) ? 1 : 0;
   if (pl.geo.W < 1) pl.geo.W = 1;
-  // rows of dZ^Q shifted (band runs on whole lines) for wide windows, where
-  // every tile of a row is a band tile
-  pl.geo.dsm = pl.geo.W >= kShiftMinW ? 31 : 0;
+  // rows of dZ^Q shifted (band runs on whole lines) for wide bands, where
+  // most tiles of a row are band tiles
+  pl.geo.dsm = wide_band(pl.geo) ? 31 : 0;
   pl.geo.Wp = z_pitch(pl.geo.W, pl.geo.dsm != 0);
   pl.phi.kind = phi->kind;
   pl.phi.N = pl.N;

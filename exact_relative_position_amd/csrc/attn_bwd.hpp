@@ -86,7 +86,7 @@ static void launch_bwd_v(const AttnArgs& a, int grid, int kblocks, int weave, hi
 template <typename T, bool GRP, bool DROP, bool ZQ>
 static void launch_bwd_z(const AttnArgs& a, bool zk, bool sq, bool sk, int grid, int kblocks,
                          int weave, hipStream_t st) {
-  // sq (W >= kStageMinW) implies W >= kStageMinWK, so sk == zk whenever sq
+  // sq (a wide band) implies sk == zk
   if (!zk) {
     if (sq) launch_bwd_v<T, GRP, DROP, ZQ, false, true, false>(a, grid, kblocks, weave, st);
     else launch_bwd_v<T, GRP, DROP, ZQ, false, false, false>(a, grid, kblocks, weave, st);
@@ -103,13 +103,13 @@ static void launch_bwd_z(const AttnArgs& a, bool zk, bool sq, bool sk, int grid,
 // the key pass (want_k: B*H*nblk blocks) or both.
 template <typename T>
 hipError_t launch_bwd_t(const AttnArgs& a, bool want_q, bool want_k, hipStream_t st) {
-  static_assert(kStageMinW >= kStageMinWK, "staging of the query pass implies the key pass's");
   const int kblocks = want_k ? a.B * a.H * a.nblk : 0;
   const int grid = kblocks + (want_q ? a.B * a.H * a.nqb : 0);
   if (grid == 0) return hipSuccess;
   const int weave = want_q && want_k && a.geo.causal && a.nqb == a.nblk;
   const bool zq = a.flags & F_ZQ, zk = a.flags & F_ZK;
-  const bool sq = a.geo.W >= kStageMinW, sk = zk && a.geo.W >= kStageMinWK;
+  // staging of the query pass implies the key pass's
+  const bool sq = wide_band(a.geo), sk = zk && (sq || a.geo.W >= kStageMinWK);
   if constexpr (sizeof(T) == 2) {
     if (a.flags & F_DROP) {
       if (a.split) {

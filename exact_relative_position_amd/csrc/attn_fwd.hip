@@ -459,7 +459,7 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
 template <typename T, bool GRP, bool DROP>
 static hipError_t launch_fwd_g(const AttnArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.nqb;
-  const bool zk = a.flags & F_ZK, zqs = (a.flags & F_ZQ) && a.geo.W >= kStageMinW;
+  const bool zk = a.flags & F_ZK, zqs = (a.flags & F_ZQ) && wide_band(a.geo);
   const int nt = fwd_threads<T, GRP>();
   if (zk && zqs)
     hipLaunchKernelGGL((fwd_kernel<T, true, true, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);

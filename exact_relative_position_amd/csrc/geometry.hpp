@@ -26,9 +26,8 @@ namespace relpos {
 constexpr int kGroup = 128;   // G: query/key group = largest block
 constexpr int kHeadDim = 64;  // d
 constexpr int kBlockRows = kGroup;  // rows owned by a workgroup (4 waves x 32)
-// Window width from which the rows of dZ^Q are stored shifted (dz_shift):
-// every key tile of such a row is a band tile.
-constexpr int kShiftMinW = 1024;
+// Window width from which a band counts as wide (see wide_band).
+constexpr int kWideW = 1024;
 
 struct Geo {
   int N;       // sequence length
@@ -54,6 +53,14 @@ RP_HD int imax(int a, int b) { return a > b ? a : b; }
 RP_HD int rrow(const Geo& g, int o) { return imin(imax(o, g.lo), g.hi) - g.lo; }
 
 RP_HD bool grouped(const Geo& g) { return g.W < g.R; }
+
+// Whether most key tiles of a query row are band tiles: a window of kWideW
+// columns or more (the identity map), or a sequence no longer than the
+// window (short sequences).  Then the lane = query kernels stage the band
+// rows of Z^Q through LDS instead of gathering them per score, and the rows
+// of dZ^Q are stored shifted (dz_shift); narrower bands, where only a few
+// tiles per row are band tiles, gather.
+RP_HD bool wide_band(const Geo& g) { return g.W >= kWideW || g.W >= g.N; }
 
 // Float offset of query row i of (b, h) in the query-side Z / dZ buffers
 // (rows outside [z0, z0 + zr) are not held).

@@ -25,10 +25,6 @@ namespace relpos {
 
 enum : int { KIND_LO = 0, KIND_BAND = 1, KIND_HI = 2 };
 
-// Window width from which the lane = query kernels stage band rows through
-// LDS (most key tiles are then band tiles); narrower bands gather per score.
-constexpr int kStageMinW = 1024;
-
 // Kind of the tile of keys [j0, j0 + 64) for the 32 queries [iw0, iw0 + 32).
 __device__ inline int tile_kind_q(const Geo& g, int j0, int iw0) {
   int omax = j0 + kTile - 1 - iw0;

@@ -175,9 +175,9 @@ relpos_status relpos_attn_workspace_size(const relpos_problem* prob, const relpo
  * (keeping them trades memory for recomputation, section on ablations):
  * B*H*N rows per present vector term, each of the window width rounded up
  * to 32 floats (128 bytes), plus 32 floats when the window is 1024 columns
- * or wider (the workspace's relation gradients then store each row shifted,
- * and all relation rows share one pitch).  0 when no vector table is present.
- * Host-only. */
+ * or wider or no narrower than N (the workspace's relation gradients then
+ * store each row shifted, and all relation rows share one pitch).  0 when no
+ * vector table is present.  Host-only. */
 relpos_status relpos_attn_zsave_size(const relpos_problem* prob, const relpos_phi* phi,
                                      int32_t terms, size_t* bytes);
 

@@ -58,8 +58,10 @@ SMALL = [
     Workload("n1_bf16", 1, 1, 1, 64, "bf16", IDENTITY, 1 / 8, has_aq=True, has_b=True),
     Workload("n129_causal_f16", 1, 1, 129, 64, "f16", IDENTITY, 1 / 8, has_aq=True, has_b=True,
              causal=True, b_std=0.02),
-    # windows of >= 1024 columns: Z^Q rows staged in LDS by the forward and the
-    # query pass, band stores staged; causal: grouped query / key passes
+    # wide bands (windows of >= 1024 columns, as here, or no shorter than the
+    # sequence, as in the tiny cases above): Z^Q rows staged in LDS by the
+    # forward and the query pass, band stores staged, rows of dZ^Q shifted;
+    # causal: grouped query / key passes
     Workload("wide_band_causal_bf16", 1, 2, 1000, 64, "bf16", IDENTITY, 1 / 8, has_aq=True,
              has_b=True, causal=True, b_std=0.02),
     Workload("wide_band_all_terms_f16", 1, 1, 1100, 64, "f16", IDENTITY, 1 / 8, has_aq=True,
