@@ -76,6 +76,8 @@ def describe(w):
         out["dropout_p"] = w.dropout[0] / 256.0
     if w.zchunk:
         out["zchunk"] = w.zchunk
+    if w.relation:
+        out["relation"] = w.relation
     return out
 
 
@@ -220,7 +222,7 @@ def measure_peak_memory(torch, dev, t, w, drop):
     import exact_relative_position_amd as rp
     args = (t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"])
     kw = dict(phi=w.phi, tau=w.tau, causal=w.causal, key_len=t["key_len"], dropout=drop,
-              zchunk=w.zchunk)
+              zchunk=w.zchunk, relation=w.relation)
     torch.cuda.synchronize(dev)
     base = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
@@ -300,6 +302,8 @@ def run_sweep(args):
                 if mechs is None or n.split("_")[0] in mechs}
         metric = "layer sweep: fwd and bwd ms, TFLOP/s, extra memory"
     for name, w in todo.items():
+        if args.relation and not (args.relation == 2 and w.has_ak):
+            w = w.with_(relation=args.relation)
         x = make_inputs(w)
         t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
         torch.cuda.synchronize(dev)
@@ -307,7 +311,7 @@ def run_sweep(args):
         torch.cuda.reset_peak_memory_stats(dev)
         run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
                           tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True,
-                          zchunk=w.zchunk)
+                          zchunk=w.zchunk, relation=w.relation)
         stage_ms, gpu_ms, _ = time_stages(torch, dev, stage_list(B_, run), args.warmup,
                                           args.steps)
         peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs
@@ -356,6 +360,9 @@ def main():
     ap.add_argument("--zchunk", type=int, default=0,
                     help="compute the query-side projection this many queries at a time "
                          "(a multiple of 128; 0 = the whole sequence)")
+    ap.add_argument("--relation", type=int, default=0, choices=(0, 1, 2),
+                    help="how the forward gets the query-side relation term: 0 by sequence "
+                         "length (default), 1 stored projection, 2 computed in each block")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="attention dropout probability (fp16/bf16; rounded to a multiple "
                          "of 1/256; generator seed 2024, offset 0)")
@@ -386,6 +393,8 @@ def main():
         w = sweep[args.workload]
     if args.zchunk:
         w = w.with_(name=f"{w.name}_chunk{args.zchunk}", zchunk=args.zchunk)
+    if args.relation:
+        w = w.with_(name=f"{w.name}_rel{args.relation}", relation=args.relation)
     t_drop = int(round(args.dropout * 256))
     if t_drop > 0:
         w = w.with_(name=f"{w.name}_dropout{t_drop}", dropout=(t_drop, 2024, 0))
@@ -401,7 +410,7 @@ def main():
     drop = None if w.dropout is None else (w.dropout[0] / 256.0, w.dropout[1], w.dropout[2])
     run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
                       tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=True,
-                      dropout=drop, zchunk=w.zchunk)
+                      dropout=drop, zchunk=w.zchunk, relation=w.relation)
     stages = stage_list(B_, run, args.separate_passes)
     stage_ms, gpu_ms, wall = time_stages(torch, dev, stages, args.warmup, args.steps)
     peak_extra = torch.cuda.max_memory_allocated(dev) - mem_inputs

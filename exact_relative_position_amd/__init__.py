@@ -39,30 +39,35 @@ class RelPosAttention(torch.autograd.Function):
     """Autograd wrapper: the forward keeps O, LSE and the relation projections."""
 
     @staticmethod
-    def forward(ctx, q, k, v, aq, ak, b, phi, tau, causal, key_len, dropout=None, zchunk=0):
+    def forward(ctx, q, k, v, aq, ak, b, phi, tau, causal, key_len, dropout=None, zchunk=0,
+                relation=0):
         O, lse, zs = _binding.forward(q, k, v, aq, ak, b, phi=phi, tau=tau, causal=causal,
                                       key_len=key_len, keep_z=True, dropout=dropout,
-                                      zchunk=zchunk)
+                                      zchunk=zchunk, relation=relation)
         ctx.save_for_backward(q, k, v, aq, ak, b, O, lse, zs, key_len)
-        ctx.cfg = (phi, tau, causal, dropout, zchunk)
+        ctx.cfg = (phi, tau, causal, dropout, zchunk, relation)
         return O
 
     @staticmethod
     def backward(ctx, dO):
         q, k, v, aq, ak, b, O, lse, zs, key_len = ctx.saved_tensors
-        phi, tau, causal, dropout, zchunk = ctx.cfg
+        phi, tau, causal, dropout, zchunk, relation = ctx.cfg
         dq, dk, dv, daq, dak, db = _binding.backward(
             q, k, v, aq, ak, b, O, lse, dO.contiguous(), zs, phi=phi, tau=tau, causal=causal,
-            key_len=key_len, dropout=dropout, zchunk=zchunk)
+            key_len=key_len, dropout=dropout, zchunk=zchunk, relation=relation)
         cast = lambda g, t: None if g is None else g.to(t.dtype)  # noqa: E731
         return (dq, dk, dv, cast(daq, aq), cast(dak, ak), cast(db, b), None, None, None, None,
-                None, None)
+                None, None, None)
 
 
 def relpos_attention(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False,
-                     key_len=None, dropout=None, zchunk=0):
+                     key_len=None, dropout=None, zchunk=0, relation=0):
     """Differentiable relative-position attention; q, k, v are [B, H, N, 64] on the GPU;
     ``dropout`` = (p, seed, offset) or None; ``zchunk`` > 0 (a multiple of 128)
     recomputes the query-side projection one chunk of queries at a time in both
-    passes, so that memory stays linear in N for the identity map."""
-    return RelPosAttention.apply(q, k, v, aq, ak, b, phi, tau, causal, key_len, dropout, zchunk)
+    passes, so that memory stays linear in N for the identity map; ``relation``
+    (0 auto, 1 stored, 2 in-block) says how the forward gets the query-side
+    relation term (in-block: recomputed inside each attention block, nothing
+    stored; the backward projects it)."""
+    return RelPosAttention.apply(q, k, v, aq, ak, b, phi, tau, causal, key_len, dropout, zchunk,
+                                 relation)

@@ -22,6 +22,7 @@ PHI_KIND = {"truncated": 0, "t5": 1, "identity": 2, "log": 3}
 MASK_CAUSAL, MASK_KEY_PADDING = 1, 2
 TERM_AQ, TERM_AK, TERM_B = 1, 2, 4
 PASS_FWD, PASS_BWD = 0, 1
+REL_AUTO, REL_STORED, REL_INBLOCK = 0, 1, 2
 T_Q, T_K, T_V, T_O, T_DO, T_DQ, T_DK, T_DV = range(8)
 
 EXPORTS = ("relpos_attn_workspace_size", "relpos_attn_zsave_size", "relpos_attn_fwd",
@@ -49,7 +50,8 @@ class Problem(ctypes.Structure):
                 ("strides", (ctypes.c_int64 * 3) * 8), ("aq_head_stride", ctypes.c_int64),
                 ("ak_head_stride", ctypes.c_int64), ("b_head_stride", ctypes.c_int64),
                 ("dropout_p", ctypes.c_float), ("dropout_offset", ctypes.c_uint32),
-                ("dropout_seed", ctypes.c_uint64), ("zchunk", ctypes.c_int64)]
+                ("dropout_seed", ctypes.c_uint64), ("zchunk", ctypes.c_int64),
+                ("relation", ctypes.c_int32)]
 
 
 class RelposError(RuntimeError):
@@ -219,10 +221,11 @@ def _check_zsave(zsave, q, nbytes):
                          f"{nbytes} bytes (the forward's saved projections)")
 
 
-def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None, zchunk=0):
+def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None, zchunk=0, relation=0):
     """Problem descriptor; ``tensors`` maps a role index to its [B,H,N,d] tensor;
     ``dropout`` = (p, seed, offset) or None; ``zchunk`` = query rows per chunk
-    of the projection (0: the whole sequence)."""
+    of the projection (0: the whole sequence); ``relation`` = REL_AUTO,
+    REL_STORED or REL_INBLOCK (how the forward gets the query-side term)."""
     B, H, N, d = q.shape
     p = Problem()
     p.B, p.H, p.N, p.d = B, H, N, d
@@ -239,6 +242,7 @@ def problem(q, tau, tensors, aq=None, ak=None, b=None, dropout=None, zchunk=0):
         p.dropout_seed = int(dropout[1]) & 0xFFFFFFFFFFFFFFFF
         p.dropout_offset = int(dropout[2]) & 0xFFFFFFFF
     p.zchunk = int(zchunk)
+    p.relation = int(relation)
     return p
 
 
@@ -297,7 +301,7 @@ def phi_rows(phi, N, device="cuda"):
 
 
 def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_len=None,
-            keep_z=True, out=None, dropout=None, zchunk=0):
+            keep_z=True, out=None, dropout=None, zchunk=0, relation=REL_AUTO):
     """O, LSE (and the saved projections, or None) of the relative-position
     attention; ``dropout`` = (p, seed, offset) or None; ``zchunk`` > 0 computes
     the projection one chunk of queries at a time (nothing is kept)."""
@@ -307,7 +311,7 @@ def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_le
     O = torch.empty_like(q) if out is None else out
     B, H, N, _ = q.shape
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout, zchunk)
+    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout, zchunk, relation)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     terms = _terms(aq, ak, b)
@@ -324,13 +328,13 @@ def forward(q, k, v, aq=None, ak=None, b=None, *, phi, tau, causal=False, key_le
 
 
 def forward_noalloc(q, k, v, aq=None, ak=None, b=None, *, phi, tau, O, lse, zsave=None,
-                    causal=False, key_len=None, dropout=None, zchunk=0):
+                    causal=False, key_len=None, dropout=None, zchunk=0, relation=REL_AUTO):
     """relpos_attn_fwd_noalloc: the forward into caller-given O and LSE (and
     zsave, or None), with the library's static scratch instead of a
     workspace; allocates nothing."""
     check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("O", O),))
     _check_lse(lse, q)
-    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout, zchunk)
+    prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: O}, aq, ak, b, dropout, zchunk, relation)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     _check_zsave(zsave, q, zsave_size(prob, phi_s, _terms(aq, ak, b)))
@@ -341,7 +345,7 @@ def forward_noalloc(q, k, v, aq=None, ak=None, b=None, *, phi, tau, O, lse, zsav
 
 
 def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=False,
-             key_len=None, dropout=None, zchunk=0):
+             key_len=None, dropout=None, zchunk=0, relation=REL_AUTO):
     """dQ, dK, dV (input dtype) and daQ, daK, db (fp32, shape of their table, or None)."""
     check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("o", o), ("do", do)))
     _check_lse(lse, q)
@@ -351,7 +355,7 @@ def backward(q, k, v, aq, ak, b, o, lse, do, zsave=None, *, phi, tau, causal=Fal
     dak = None if ak is None else torch.empty(ak.shape, dtype=torch.float32, device=dev)
     db = None if b is None else torch.empty(b.shape, dtype=torch.float32, device=dev)
     prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: o, T_DO: do, T_DQ: dq, T_DK: dk,
-                            T_DV: dv}, aq, ak, b, dropout, zchunk)
+                            T_DV: dv}, aq, ak, b, dropout, zchunk, relation)
     phi_s = phi_struct(phi)
     mask_s = mask_struct(causal, key_len)
     terms = _terms(aq, ak, b)
@@ -371,7 +375,7 @@ class Prepared:
     library calls (nothing is allocated in between)."""
 
     def __init__(self, q, k, v, aq, ak, b, do, *, phi, tau, causal=False, key_len=None,
-                 keep_z=True, dropout=None, zchunk=0):
+                 keep_z=True, dropout=None, zchunk=0, relation=REL_AUTO):
         check_inputs(q, k, v, aq, ak, b, phi=phi, key_len=key_len, tensors=(("do", do),))
         dev = q.device
         self.dev = dev
@@ -386,7 +390,7 @@ class Prepared:
         self.dak = None if ak is None else torch.empty(ak.shape, **f32)
         self.db = None if b is None else torch.empty(b.shape, **f32)
         self.prob = problem(q, tau, {T_Q: q, T_K: k, T_V: v, T_O: self.O, T_DO: do, T_DQ: self.dq,
-                                     T_DK: self.dk, T_DV: self.dv}, aq, ak, b, dropout, zchunk)
+                                     T_DK: self.dk, T_DV: self.dv}, aq, ak, b, dropout, zchunk, relation)
         self.phi_s = phi_struct(phi)
         self.mask_s = mask_struct(causal, key_len)
         terms = _terms(aq, ak, b)

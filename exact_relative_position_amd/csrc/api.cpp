@@ -77,6 +77,7 @@ struct Plan {
   int ncol_q = 0, ncol_k = 0;
   int zr = 0;          // query rows per chunk of the query-side projection
   int nchunk = 1;      // chunks of queries (1: the whole sequence at once)
+  bool inblock = false;  // forward: query-side relation computed in the block
   size_t zq_elems = 0; // query-side projection buffer (Z^Q, dZ^Q), elements
   size_t zk_elems = 0; // key-side projection buffer (Z^K, dZ^K), elements
   int rtiles = 0, Rpad = 0;
@@ -248,6 +249,21 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
       return fail(RELPOS_ERR_UNSUPPORTED,
                   "a chunked projection covers the query-side terms only (aK must be absent)");
   }
+  // how the forward gets the query-side relation (length-bucket table: the
+  // in-block path for sequences no longer than the relation window, where a
+  // stored window is as large as a dense bias; the stored projection beyond)
+  if (prob->relation < RELPOS_REL_AUTO || prob->relation > RELPOS_REL_INBLOCK)
+    return fail(RELPOS_ERR_INVALID_ARG, "unknown relation mode");
+  {
+    const bool can = pl.esz == 2 && !pl.has_ak && pl.nchunk == 1;
+    if (prob->relation == RELPOS_REL_INBLOCK && pl.has_aq && !can)
+      return fail(RELPOS_ERR_UNSUPPORTED,
+                  "the in-block relation needs fp16 or bf16 inputs, no aK and zchunk = 0");
+    const bool shortn = pl.geo.W >= pl.N;
+    pl.inblock = pl.has_aq && can &&
+                 (prob->relation == RELPOS_REL_INBLOCK ||
+                  (prob->relation == RELPOS_REL_AUTO && shortn));
+  }
   pl.geo.zr = pl.zr;
   pl.geo.z0 = 0;
   pl.zq_elems = (size_t)pl.B * pl.H * pl.zr * pl.geo.Wp;
@@ -354,7 +370,7 @@ size_t carve_fwd(const Plan& pl, bool zsave_given, void* base, WsFwd& w) {
   Carve c(base);
   if (pl.bucketed) w.fold = c.take<int32_t>(sizeof(int32_t) * pl.Runf);
   if (need_bunf(pl)) w.bunf = c.take<float>(sizeof(float) * pl.Runf * pl.ho_b);
-  if (!zsave_given) {
+  if (!zsave_given && !pl.inblock) {
     if (pl.has_aq) w.zq = c.take<float>(sizeof(float) * pl.zq_elems);
     if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.zk_elems);
   }
@@ -411,6 +427,7 @@ size_t carve_bwd(const Plan& pl, bool zsave_given, void* base, WsBwd& w) {
 
 size_t zsave_bytes(const Plan& pl) {
   if (pl.nchunk > 1) return 0;  // a chunked projection is never kept
+  if (pl.inblock) return 0;     // nor is there one with the in-block relation
   size_t n = 0;
   if (pl.has_aq) n += align256(sizeof(float) * pl.zq_elems);
   if (pl.has_ak) n += align256(sizeof(float) * pl.zk_elems);
@@ -624,6 +641,9 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
   if (zsave && !aligned16(zsave)) return fail(RELPOS_ERR_INVALID_ARG, "misaligned: zsave");
   if (zsave && pl.nchunk > 1)
     return fail(RELPOS_ERR_INVALID_ARG, "zsave must be NULL when the projection is chunked");
+  if (zsave && pl.inblock)
+    return fail(RELPOS_ERR_INVALID_ARG,
+                "zsave must be NULL with the in-block relation (relpos_attn_zsave_size is 0)");
   WsFwd w;
   const size_t need = carve_fwd(pl, zsave != nullptr, nullptr, w);
   if (use_scratch) {
@@ -649,7 +669,7 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
   hipStream_t st = (hipStream_t)stream;
   if (stages & RELPOS_FWD_PROJECT) {
     if ((s = prepare_tables(pl, b, w.fold, nullptr, nullptr, w.bunf, st)) != RELPOS_OK) return s;
-    if (pl.nchunk == 1 &&
+    if (pl.nchunk == 1 && !pl.inblock &&
         (s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st, pl.geo, 0, pl.nblk)) !=
             RELPOS_OK)
       return s;
@@ -661,6 +681,15 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
   a.zq = w.zq;
   a.zk = w.zk;
   a.bunf = w.bunf;
+  if (pl.inblock) {
+    a.flags |= F_ZIB;
+    a.tabq = aQ;
+    a.tabq_hs = pl.aq_hs;
+    a.tabb = b;
+    a.tabb_hs = pl.b_hs;
+    a.fold = pl.bucketed ? w.fold : nullptr;
+    a.split = 0;  // one wave group per block
+  }
   if (pl.nchunk == 1) return hip_check(launch_fwd(pl.dtype, a, st), "forward");
   // chunked projection: Z^Q of one chunk of queries, then their attention
   for (int c = 0; c < pl.nchunk; ++c) {
@@ -974,6 +1003,9 @@ relpos_status relpos_attn_bwd_stages(const relpos_problem* prob, const relpos_ph
       (stages & (RELPOS_BWD_QUERY_PASS | RELPOS_BWD_KEY_PASS)) !=
           (RELPOS_BWD_QUERY_PASS | RELPOS_BWD_KEY_PASS))
     return fail(RELPOS_ERR_INVALID_ARG, "a chunked backward runs both passes together");
+  if (zsave && pl.inblock)
+    return fail(RELPOS_ERR_INVALID_ARG,
+                "zsave must be NULL with the in-block relation (the forward keeps no projection)");
   carve_bwd(pl, zsave != nullptr, workspace, w);
   if (zsave) {
     Carve c(const_cast<void*>(zsave));

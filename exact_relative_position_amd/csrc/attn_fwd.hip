@@ -29,6 +29,7 @@
 // only, the normaliser sums all of them, and the final division carries the
 // 1 / (1 - p) factor; the keep bits come from dropout.hpp.
 #include "dropout.hpp"
+#include "inblock.hpp"
 #include "qside.hpp"
 
 namespace relpos {
@@ -45,31 +46,40 @@ template <typename T, bool GRP>
 constexpr int fwd_groups() {
   return (GRP && sizeof(T) == 2) ? 2 : 1;
 }
+// Ways the band tiles get the query-side relation: gathered per score from
+// the stored Z^Q, staged from it in LDS by row DMA (wide bands), or computed
+// in the block (no stored Z^Q; inblock.hpp).
+enum : int { ZM_GATHER = 0, ZM_STAGED = 1, ZM_INBLOCK = 2 };
+
 // Waves per SIMD the forward is compiled for: 16-bit inputs without a
-// key-side term, staged rows or groups fit 3 (168 VGPRs), which hides more
-// latency than operand prefetch (with dropout too: its few spills cost less
-// than the third wave gains); the others keep 2.
-template <typename T, bool ZK, bool ZQS, bool GRP, bool DROP>
+// key-side term, staged rows, in-block relation or groups fit 3 (168 VGPRs),
+// which hides more latency than operand prefetch (with dropout too: its few
+// spills cost less than the third wave gains); the others keep 2.
+template <typename T, bool ZK, int ZM, bool GRP, bool DROP>
 constexpr int fwd_occupancy() {
-  return (sizeof(T) == 2 && !ZK && !ZQS && !GRP) ? 3 : (sizeof(T) == 2 ? 2 : 1);
+  return (sizeof(T) == 2 && !ZK && ZM == ZM_GATHER && !GRP) ? 3 : (sizeof(T) == 2 ? 2 : 1);
 }
 template <typename T, bool GRP>
 constexpr int fwd_threads() {
   return kThreads * fwd_groups<T, GRP>();
 }
-template <typename T, bool ZK, bool ZQS, bool GRP, bool DROP>
+template <typename T, bool ZK, int ZM, bool GRP, bool DROP>
 constexpr int fwd_blocks_per_cu() {
-  return fwd_occupancy<T, ZK, ZQS, GRP, DROP>() / fwd_groups<T, GRP>();
+  return fwd_occupancy<T, ZK, ZM, GRP, DROP>() / fwd_groups<T, GRP>();
 }
 
-// ZQS: Z^Q band rows staged in LDS (wide bands) instead of gathered per score.
+struct NoInBlock {};
+
+// ZM: how band tiles get the query-side relation (ZM_*).
 // OCC3: compiled for 3 waves per SIMD: each subtile reads its own operand
 // fragments (instead of the whole tile's up front), which keeps fewer
 // registers live.  DROP: attention dropout.
-template <typename T, bool ZQS, bool OCC3, bool GRP, bool DROP>
+template <typename T, int ZM, bool OCC3, bool GRP, bool DROP>
 struct Fwd {
   using M = MT<T>;
   using frag = typename M::frag;
+  static constexpr bool ZQS = ZM == ZM_STAGED;
+  static constexpr bool ZIB = ZM == ZM_INBLOCK;
   static constexpr bool kHalf = sizeof(T) == 2;
   static constexpr bool kOcc3 = OCC3;
   static constexpr int kGroups = fwd_groups<T, GRP>();
@@ -103,6 +113,11 @@ struct Fwd {
   float m_used, lsum;
   RowStage zs;  // Z^Q band rows of this wave, staged per subtile
   DropCtx dr;   // DROP only
+  // in-block relation (ZIB only): the ring of table rows, and whether b is
+  // present
+  std::conditional_t<ZIB, InBlock<T>, NoInBlock> ib;
+  char* ring;
+  bool ib_b;
 
   // Issue the loads of tile t into LDS buffer BUF (asynchronous).
   template <int BUF>
@@ -110,6 +125,7 @@ struct Fwd {
     const int j0 = t * kTile;
     ldK.load(sK[BUF] + goff, Kb + (int64_t)j0 * sk, N - j0, lane);
     ldV.load(sV[BUF] + goff, Vb + (int64_t)j0 * sv, N - j0, lane);
+    if constexpr (ZIB) ib.load_block(g, ring, j0 - i0);  // the tile's 64 new offsets
     if (c.has_zk && w < 2) {
       const float* p = kside_sat_ptr(g, c.zkb, j0 + lane, w);
       dword_direct((char*)(sZK[BUF] + (2 * grp + w) * kTile), p, p != nullptr, lane);
@@ -163,6 +179,21 @@ struct Fwd {
     // the first half's MFMAs and softmax; at occupancy 3 (and for fp32) each
     // subtile reads its own
     frag kf[2][NSD], vf[2][2 * KPS];
+    // in-block relation: offset tiles U = 0, 1, 2 start at j0 - iw0 - 31 + 32 U;
+    // subtile st takes its seeds from tiles st and st + 1
+    f32x16 tprev;
+    int ob = 0;
+    T bv[3] = {};
+    if constexpr (ZIB) {
+      if (BAND && kind == KIND_BAND) {
+        ob = j0 - iw0 - 31;
+        if (ib_b) {
+#pragma unroll
+          for (int u = 0; u < 3; ++u) bv[u] = ib.b_of(g, ob + 32 * u);
+        }
+        tprev = ib.tmm(ob, qf, ib_b, bv[0], hl);
+      }
+    }
     if constexpr (kHalf && !kOcc3) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -189,7 +220,15 @@ struct Fwd {
           for (int kk = 0; kk < KPS; ++kk) vf[st][dt * KPS + kk] = vfrag(tV, dt, KPS * st + kk);
       }
       f32x16 s;
-      if (BAND && kind == KIND_BAND) {
+      if (ZIB && BAND && kind == KIND_BAND) {
+        if constexpr (ZIB) {
+          const f32x16 tn = ib.tmm(ob + 32 * (st + 1), qf, ib_b, bv[st + 1], hl);
+          float v[16];
+          ib.seeds(tprev, tn, v);
+          tprev = tn;
+          s = seeded_scores<T>(g, c, kf[st], qf, v, j0, st, needmask);
+        }
+      } else if (BAND && kind == KIND_BAND) {
         s = qside_scores<T, ZQS>(g, c, kf[st], zk, qf, KIND_BAND, j0, st, needmask,
                             ZQS ? zs.row(st, l32) + E * hl : nullptr);
         if (stage_next) {
@@ -275,7 +314,14 @@ struct Fwd {
   // same number of steps (one workgroup barrier each), step m in buffer m & 1.
   __device__ __forceinline__ void run(int t1, int t2) {
     const int t0 = grp;
-    if (t0 < nkt) issue<0>(t0);
+    if (t0 < nkt) {
+      issue<0>(t0);
+      if constexpr (ZIB) {
+        // the two blocks of offsets below the first tile's own
+        ib.load_block(g, ring, t0 * kTile - i0 - 128);
+        ib.load_block(g, ring, t0 * kTile - i0 - 64);
+      }
+    }
     if (band_here(t0)) {
       stage<0>(t0);
       stage<1>(t0);
@@ -295,29 +341,45 @@ struct Fwd {
 
 // ZK: whether the key-side relation term is present (a compile-time switch, so
 // that saturated tiles without it seed their MFMA accumulators with zero and
-// carry no branch); ZQS: Z^Q band rows staged in LDS; GRP: grouped workgroup;
-// DROP: attention dropout.
-template <typename T, bool ZK, bool ZQS, bool GRP, bool DROP>
-__global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, ZQS, GRP, DROP>()))
+// carry no branch); ZM: how band tiles get the query-side relation (ZM_*);
+// GRP: grouped workgroup; DROP: attention dropout.
+template <typename T, bool ZK, int ZM, bool GRP, bool DROP>
+__global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, ZM, GRP, DROP>()))
     void fwd_kernel(AttnArgs a) {
   using M = MT<T>;
   constexpr float kLn2 = 0.693147180559945309f;
   constexpr int TB = DTile<T>::BYTES;
   constexpr int G = fwd_groups<T, GRP>();
+  constexpr bool ZQS = ZM == ZM_STAGED;
 
   __shared__ __align__(16) char sK0[G * TB], sK1[G * TB], sV0[G * TB], sV1[G * TB];
-  __shared__ __align__(16) float sZK0[G * 2 * kTile], sZK1[G * 2 * kTile];
-  constexpr int kZQ = ZQS ? 4 * G * RowStage::kFloats : 4;
-  __shared__ __align__(16) float sZQ0[kZQ], sZQ1[kZQ];
 
-  using F = Fwd<T, ZQS, fwd_occupancy<T, ZK, ZQS, GRP, DROP>() == 3, GRP, DROP>;
+  using F = Fwd<T, ZM, fwd_occupancy<T, ZK, ZM, GRP, DROP>() == 3, GRP, DROP>;
   F f;
   f.sK[0] = sK0;
   f.sK[1] = sK1;
   f.sV[0] = sV0;
   f.sV[1] = sV1;
-  f.sZK[0] = sZK0;
-  f.sZK[1] = sZK1;
+  // (the in-block kernel has neither Z^K scalars nor staged rows: its ring
+  // and skew tiles take that LDS, 80 KB per block in all, two blocks per CU)
+  float* zq_stage[2];
+  if constexpr (ZM == ZM_INBLOCK) {
+    __shared__ __align__(128) char sRing[kRingBytes];
+    __shared__ __align__(128) float sSkew[4 * kSkewFloats];
+    f.ring = sRing;
+    f.ib.init(lds_addr(sRing), lds_addr(sSkew + wave_id() * kSkewFloats), wave_id(),
+              threadIdx.x & 63);
+    f.sZK[0] = f.sZK[1] = reinterpret_cast<float*>(sK0);
+    zq_stage[0] = zq_stage[1] = reinterpret_cast<float*>(sK0);
+  } else {
+    __shared__ __align__(16) float sZK0[G * 2 * kTile], sZK1[G * 2 * kTile];
+    constexpr int kZQ = ZQS ? 4 * G * RowStage::kFloats : 4;
+    __shared__ __align__(16) float sZQ0[kZQ], sZQ1[kZQ];
+    f.sZK[0] = sZK0;
+    f.sZK[1] = sZK1;
+    zq_stage[0] = ZQS ? sZQ0 + wave_id() * RowStage::kFloats : sZQ0;
+    zq_stage[1] = ZQS ? sZQ1 + wave_id() * RowStage::kFloats : sZQ1;
+  }
   f.g = a.geo;
   const Geo& g = f.g;
   const int N = g.N;
@@ -371,18 +433,18 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
   c.hl = hl;
   c.sig = sigma<T>(l32);
   c.kv_end = kv_end;
-  c.has_zq = a.flags & F_ZQ;
+  // (an in-block kernel reads no Z^Q; b is part of its relation term)
+  c.has_zq = ZM != ZM_INBLOCK && (a.flags & F_ZQ);
   c.has_zk = ZK;
   // (a staged kernel has a query-side table, into which b is folded: no
   // lookup of its own, and no code for one)
-  c.has_b = !ZQS && (a.flags & F_B);
+  c.has_b = ZM == ZM_GATHER && (a.flags & F_B);
   c.wsq = win_q(g, qb);
   c.zq_row = c.has_zq ? a.zq + zq_off(g, bh, imin(iq, zq_last(g))) : nullptr;
   c.zkb = c.has_zk ? a.zk + (int64_t)bh * N * g.Wp : nullptr;
   c.bun = c.has_b ? a.bunf + hh * a.bunf_hs : nullptr;
-  qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
-  f.zs.buf[0] = ZQS ? sZQ0 + wall * RowStage::kFloats : sZQ0;
-  f.zs.buf[1] = ZQS ? sZQ1 + wall * RowStage::kFloats : sZQ1;
+  f.zs.buf[0] = zq_stage[0];
+  f.zs.buf[1] = zq_stage[1];
   f.zs.init(g, c.has_zq ? a.zq + zq_off(g, bh, 0) : nullptr, -1, lane);
   f.sc2 = a.scale2;
   if constexpr (DROP) f.dr = drop_ctx(a, bh, lane);
@@ -392,6 +454,16 @@ __global__ __launch_bounds__((fwd_threads<T, GRP>()), (fwd_blocks_per_cu<T, ZK, 
 #pragma unroll
     for (int ks = 0; ks < F::NSD; ++ks)
       f.qf[ks] = iq < N ? frag_g<T>(qrow, F::KS * ks + F::E * hl) : M::zero();
+  }
+  if constexpr (ZM == ZM_INBLOCK) {
+    f.ib.tab = (const T*)a.tabq + hh * a.tabq_hs;
+    // (b is part of the relation term here whenever it is present)
+    f.ib.bt = a.tabb ? (const T*)a.tabb + hh * a.tabb_hs : nullptr;
+    f.ib.fold = a.fold;
+    f.ib_b = a.tabb != nullptr;
+    f.ib.consts(g, f.qf, hl, f.cst_lo, f.cst_hi);
+  } else {
+    qside_consts(g, c, qb, f.cst_lo, f.cst_hi);
   }
   f.oacc[0] = zero16();
   f.oacc[1] = zero16();
@@ -462,19 +534,36 @@ static hipError_t launch_fwd_g(const AttnArgs& a, hipStream_t st) {
   const bool zk = a.flags & F_ZK, zqs = (a.flags & F_ZQ) && wide_band(a.geo);
   const int nt = fwd_threads<T, GRP>();
   if (zk && zqs)
-    hipLaunchKernelGGL((fwd_kernel<T, true, true, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, true, ZM_STAGED, GRP, DROP>), dim3(total), dim3(nt), 0, st,
+                       a);
   else if (zk)
-    hipLaunchKernelGGL((fwd_kernel<T, true, false, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, true, ZM_GATHER, GRP, DROP>), dim3(total), dim3(nt), 0, st,
+                       a);
   else if (zqs)
-    hipLaunchKernelGGL((fwd_kernel<T, false, true, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, false, ZM_STAGED, GRP, DROP>), dim3(total), dim3(nt), 0, st,
+                       a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, false, false, GRP, DROP>), dim3(total), dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<T, false, ZM_GATHER, GRP, DROP>), dim3(total), dim3(nt), 0, st,
+                       a);
+  return hipGetLastError();
+}
+
+// In-block relation (16-bit inputs, query-side terms only, one wave group).
+template <typename T, bool DROP>
+static hipError_t launch_fwd_inblock(const AttnArgs& a, hipStream_t st) {
+  const int total = a.B * a.H * a.nqb;
+  hipLaunchKernelGGL((fwd_kernel<T, false, ZM_INBLOCK, false, DROP>), dim3(total),
+                     dim3(fwd_threads<T, false>()), 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
+    if (a.flags & F_ZIB) {
+      if (a.flags & F_DROP) return launch_fwd_inblock<T, true>(a, st);
+      return launch_fwd_inblock<T, false>(a, st);
+    }
     if (a.flags & F_DROP) {
       if (a.split) return launch_fwd_g<T, true, true>(a, st);
       return launch_fwd_g<T, false, true>(a, st);

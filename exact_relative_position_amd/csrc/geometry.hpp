@@ -128,7 +128,10 @@ RP_HD void cols_k(const Geo& g, int grp, int& cb, int& ce) {
   ce = imin(g.W, rrow(g, omax) - ws + 1);
 }
 
-enum : int { F_ZQ = 1, F_ZK = 2, F_B = 4, F_KEYPAD = 8, F_ZQ_NEEDED = 16, F_DROP = 32 };
+enum : int {
+  F_ZQ = 1, F_ZK = 2, F_B = 4, F_KEYPAD = 8, F_ZQ_NEEDED = 16, F_DROP = 32,
+  F_ZIB = 64  // forward: the query-side relation computed in the block (no Z^Q)
+};
 
 // Strides of a [B, H, N, d] tensor in elements.
 struct Str {
@@ -178,6 +181,13 @@ struct AttnArgs {
   const float* zk;
   const float* bunf;  // [Hb][R] fp32 unfolded scalar bias, or null
   int64_t bunf_hs;
+  // F_ZIB: the tables themselves (input dtype), their head strides in
+  // elements, and the fold table of a bucketed map (or null)
+  const void* tabq;
+  int64_t tabq_hs;
+  const void* tabb;
+  int64_t tabb_hs;
+  const int32_t* fold;
   const int32_t* key_len;
   void* dq;        // output (dtype) or fp32 partial when F_ZQ
   void* dk;

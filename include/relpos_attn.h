@@ -142,7 +142,24 @@ enum {
  *    (both together) every chunk's row terms, passes and contraction, and
  *    BWD_CONTRACT alone does nothing.  Each chunk's results are summed into
  *    dK, dV, daQ and db in chunk order, so the outputs are deterministic;
- *    they may differ from the unchunked ones in the last bits. */
+ *    they may differ from the unchunked ones in the last bits.
+ *  - relation: how the forward gets the query-side relation term of the
+ *    band tiles (the digest's ablation of keeping the projection against
+ *    recomputing it inside each block, and its limitations section).
+ *    RELPOS_REL_STORED: projected once into Z^Q (kept in zsave when one is
+ *    given).  RELPOS_REL_INBLOCK: computed inside each attention block from
+ *    Q and the tables (Q aQ^T of the tile's offsets by MFMA, plus b), so the
+ *    forward holds no projection at all (zsave must be NULL and
+ *    relpos_attn_zsave_size returns 0; the backward then projects Z^Q
+ *    itself).  It needs fp16 or bf16 inputs, no aK and zchunk = 0
+ *    (ERR_UNSUPPORTED otherwise); without aQ it changes nothing.
+ *    RELPOS_REL_AUTO (0) picks by sequence length: in-block where it is
+ *    supported and the relation window min(R, N + 127) is at least as wide
+ *    as the sequence, i.e. N <= R for a map of R unfolded rows (short
+ *    sequences, where a stored window is as large as a dense bias, and the
+ *    identity map, R = 2N - 1), else stored. */
+enum { RELPOS_REL_AUTO = 0, RELPOS_REL_STORED = 1, RELPOS_REL_INBLOCK = 2 };
+
 typedef struct relpos_problem {
   int64_t B, H, N, d;
   int32_t dtype;            /* relpos_dtype */
@@ -155,6 +172,7 @@ typedef struct relpos_problem {
   uint32_t dropout_offset;  /* counter word 3 of the generator */
   uint64_t dropout_seed;    /* generator key */
   int64_t zchunk;           /* query rows per projection chunk; 0 = whole sequence */
+  int32_t relation;         /* RELPOS_REL_* */
 } relpos_problem;
 
 /* Which relation terms are present (a "= 0" table is simply absent). */

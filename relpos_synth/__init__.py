@@ -57,6 +57,9 @@ class Workload:
     # query rows per chunk of the query-side projection (0: the whole
     # sequence); a run setting, not an input
     zchunk: int = 0
+    # how the forward gets the query-side relation: 0 by sequence length,
+    # 1 stored projection, 2 in the block; a run setting, not an input
+    relation: int = 0
 
     def with_(self, **kw):
         return dataclasses.replace(self, **kw)

@@ -45,13 +45,14 @@ def gpu_run(w, x, dev, keep_z=True, backward=True):
     drop = gpu_dropout(w)
     O, lse, zs = rp.forward(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], phi=w.phi,
                             tau=w.tau, causal=w.causal, key_len=t["key_len"], keep_z=keep_z,
-                            dropout=drop, zchunk=w.zchunk)
+                            dropout=drop, zchunk=w.zchunk, relation=w.relation)
     out = {"O": O, "lse": lse}
     if backward:
         dq, dk, dv, daq, dak, db = rp.backward(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"],
                                                O, lse, t["do"], zs, phi=w.phi, tau=w.tau,
                                                causal=w.causal, key_len=t["key_len"],
-                                               dropout=drop, zchunk=w.zchunk)
+                                               dropout=drop, zchunk=w.zchunk,
+                                               relation=w.relation)
         out.update(dq=dq, dk=dk, dv=dv, daq=daq, dak=dak, db=db)
     torch.cuda.synchronize(dev)
     return {k: (None if v is None else v.detach().cpu().double().numpy()) for k, v in out.items()}

@@ -105,8 +105,13 @@ def test_zsave_size_closed_form(L):
     # identity map: the window is N + G - 1 = N + 127 = 4223 columns per row,
     # padded to 4224, plus 32 floats of slack for the shifted rows of dZ^Q
     # (windows of 1024 columns or more)
+    # (with the stored relation; the automatic choice computes the identity
+    # map's relation in the block and keeps nothing)
     p = _prob(B=2, H=8, N=4096, dtype=2)
     phi = b.phi_struct({"kind": "identity"})
+    assert L.relpos_attn_zsave_size(ctypes.byref(p), ctypes.byref(phi), 1, ctypes.byref(n)) == 0
+    assert n.value == 0
+    p.relation = 1
     assert L.relpos_attn_zsave_size(ctypes.byref(p), ctypes.byref(phi), 1, ctypes.byref(n)) == 0
     assert n.value == 2 * 8 * 4096 * 4256 * 4
     # no vector table: nothing to keep
@@ -198,7 +203,8 @@ def test_problem_struct_layout():
     assert b.Problem.dropout_offset.offset == b.Problem.dropout_p.offset + 4
     assert b.Problem.dropout_seed.offset == b.Problem.dropout_offset.offset + 4
     assert b.Problem.zchunk.offset == b.Problem.dropout_seed.offset + 8
-    assert ctypes.sizeof(b.Problem) == b.Problem.zchunk.offset + 8
+    assert b.Problem.relation.offset == b.Problem.zchunk.offset + 8
+    assert ctypes.sizeof(b.Problem) == b.Problem.relation.offset + 8  # padded to 8 bytes
 
 
 @pytest.mark.parametrize("phi", [
@@ -465,3 +471,60 @@ def test_chunked_identity_workspace_is_linear_in_n(L):
     p.zchunk = 1024
     st, n = _ws(L, p, phi, terms=5, pass_=0)
     assert st == 0 and n < 12 * 1024 * (16384 + 160) * 4 + (1 << 20)
+
+
+# Relation mode (stored projection or in-block recompute): validation, the
+# length rule of the automatic choice, and the memory it saves.
+
+SHAW = {"kind": "truncated", "lo": -128, "hi": 128}
+
+
+def _zsave(L, p, phi, terms):
+    n = ctypes.c_size_t()
+    st = L.relpos_attn_zsave_size(ctypes.byref(p), ctypes.byref(phi), terms, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("dtype,terms,zchunk,relation,code", [
+    (1, 1, 0, 3, -1), (1, 1, 0, -1, -1),          # unknown modes
+    (0, 1, 0, 2, -2),                             # fp32: not in the block
+    (1, 3, 0, 2, -2),                             # aK present
+    (1, 1, 128, 2, -2),                           # chunked projection
+    (1, 4, 0, 2, 0), (0, 4, 0, 2, 0),             # no aQ: nothing to compute, accepted
+    (1, 5, 0, 2, 0), (2, 1, 0, 2, 0), (0, 1, 0, 1, 0), (0, 3, 0, 0, 0),
+])
+def test_relation_mode_validation(L, dtype, terms, zchunk, relation, code):
+    p = _prob(N=1000, dtype=dtype)
+    p.zchunk = zchunk
+    p.relation = relation
+    assert _ws(L, p, b.phi_struct(SHAW), terms=terms, pass_=0)[0] == code
+
+
+@pytest.mark.parametrize("N,relation,inblock", [
+    (128, 0, True), (257, 0, True), (258, 0, False), (8192, 0, False),  # 257 table rows
+    (128, 1, False), (8192, 2, True),
+])
+def test_relation_mode_keeps_no_projection_in_block(L, N, relation, inblock):
+    """In the block (chosen, or picked automatically where the relation window
+    min(R, N + 127) is no narrower than the sequence, i.e. N <= R) the
+    forward holds no projection: nothing to keep, and its workspace has no
+    Z^Q.  The backward still projects Z^Q into its own workspace."""
+    phi = b.phi_struct(SHAW)
+    p = _prob(H=12, N=N)
+    p.relation = relation
+    st, nz = _zsave(L, p, phi, 1)
+    assert st == 0
+    st, nf = _ws(L, p, phi, terms=1, pass_=0)
+    assert st == 0
+    p.relation = 1
+    _, nz_stored = _zsave(L, p, phi, 1)
+    _, nf_stored = _ws(L, p, phi, terms=1, pass_=0)
+    _, nb_stored = _ws(L, p, phi, terms=1, pass_=1)
+    p.relation = relation
+    _, nb = _ws(L, p, phi, terms=1, pass_=1)
+    assert nb == nb_stored  # the backward is the same either way
+    if inblock:
+        assert nz == 0 and nf == 0
+        assert nz_stored >= 12 * N * min(257, N + 127) * 4
+    else:
+        assert nz == nz_stored and nf == nf_stored

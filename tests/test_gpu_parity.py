@@ -175,6 +175,77 @@ def _random_workloads(n, seed=7):
     return out
 
 
+# In-block relation (RELPOS_REL_INBLOCK): the forward computes the query-side
+# term inside each block from Q and the tables, with no stored projection.
+# Narrow and wide bands, saturated tiles on both sides, ragged tails, every
+# mask, b, bucketed maps through the fold table, shared tables, dropout and
+# degenerate sizes; "stored_" cases pin the stored path on shapes that the
+# automatic choice sends in-block (the identity map, short sequences).
+INBLOCK = [
+    Workload("ib_shaw_ragged_f16", 2, 2, 333, 64, "f16", SHAW16, 1 / 8, has_aq=True, relation=2),
+    Workload("ib_trunc_bias_bf16", 1, 3, 700, 64, "bf16", {"kind": "truncated", "lo": -100,
+                                                            "hi": 60},
+             1 / 8, has_aq=True, has_b=True, relation=2),
+    Workload("ib_txl_causal_bf16", 2, 2, 300, 64, "bf16", IDENTITY, 1 / 8, has_aq=True,
+             has_b=True, causal=True, b_std=0.02, relation=2),
+    Workload("ib_keypad_causal_f16", 2, 2, 450, 64, "f16", {"kind": "truncated", "lo": -64,
+                                                             "hi": 64},
+             1 / 8, has_aq=True, has_b=True, causal=True, key_padding=True, pad_frac=0.3,
+             relation=2),
+    Workload("ib_log_buckets_keypad_bf16", 2, 2, 420, 64, "bf16",
+             {"kind": "log", "num_buckets": 32, "max_distance": 40}, 1 / 8, has_aq=True,
+             has_b=True, key_padding=True, pad_frac=0.3, relation=2),
+    Workload("ib_t5_vector_f16", 1, 2, 400, 64, "f16", T5_32_128, 1 / 8, has_aq=True,
+             has_b=True, relation=2),
+    Workload("ib_shared_tables_f16", 2, 3, 270, 64, "f16", {"kind": "truncated", "lo": -64,
+                                                             "hi": 64},
+             1 / 8, has_aq=True, has_b=True, shared_tables=True, relation=2),
+    Workload("ib_one_row_table_bf16", 1, 1, 150, 64, "bf16", {"kind": "truncated", "lo": 3,
+                                                               "hi": 3},
+             1 / 8, has_aq=True, has_b=True, relation=2),
+    Workload("ib_n5_f16", 1, 1, 5, 64, "f16", SHAW16, 1 / 8, has_aq=True, has_b=True, relation=2),
+    Workload("ib_n1_bf16", 1, 1, 1, 64, "bf16", IDENTITY, 1 / 8, has_aq=True, has_b=True,
+             relation=2),
+    Workload("ib_wide_causal_f16", 1, 2, 1000, 64, "f16", IDENTITY, 1 / 8, has_aq=True,
+             has_b=True, causal=True, b_std=0.02, relation=2),
+    Workload("ib_dropout_shaw_f16", 2, 2, 333, 64, "f16", SHAW16, 1 / 8, has_aq=True,
+             has_b=True, dropout=(26, 0x9E3779B97F4A7C15, 3), relation=2),
+    Workload("ib_dropout_txl_bf16", 1, 2, 520, 64, "bf16", IDENTITY, 1 / 8, has_aq=True,
+             has_b=True, causal=True, b_std=0.02, dropout=(64, 12345, 0), relation=2),
+    Workload("stored_txl_causal_bf16", 2, 2, 300, 64, "bf16", IDENTITY, 1 / 8, has_aq=True,
+             has_b=True, causal=True, b_std=0.02, relation=1),
+    Workload("stored_wide_band_causal_bf16", 1, 2, 1000, 64, "bf16", IDENTITY, 1 / 8,
+             has_aq=True, has_b=True, causal=True, b_std=0.02, relation=1),
+    Workload("stored_short_shaw_f16", 4, 2, 200, 64, "f16", {"kind": "truncated", "lo": -128,
+                                                              "hi": 128},
+             1 / 8, has_aq=True, has_b=True, relation=1),
+]
+
+
+@pytest.mark.parametrize("w", INBLOCK, ids=[w.name for w in INBLOCK])
+def test_inblock_parity(w):
+    """Every output against the oracle (the backward projects Z^Q itself)."""
+    test_small_parity(w)
+
+
+def test_inblock_matches_stored_forward():
+    """The in-block forward against the stored one on the same inputs: the
+    same mathematics in fp32, summed in a different order, so O agrees to
+    well within one 16-bit unit and LSE closely; both are deterministic."""
+    dev = require_gpu()
+    w = Workload("ib_vs_stored_f16", 2, 3, 777, 64, "f16", {"kind": "truncated", "lo": -200,
+                                                             "hi": 100},
+                 1 / 8, has_aq=True, has_b=True, causal=True)
+    x = make_inputs(w)
+    _say("[gpu] in-block vs stored forward")
+    a = gpu_run(w.with_(relation=2), x, dev, backward=False)
+    a2 = gpu_run(w.with_(relation=2), x, dev, backward=False)
+    s = gpu_run(w.with_(relation=1), x, dev, backward=False)
+    assert np.array_equal(a["O"], a2["O"]) and np.array_equal(a["lse"], a2["lse"])
+    assert rel_err(a["O"], s["O"]) < 1e-3
+    assert np.abs(a["lse"] - s["lse"]).max() < 1e-4
+
+
 @pytest.mark.parametrize("w", _random_workloads(24), ids=lambda w: w.name)
 def test_random_small_parity(w):
     """Seeded random configurations, every output against the oracle."""
@@ -418,6 +489,15 @@ def full_heads(H):
     heads, so these three reach different XCDs, the start, middle and end of
     the dispatch order, and both ends of the causal interleave."""
     return sorted({0, H // 2, H - 1})
+
+
+@pytest.mark.parametrize("name,relation", [("txl_n4096_bf16", 1), ("txl_n4096_bf16", 2),
+                                           ("shaw_n8192_f16", 2)])
+def test_full_shape_relation_modes(name, relation):
+    """A full-size workload with the relation forced stored (1) or in the
+    block (2), whichever the automatic choice would not take."""
+    w = WORKLOADS[name]
+    _full_parity(w.with_(name=f"{name}_rel{relation}", relation=relation))
 
 
 def _full_parity(w, n_others=6):
