@@ -165,7 +165,7 @@ def window_columns(w, key_side=False):
 
 _COMMON = ("qside.hpp", "tiles.hpp", "device.hpp", "geometry.hpp", "dropout.hpp")
 KERNEL_SOURCES = {
-    "fwd_kernel": ("attn_fwd.hip",) + _COMMON,
+    "fwd_kernel": ("attn_fwd.hip", "inblock.hpp") + _COMMON,
     "bwd_kernel": ("attn_bwd.hpp", "attn_bwd_q.hpp", "attn_bwd_k.hpp", "attn_bwd_f32.hip",
                    "attn_bwd_f16.hip", "attn_bwd_bf16.hip") + _COMMON,
 }
