@@ -255,10 +255,12 @@ relpos_status make_plan(const relpos_problem* prob, const relpos_phi* phi,
   if (prob->relation < RELPOS_REL_AUTO || prob->relation > RELPOS_REL_INBLOCK)
     return fail(RELPOS_ERR_INVALID_ARG, "unknown relation mode");
   {
-    const bool can = pl.esz == 2 && !pl.has_ak && pl.nchunk == 1;
+    // (with zchunk the in-block forward needs no chunks: it holds no Z^Q at
+    // all; the backward still projects one chunk of queries at a time)
+    const bool can = pl.esz == 2 && !pl.has_ak;
     if (prob->relation == RELPOS_REL_INBLOCK && pl.has_aq && !can)
       return fail(RELPOS_ERR_UNSUPPORTED,
-                  "the in-block relation needs fp16 or bf16 inputs, no aK and zchunk = 0");
+                  "the in-block relation needs fp16 or bf16 inputs and no aK");
     const bool shortn = pl.geo.W >= pl.N;
     pl.inblock = pl.has_aq && can &&
                  (prob->relation == RELPOS_REL_INBLOCK ||
@@ -690,7 +692,7 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
     a.fold = pl.bucketed ? w.fold : nullptr;
     a.split = 0;  // one wave group per block
   }
-  if (pl.nchunk == 1) return hip_check(launch_fwd(pl.dtype, a, st), "forward");
+  if (pl.nchunk == 1 || pl.inblock) return hip_check(launch_fwd(pl.dtype, a, st), "forward");
   // chunked projection: Z^Q of one chunk of queries, then their attention
   for (int c = 0; c < pl.nchunk; ++c) {
     Geo gc = pl.geo;

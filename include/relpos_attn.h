@@ -129,8 +129,9 @@ enum {
  *  - zchunk (a multiple of 128, or 0): linear-memory mode for wide relation
  *    windows (the identity map's is N + 127 columns per query).  When
  *    0 < zchunk < N the query-side projection Z^Q and its gradient dZ^Q are
- *    never held for the whole sequence: the forward and the backward each
- *    recompute them one chunk of zchunk queries at a time inside the
+ *    never held for the whole sequence: the forward (unless it computes the
+ *    relation in the block, below, and holds no Z^Q at all) and the backward
+ *    each recompute them one chunk of zchunk queries at a time inside the
  *    workspace (the digest's section on limitations: recomputing the
  *    projection instead of storing it makes the memory linear), so the
  *    workspace is O(B H zchunk W) plus O(B H N d) for the chunk-summed dK
@@ -138,7 +139,8 @@ enum {
  *    relpos_attn_zsave_size returns 0).  The key-side term must be absent
  *    (ERR_UNSUPPORTED).  Under this mode the stage calls run whole chunks:
  *    FWD_PROJECT and BWD_PREPARE only build the map tables, FWD_ATTEND runs
- *    every chunk's projection and attention, BWD_QUERY_PASS | BWD_KEY_PASS
+ *    every chunk's projection and attention (in-block: one attention launch
+ *    over all queries), BWD_QUERY_PASS | BWD_KEY_PASS
  *    (both together) every chunk's row terms, passes and contraction, and
  *    BWD_CONTRACT alone does nothing.  Each chunk's results are summed into
  *    dK, dV, daQ and db in chunk order, so the outputs are deterministic;
@@ -151,8 +153,9 @@ enum {
  *    Q and the tables (Q aQ^T of the tile's offsets by MFMA, plus b), so the
  *    forward holds no projection at all (zsave must be NULL and
  *    relpos_attn_zsave_size returns 0; the backward then projects Z^Q
- *    itself).  It needs fp16 or bf16 inputs, no aK and zchunk = 0
- *    (ERR_UNSUPPORTED otherwise); without aQ it changes nothing.
+ *    itself, one chunk at a time when zchunk is set).  It needs fp16 or
+ *    bf16 inputs and no aK (ERR_UNSUPPORTED otherwise); without aQ it
+ *    changes nothing.
  *    RELPOS_REL_AUTO (0) picks by sequence length: in-block where it is
  *    supported and the relation window min(R, N + 127) is at least as wide
  *    as the sequence, i.e. N <= R for a map of R unfolded rows (short

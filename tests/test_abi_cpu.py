@@ -489,7 +489,7 @@ def _zsave(L, p, phi, terms):
     (1, 1, 0, 3, -1), (1, 1, 0, -1, -1),          # unknown modes
     (0, 1, 0, 2, -2),                             # fp32: not in the block
     (1, 3, 0, 2, -2),                             # aK present
-    (1, 1, 128, 2, -2),                           # chunked projection
+    (1, 1, 128, 2, 0),                            # the backward is chunked, not the forward
     (1, 4, 0, 2, 0), (0, 4, 0, 2, 0),             # no aQ: nothing to compute, accepted
     (1, 5, 0, 2, 0), (2, 1, 0, 2, 0), (0, 1, 0, 1, 0), (0, 3, 0, 0, 0),
 ])

@@ -588,19 +588,21 @@ CHUNKED = [
 
 @pytest.mark.parametrize("w", CHUNKED, ids=[w.name for w in CHUNKED])
 def test_chunked_projection_parity(w):
-    """Every output against the oracle; the forward's O and LSE and the dQ of
-    the chunked run are the unchunked stored run's bit for bit (each query block
-    does the same arithmetic on the same projection values), and the
-    chunk-summed outputs (dK, dV, daQ, db) are deterministic."""
+    """Every output against the oracle, with the automatic relation choice
+    (the identity map's forward in-block, its backward chunked) and with the
+    projection stored and chunked in both passes; stored, the forward's O
+    and LSE and the dQ of the chunked run are the unchunked stored run's bit
+    for bit (each query block does the same arithmetic on the same
+    projection values), and the chunk-summed outputs (dK, dV, daQ, db) are
+    deterministic."""
     test_small_parity(w)
+    ws = w.with_(name=w.name + "_stored", relation=1)
+    test_small_parity(ws)
     dev = require_gpu()
     x = make_inputs(w)
-    got = gpu_run(w, x, dev)
-    again = gpu_run(w, x, dev)
-    # (the unchunked run with the stored projection: the in-block forward,
-    # which the automatic choice takes for the identity map, sums the
-    # relation in another order)
-    whole = gpu_run(w.with_(zchunk=0, relation=1), x, dev, keep_z=False)
+    got = gpu_run(ws, x, dev)
+    again = gpu_run(ws, x, dev)
+    whole = gpu_run(ws.with_(zchunk=0), x, dev, keep_z=False)
     for n in ALL:
         if got[n] is not None:
             np.testing.assert_array_equal(got[n], again[n], err_msg=n)
