@@ -669,14 +669,20 @@ relpos_status fwd_run(const relpos_problem* prob, const relpos_phi* phi, const r
     if (pl.has_ak) w.zk = c.take<float>(sizeof(float) * pl.zk_elems);
   }
   hipStream_t st = (hipStream_t)stream;
-  if (stages & RELPOS_FWD_PROJECT) {
+  // (in the block, the attention launch reads the map tables itself, so
+  // they are built with it, in the same call, and there is nothing to
+  // project)
+  if ((stages & RELPOS_FWD_PROJECT) && !pl.inblock) {
     if ((s = prepare_tables(pl, b, w.fold, nullptr, nullptr, w.bunf, st)) != RELPOS_OK) return s;
-    if (pl.nchunk == 1 && !pl.inblock &&
+    if (pl.nchunk == 1 &&
         (s = project(pl, prob, Q, K, aQ, aK, b, w.fold, w.zq, w.zk, st, pl.geo, 0, pl.nblk)) !=
             RELPOS_OK)
       return s;
   }
   if (!(stages & RELPOS_FWD_ATTEND)) return RELPOS_OK;
+  if (pl.inblock &&
+      (s = prepare_tables(pl, b, w.fold, nullptr, nullptr, w.bunf, st)) != RELPOS_OK)
+    return s;
   AttnArgs a = attn_args(pl, prob, mask, Q, K, V);
   a.o_out = O;
   a.lse = lse;

@@ -264,8 +264,10 @@ relpos_status relpos_attn_fwd_noalloc(const relpos_problem* prob, const relpos_p
  * projection, then the fused tiled attention; the backward section as the
  * query-parallel pass, the key-parallel pass, then the final contraction.
  *  FWD_PROJECT   map tables (bucket unfold) and Z^Q, Z^K of the reachable window
- *                (Eq. 3; section on the grouped reachable range)
- *  FWD_ATTEND    fused forward: O and LSE
+ *                (Eq. 3; section on the grouped reachable range); nothing with
+ *                the in-block relation
+ *  FWD_ATTEND    fused forward: O and LSE (with the in-block relation, the map
+ *                tables first)
  *  BWD_PREPARE   map tables, projections (only when zsave is NULL) and the
  *                row terms D_i = sum_d dO_id O_id
  *  BWD_QUERY_PASS  dQ (partial when aQ is present) and dZ^Q per offset

@@ -491,6 +491,28 @@ def full_heads(H):
     return sorted({0, H // 2, H - 1})
 
 
+def test_inblock_attend_stage_builds_its_tables():
+    """With the relation in the block, the attention stage alone (no
+    projection stage before it) builds the fold table of a bucketed map
+    itself and gives the oracle's O and LSE."""
+    import exact_relative_position_amd._binding as B_
+    dev = require_gpu()
+    w = Workload("ib_attend_stage_log_f16", 1, 2, 500, 64, "f16",
+                 {"kind": "log", "num_buckets": 32, "max_distance": 60}, 1 / 8, has_aq=True,
+                 has_b=True, relation=2)
+    x = make_inputs(w)
+    t = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    _say("[gpu] in-block attend stage alone")
+    run = B_.Prepared(t["q"], t["k"], t["v"], t["aq"], t["ak"], t["b"], t["do"], phi=w.phi,
+                      tau=w.tau, relation=2)
+    run.fwd(B_.FWD_ATTEND)
+    torch.cuda.synchronize(dev)
+    got = {"O": run.O.cpu().double().numpy(), "lse": run.lse.cpu().double().numpy()}
+    ref = oracle_run(w, x, backward=False)
+    to, tg = tolerances(w.dtype)
+    compare(got, ref, ("O", "lse"), tol_o=to, tol_g=tg, label=w.name, dtype=w.dtype)
+
+
 @pytest.mark.parametrize("name,relation", [("txl_n4096_bf16", 1), ("txl_n4096_bf16", 2),
                                            ("shaw_n8192_f16", 2)])
 def test_full_shape_relation_modes(name, relation):
