@@ -332,11 +332,19 @@ def test_bitwise_deterministic():
 
 
 @pytest.mark.parametrize("dropout", [None, (26, 77, 1)])
-def test_strided_layout_bnhd(dropout):
-    """Q, K, V given as [B, N, H, d] memory viewed as [B, H, N, d]."""
+@pytest.mark.parametrize("inblock", [False, True])
+def test_strided_layout_bnhd(dropout, inblock):
+    """Q, K, V given as [B, N, H, d] memory viewed as [B, H, N, d] (with the
+    relation stored, or computed in the block from Q read through the
+    strides)."""
     dev = require_gpu()
-    w = Workload("strided_f16", 2, 3, 257, 64, "f16", SHAW16, 1 / 8, has_aq=True, has_ak=True,
-                 dropout=dropout)
+    if inblock:
+        w = Workload("strided_inblock_bf16", 2, 3, 300, 64, "bf16", IDENTITY, 1 / 8,
+                     has_aq=True, has_b=True, causal=True, b_std=0.02, dropout=dropout,
+                     relation=2)
+    else:
+        w = Workload("strided_f16", 2, 3, 257, 64, "f16", SHAW16, 1 / 8, has_aq=True,
+                     has_ak=True, dropout=dropout)
     x = make_inputs(w)
     _say("[gpu] strided layout")
     ref = gpu_run(w, x, dev)
