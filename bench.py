@@ -257,7 +257,8 @@ def stage_list(B_, run, separate_passes=False):
 def time_stages(torch, dev, stages, warmup, steps):
     """W untimed steps, then K timed steps with HIP events between the stage
     calls on the launch stream.  Returns (average ms per stage, GPU ms per
-    step, wall seconds of the timed steps)."""
+    step, wall seconds of the timed steps); the per-step stage times are left
+    in time_stages.per_step for the median and minimum."""
     for _ in range(warmup):
         for _, fn in stages:
             fn()
@@ -273,10 +274,27 @@ def time_stages(torch, dev, stages, warmup, steps):
             ev[s][k + 1].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    stage_ms = {name: sum(ev[s][k].elapsed_time(ev[s][k + 1]) for s in range(steps)) / steps
-                for k, (name, _) in enumerate(stages)}
+    per_step = [{name: ev[s][k].elapsed_time(ev[s][k + 1]) for k, (name, _) in enumerate(stages)}
+                for s in range(steps)]
+    time_stages.per_step = per_step
+    stage_ms = {name: sum(p[name] for p in per_step) / steps for name, _ in stages}
     gpu_ms = ev[0][0].elapsed_time(ev[steps - 1][len(stages)]) / steps
     return stage_ms, gpu_ms, wall
+
+
+FWD_STAGES = ("project", "attend")
+BWD_STAGES = ("prepare", "passes", "query_pass", "key_pass", "contract")
+
+
+def spread(per_step):
+    """Median and minimum over the timed steps of the step, its forward and
+    its backward (ms)."""
+    import statistics
+    out = {}
+    for key, names in (("step", None), ("fwd", FWD_STAGES), ("bwd", BWD_STAGES)):
+        v = [sum(t for n, t in p.items() if names is None or n in names) for p in per_step]
+        out[key] = {"median": round(statistics.median(v), 4), "min": round(min(v), 4)}
+    return out
 
 
 def run_sweep(args):
@@ -324,6 +342,7 @@ def run_sweep(args):
         out = {"metric": metric, "config":
                describe(w), "dtype": w.dtype, "fwd_ms": round(fwd_ms, 4),
                "bwd_ms": round(bwd_ms, 4), "ms_per_step": round(gpu_ms, 4),
+               "ms_spread": spread(time_stages.per_step),
                "fwd_tflops": round(4.0 * w.d * pairs / (fwd_ms * 1e-3) / 1e12, 2),
                "bwd_tflops": round(10.0 * w.d * pairs / (bwd_ms * 1e-3) / 1e12, 2),
                "fwd_pct_peak": round(100.0 * 4.0 * w.d * pairs / (fwd_ms * 1e-3) / 1e12 / peak,
@@ -477,6 +496,7 @@ def main():
         "config": describe(w),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "ms_spread": spread(time_stages.per_step),
         "wall_ms_per_step": round(wall * 1e3 / K, 4),
         "pct_peak": round(100.0 * value / peak, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
