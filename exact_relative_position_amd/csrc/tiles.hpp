@@ -198,11 +198,20 @@ struct DLoader {
     }
   }
   // Load rows [0, nvalid) of the tile starting at src; zero the others.
+  // A whole tile (the common case, a wave-uniform test) issues its loads
+  // with no per-lane condition, so they need no exec-mask branches.
   __device__ __forceinline__ void load(char* lds, const T* src, int nvalid, int lane) const {
+    if (nvalid >= 64) {
+#pragma unroll
+      for (int u = 0; u < PW; ++u)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off[u]),
+                                         (lds_void_t*)(lds + (blk0 + u) * 1024), 16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       char* dst = lds + (blk0 + u) * 1024;
-      if (nvalid >= 64 || row[u] < nvalid) {
+      if (row[u] < nvalid) {
         __builtin_amdgcn_global_load_lds((glb_void_t*)(src + off[u]), (lds_void_t*)dst, 16, 0, 0);
       } else {
         *reinterpret_cast<Chunk*>(dst + lane * 16) = Chunk{{0u, 0u, 0u, 0u}};
