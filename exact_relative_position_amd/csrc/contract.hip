@@ -62,13 +62,20 @@ struct RowsK {
   // dZ rows [i0, i0 + 128) x columns [c0, c0 + 32) and the table rows
   // ws + c0 .. + 31 into (zb, tb), asynchronously
   __device__ __forceinline__ void issue(float* zb, float* tb, int c0) const {
+    // (a block whose 128 rows all exist, a wave-uniform test, loads with no
+    // per-lane condition and so without exec-mask branches)
+    const bool whole = i0 + kBlockRows <= N;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = 4 * w + u;  // 8 rows per instruction
       const int r = 8 * j + (lane >> 3);
       const int lc = (lane & 7) ^ zswz(r);
       float* dst = zb + 256 * j;
-      if (i0 + r < N) {
+      if (whole) {
+        const int sc = c0 + 4 * lc + (SH ? (i0 + r + shb) & 31 : 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + sc),
+                                         (lds_void_t*)dst, 16, 0, 0);
+      } else if (i0 + r < N) {
         const int sc = c0 + 4 * lc + (SH ? (i0 + r + shb) & 31 : 0);
         __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + sc),
                                          (lds_void_t*)dst, 16, 0, 0);
@@ -200,13 +207,18 @@ struct Rows2K {
   TrReader<__bf16> tr;
 
   __device__ __forceinline__ void issue(float* zb, char* th, char* tl, int c0) const {
+    const bool whole = i0 + kBlockRows <= N;  // (as in RowsK::issue)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = 4 * w + u;  // 8 rows per instruction
       const int r = 8 * j + (lane >> 3);
       const int lc = (lane & 7) ^ RowsK<T, SH>::zswz(r);
       float* dst = zb + 256 * j;
-      if (i0 + r < N) {
+      if (whole) {
+        const int sc = c0 + 4 * lc + (SH ? (i0 + r + shb) & 31 : 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + sc),
+                                         (lds_void_t*)dst, 16, 0, 0);
+      } else if (i0 + r < N) {
         const int sc = c0 + 4 * lc + (SH ? (i0 + r + shb) & 31 : 0);
         __builtin_amdgcn_global_load_lds((glb_void_t*)(dzb + (int64_t)(i0 + r) * Wp + sc),
                                          (lds_void_t*)dst, 16, 0, 0);
@@ -434,13 +446,20 @@ struct ColsK {
     const int shb = i + g.lo + ws;
     const int span = SH ? z_span(g) : Wp;
     if ((colb & 3) == 0) {
+      // (every lane's row and columns inside the stored rows, a wave-uniform
+      // test: loads with no per-lane condition, without exec-mask branches)
+      const bool whole = nrow >= 16 * w + 16 && colb >= 0 && colb + 64 <= span;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = 4 * w + u;  // 4 rows of 64 floats per instruction
         const int r = 4 * j + (lane >> 4);
         const int col = colb + 4 * (lane & 15);
         float* dst = zb + 256 * j;
-        if (r < nrow && col >= 0 && col < span) {
+        if (whole) {
+          const int sc = col + (SH ? (r + shb) & 31 : 0);
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + sc),
+                                           (lds_void_t*)dst, 16, 0, 0);
+        } else if (r < nrow && col >= 0 && col < span) {
           const int sc = col + (SH ? (r + shb) & 31 : 0);
           __builtin_amdgcn_global_load_lds((glb_void_t*)(dzs + (int64_t)(i + r) * Wp + sc),
                                            (lds_void_t*)dst, 16, 0, 0);
