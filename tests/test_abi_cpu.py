@@ -528,3 +528,26 @@ def test_relation_mode_keeps_no_projection_in_block(L, N, relation, inblock):
         assert nz_stored >= 12 * N * min(257, N + 127) * 4
     else:
         assert nz == nz_stored and nf == nf_stored
+
+
+# Empty inputs: no token, or no batch entry, is a no-op that succeeds before
+# any device call (null tensors are fine then); the backward with no table
+# gradient to clear needs no device either.
+
+@pytest.mark.parametrize("B,N", [(1, 0), (0, 256), (0, 0)])
+def test_empty_problem_is_a_no_op(L, B, N):
+    p = _prob(B=B, N=N)
+    phi = b.phi_struct({"kind": "truncated", "lo": -16, "hi": 16})
+    m = b.Mask()
+    for relation in (0, 1, 2):
+        p.relation = relation
+        st, n = _ws(L, p, phi, terms=5, pass_=0)
+        assert st == 0
+        assert L.relpos_attn_fwd(ctypes.byref(p), ctypes.byref(phi), ctypes.byref(m), None,
+                                 None, None, None, None, None, None, None, None, None, 0,
+                                 None) == 0
+    # backward without the contraction stage and without tables: nothing to do
+    assert L.relpos_attn_bwd_stages(ctypes.byref(p), ctypes.byref(phi), ctypes.byref(m), None,
+                                    None, None, None, None, None, None, None, None, None, None,
+                                    None, None, None, None, None, None, 0, None,
+                                    b.BWD_ALL & ~b.BWD_CONTRACT) == 0

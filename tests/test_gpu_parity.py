@@ -280,6 +280,29 @@ def test_present_all_zero_table(table):
             ("O", "lse", "dq", "dk", "dv"), tol_o=to, tol_g=tg, label=f"zero vs absent {table}")
 
 
+@pytest.mark.parametrize("B,N,relation", [(1, 0, 0), (0, 100, 0), (2, 0, 2), (0, 0, 1)])
+def test_empty_inputs(B, N, relation):
+    """No token (N = 0) or no batch entry (B = 0): empty outputs, and the
+    table gradients exist and are zero (no pair reaches any row)."""
+    import exact_relative_position_amd as rp
+    dev = require_gpu()
+    H, R = 2, 33
+    f16 = dict(dtype=torch.float16, device=dev)
+    q = torch.zeros(B, H, N, 64, **f16)
+    aq = torch.randn(H, R, 64, **f16)
+    bt = torch.randn(H, R, **f16)
+    phi = SHAW16
+    _say(f"[gpu] empty inputs B{B} N{N} relation {relation}")
+    O, lse, zs = rp.forward(q, q, q, aq, None, bt, phi=phi, tau=0.125, relation=relation)
+    assert O.shape == q.shape and lse.shape == (B, H, N)
+    dq, dk, dv, daq, dak, db = rp.backward(q, q, q, aq, None, bt, O, lse, q, zs, phi=phi,
+                                           tau=0.125, relation=relation)
+    torch.cuda.synchronize(dev)
+    assert dq.shape == q.shape and dk.shape == q.shape and dv.shape == q.shape and dak is None
+    assert daq.shape == (H, R, 64) and db.shape == (H, R)
+    assert torch.count_nonzero(daq).item() == 0 and torch.count_nonzero(db).item() == 0
+
+
 def test_fully_masked_batch():
     dev = require_gpu()
     w = Workload("dead_rows_f16", 2, 2, 200, 64, "f16", SHAW16, 1 / 8, has_aq=True, has_b=True,
